@@ -1,0 +1,399 @@
+"""Pins of the fp64 oracle against facts fixed by the mathematics and by the
+source pages' definitions (runs on the CPU, no GPU, no HIP library).
+
+Each test names the fact it checks.  A pin never re-types the oracle's own
+formula: it uses a closed form, a brute-force enumeration, a library routine
+(torch's CPU scaled_dot_product_attention, numpy sort / argpartition) or an
+invariant that a dropped term, a wrong sign or index or a transposed operand
+would break.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import (block_stats, build_segments, dense_attention, gather_pages,
+                    index_attention, lse_combine, masked_attention, pool_queries,
+                    segment_attention, select_blocks, topk)
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _sdpa(q, k, v, scale, causal):
+    """torch CPU float64 scaled_dot_product_attention on one head."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), is_causal=causal, scale=scale)
+    return o[0, 0].numpy()
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- F1 -------
+@pytest.mark.parametrize("S,D,T", [(8, 4, 2), (256, 64, 64), (320, 32, 64)])
+def test_F1_all_blocks_mask_is_dense_causal(S, D, T):
+    rng = _rng(S + D)
+    q, k, v = (rng.standard_normal((S, D)) for _ in range(3))
+    scale = 1 / math.sqrt(D)
+    nB = S // T
+    full = np.tril(np.ones((nB, nB), dtype=bool))
+    om, lm = masked_attention(q, k, v, full, T, scale)
+    od, ld = dense_attention(q, k, v, scale, causal=True)
+    assert np.abs(om - od).max() <= 1e-12
+    assert np.abs(lm - ld).max() <= 1e-12
+    ref = _sdpa(q, k, v, scale, causal=True)
+    assert np.abs(od - ref).max() <= 1e-12
+    # the selector with p_c = 1 keeps every visible block
+    c, r = block_stats(k, T)
+    sel = select_blocks(pool_queries(q, T), c, r, 1.0, 0.1)
+    assert (sel["M"] == full).all()
+
+
+def test_F1_lse_matches_logsumexp():
+    rng = _rng(3)
+    q, k, v = (rng.standard_normal((16, 8)) for _ in range(3))
+    _, lse = dense_attention(q, k, v, 0.5, causal=True)
+    for t in range(16):
+        ref = torch.logsumexp(torch.from_numpy(0.5 * (k[:t + 1] @ q[t])), 0).item()
+        assert abs(lse[t] - ref) <= 1e-12
+
+
+# ---------------------------------------------------------------- F2 -------
+def test_F2_zero_query_gives_mean_of_visible_values():
+    rng = _rng(5)
+    S, D = 64, 16
+    k, v = rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    o, lse = dense_attention(np.zeros((S, D)), k, v, 0.3, causal=True)
+    for t in range(S):
+        assert np.abs(o[t] - v[:t + 1].sum(0) / (t + 1)).max() <= 1e-12
+        assert abs(lse[t] - math.log(t + 1)) <= 1e-12
+
+
+def test_F2_first_row_and_dominant_key():
+    rng = _rng(6)
+    S, D = 32, 8
+    q, k, v = (rng.standard_normal((S, D)) for _ in range(3))
+    o, _ = dense_attention(q, k, v, 1.0, causal=True)
+    assert np.abs(o[0] - v[0]).max() <= 1e-15
+    # one key with a +50 logit margin over all others takes all the weight
+    qq = np.zeros(D); qq[0] = 1.0
+    kk = np.zeros((S, D)); kk[17, 0] = 50.0
+    oo, _ = index_attention(qq, kk, v, np.arange(S), 1.0)
+    # every other weight is below e^-50, so the error is below 2 S e^-50 max|v|
+    assert np.abs(oo - v[17]).max() <= 2 * S * math.exp(-50) * np.abs(v).max()
+
+
+def test_F2_golden_two_key_softmax():
+    g = _gold("two_key_softmax.json")
+    o, lse = index_attention(g["q"], g["k"], g["v"], [0, 1], g["scale"])
+    assert np.abs(o - np.array(g["o"])).max() <= 1e-15
+    assert abs(lse - g["lse"]) <= 1e-15
+
+
+# ---------------------------------------------------------------- F3 -------
+@pytest.mark.parametrize("D", [2, 4, 8, 64])
+@pytest.mark.parametrize("T", [1, 2, 8, 64])
+def test_F3_rescue_bound_never_below_block_max(D, T):
+    rng = _rng(100 * D + T)
+    for trial in range(10000 // (D * T) + 20):
+        keys = rng.standard_normal((T, D)) * rng.uniform(0.1, 3.0)
+        queries = rng.standard_normal((T, D))
+        c, r = block_stats(keys, T)
+        for qv in (queries[0], pool_queries(queries, T)[0]):
+            sc = float(qv @ c[0])
+            sr = sc + np.linalg.norm(qv) * r[0]
+            true_max = (keys @ qv).max()
+            assert sr >= true_max - 1e-12
+            if T == 1:
+                assert abs(sr - true_max) <= 1e-12
+
+
+def test_F3_bound_is_tight_when_farthest_key_lies_along_query():
+    # keys c + u and c - u with u parallel to q: max q.k = q.c + ||q|| ||u||
+    D = 6
+    rng = _rng(9)
+    cvec = rng.standard_normal(D)
+    qv = rng.standard_normal(D)
+    u = 0.7 * qv / np.linalg.norm(qv)
+    keys = np.stack([cvec + u, cvec - u])
+    c, r = block_stats(keys, 2)
+    sr = qv @ c[0] + np.linalg.norm(qv) * r[0]
+    assert abs(sr - (keys @ qv).max()) <= 1e-12
+
+
+# ---------------------------------------------------------------- F4 -------
+def _spike_fixture(seed=0):
+    """One query block of 8 queries all equal to 3 e1, 8 visible key blocks."""
+    D = T = 8
+    rng = _rng(seed)
+    e = np.eye(D)
+    blocks = []
+    for j in range(8):
+        if j in (1, 4):                   # decoys: e1 + small noise orthogonal to e1
+            nz = 0.05 * rng.standard_normal((T, D)); nz[:, 0] = 0
+            blocks.append(e[0] + nz)
+        elif j == 6:                      # spike block: one key 6 e1, seven keys e2..e8
+            blocks.append(np.vstack([6 * e[0], e[1:]]))
+        else:
+            blocks.append(0.1 * rng.standard_normal((T, D)))
+    k = np.vstack(blocks)
+    q = np.tile(3 * e[0], (8 * T, 1))
+    return q, k, T
+
+
+def test_F4_planted_spike_dropped_by_centroid_recovered_by_rescue():
+    g = _gold("planted_spike.json")
+    q, k, T = _spike_fixture()
+    c, r = block_stats(k, T)
+    qbar = pool_queries(q, T)
+    assert abs(r[6] - g["spike_r"]) <= 1e-12
+    sel = select_blocks(qbar, c, r, 0.25, 0.10)
+    i = 7
+    assert abs(sel["Sc"][i, 6] - g["spike_Sc"]) <= 1e-12
+    assert abs(sel["Sr"][i, 6] - g["spike_Sr"]) <= 1e-12
+    assert abs(sel["Sc"][i, 1] - g["decoy_Sc"]) <= 1e-12
+    assert (k[6 * T:7 * T] @ qbar[i]).max() == g["spike_true_max"]
+    assert sel["k_c"][i] == 2 and sel["k_r"][i] == 1
+    assert set(np.flatnonzero(sel["C"][i])) == {1, 4}       # centroid branch: decoys only
+    assert set(np.flatnonzero(sel["R"][i])) == {6}          # rescue branch: the spike block
+    assert set(np.flatnonzero(sel["M"][i])) == {1, 4, 6}
+
+
+# ---------------------------------------------------------------- F5 -------
+def test_F5_block_stat_closed_forms():
+    rng = _rng(11)
+    key = rng.integers(-64, 64, 16) / 8.0     # dyadic: the block sum is exact
+    c, r = block_stats(np.tile(key, (8, 1)), 8)
+    assert np.abs(c[0] - key).max() <= 1e-15 and r[0] == 0.0
+    cen, u = rng.standard_normal(16), rng.standard_normal(16)
+    c, r = block_stats(np.stack([cen + u, cen - u]), 2)
+    assert np.abs(c[0] - cen).max() <= 1e-14
+    assert abs(r[0] - np.linalg.norm(u)) <= 1e-14
+    # blocks are independent and ordered: block j sees rows j*T..j*T+T-1
+    ks = np.concatenate([np.full((4, 3), j, dtype=np.float64) for j in range(5)])
+    c, r = block_stats(ks, 4)
+    assert (c[:, 0] == np.arange(5)).all() and (r == 0).all()
+
+
+def test_F5_pool_queries_block_means():
+    q = np.arange(24, dtype=np.float64).reshape(6, 4)
+    p = pool_queries(q, 3)
+    assert (p[0] == q[1]).all() and (p[1] == q[4]).all()  # mean of an arithmetic run is its middle
+
+
+# ---------------------------------------------------------------- F6 -------
+def _rank_topk(s, k):
+    """Brute force: keep j iff fewer than k entries beat it, where i beats j
+    when s_i > s_j or (s_i == s_j and i < j)."""
+    n = len(s)
+    keep = [j for j in range(n)
+            if sum(1 for i in range(n) if s[i] > s[j] or (s[i] == s[j] and i < j)) < k]
+    return np.array(keep)
+
+
+def test_F6_topk_special_cases_and_brute_force():
+    rng = _rng(12)
+    s = rng.standard_normal(50)
+    idx, kth = topk(s, 50)
+    assert (idx == np.arange(50)).all() and kth == s.min()
+    idx, kth = topk(s, 1)
+    assert idx.tolist() == [int(np.argmax(s))] and kth == s.max()
+    for k in (3, 7, 20):
+        idx, kth = topk(s, k)
+        assert (idx == np.sort(np.argpartition(-s, k - 1)[:k])).all()
+        assert (idx == _rank_topk(s, k)).all()
+        assert kth == np.sort(s)[::-1][k - 1]
+    # duplicated scores: lower indices win
+    d = np.array([1.0, 5.0, 3.0, 5.0, 3.0, 3.0, 0.0])
+    assert topk(d, 3)[0].tolist() == [1, 2, 3]
+    assert topk(d, 4)[0].tolist() == [1, 2, 3, 4]
+    for k in range(1, 8):
+        assert (topk(d, k)[0] == _rank_topk(d, k)).all()
+    with pytest.raises(ValueError):
+        topk(d, 0)
+
+
+def test_F6_selector_branches_match_brute_force_rank():
+    rng = _rng(13)
+    nB, D, T = 12, 5, 3
+    q = rng.standard_normal((nB * T, D))
+    k = rng.standard_normal((nB * T, D))
+    c, r = block_stats(k, T)
+    qbar = pool_queries(q, T)
+    sel = select_blocks(qbar, c, r, 0.3, 0.2, band_blocks=2, sink_blocks=1)
+    for i in range(nB):
+        n = i + 1
+        sc = np.array([qbar[i] @ c[j] for j in range(n)])
+        sr = sc + math.sqrt(qbar[i] @ qbar[i]) * r[:n]
+        kc = max(1, math.ceil(0.3 * n)); kr = max(1, math.ceil(0.2 * n))
+        assert set(np.flatnonzero(sel["C"][i])) == set(_rank_topk(sc, kc).tolist())
+        assert set(np.flatnonzero(sel["R"][i])) == set(_rank_topk(sr, kr).tolist())
+        forced = {0} | {j for j in range(max(0, i - 1), n)}
+        want = set(_rank_topk(sc, kc).tolist()) | set(_rank_topk(sr, kr).tolist()) | forced
+        assert set(np.flatnonzero(sel["M"][i])) == want
+        assert not sel["M"][i, n:].any()
+
+
+def test_F6_k_of_closed_values():
+    assert oracle.k_of(0.25, 16) == 4
+    assert oracle.k_of(0.25, 1) == 1
+    assert oracle.k_of(0.1, 10) == 1
+    assert oracle.k_of(0.1, 11) == 2
+    assert oracle.k_of(0.0, 9) == 1
+    assert oracle.k_of(1.5, 9) == 9
+    assert oracle.k_of(-1.0, 9) == 0
+
+
+# ---------------------------------------------------------------- F7 -------
+def test_F7_index_attention_full_index_set_is_dense_decode():
+    rng = _rng(14)
+    N, D = 300, 32
+    q = rng.standard_normal(D)
+    k, v = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    o, lse = index_attention(q, k, v, np.arange(N), 0.2)
+    ref = _sdpa(q[None], k, v, 0.2, causal=False)[0]
+    assert np.abs(o - ref).max() <= 1e-12
+    assert abs(lse - torch.logsumexp(torch.from_numpy(0.2 * (k @ q)), 0).item()) <= 1e-12
+    # order of the index list does not matter; -1 slots are skipped
+    perm = rng.permutation(N)
+    o2, _ = index_attention(q, k, v, np.concatenate([perm, [-1, -1]]), 0.2)
+    assert np.abs(o2 - o).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- F8 -------
+def test_F8_segment_modes():
+    rng = _rng(15)
+    n, D = 3000, 16
+    q = rng.standard_normal(D)
+    k, v = rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    og, _ = segment_attention(q, k, v, build_segments(oracle.SEG_GLOBAL, n), 0.25)
+    ref = _sdpa(q[None], k, v, 0.25, causal=False)[0]
+    assert np.abs(og - ref).max() <= 1e-12
+    loc = build_segments(oracle.SEG_LOCAL, 3008, local_len=1024)
+    assert loc == [(3008 - 1024, 3008)]
+    ol, _ = segment_attention(q, k, v, build_segments(oracle.SEG_LOCAL, n, local_len=1024), 0.25)
+    ref_l = _sdpa(q[None], k[n - 1024 - 8:], v[n - 1024 - 8:], 0.25, causal=False)[0]  # 3000-1024=1976 -> 1968
+    assert np.abs(ol - ref_l).max() <= 1e-12
+    st = build_segments(oracle.SEG_STREAMING, n, local_len=1024, n_sink=4)
+    assert st == [(0, 4), (n - 1024, n)]
+
+
+@pytest.mark.parametrize("start", [0, 1, 15, 16, 17, 1000, 2048 * 7 + 3, 100000 - 2048])
+def test_F8_focus_ranges_page_aligned_and_tight(start):
+    n, L, P = 100000, 2048, 16
+    rs = build_segments(oracle.SEG_FOCUS, n, chunk_start=start, chunk_len=L, local_len=1024, page=P)
+    covered = np.zeros(n, dtype=bool)
+    for a, b in rs:
+        assert a % P == 0 and (b % P == 0 or b == n)
+        covered[a:b] = True
+    assert covered[start:start + L].all() and covered[n - 1024:].all()
+    a0 = (start // P) * P
+    assert start - a0 <= P - 1
+    chunk = [r for r in rs if r[0] <= start < r[1]][0]
+    if chunk[1] < n - 1024:
+        assert chunk[1] - (start + L) <= P - 1
+
+
+def test_F8_golden_focus_segments():
+    g = _gold("focus_segments.json")
+    rs = build_segments(oracle.SEG_FOCUS, g["n"], g["chunk_start"], g["chunk_len"],
+                        g["local_len"], page=g["page"])
+    assert [list(r) for r in rs] == g["ranges"]
+
+
+# ---------------------------------------------------------------- F9 -------
+def test_F9_lse_combine_partition_invariant():
+    rng = _rng(16)
+    N, D = 200, 8
+    q = rng.standard_normal(D) * 2
+    k, v = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    o_ref, lse_ref = index_attention(q, k, v, np.arange(N), 1.0)
+    for trial in range(10):
+        perm = rng.permutation(N)
+        cuts = np.sort(rng.choice(np.arange(1, N), size=rng.integers(1, 9), replace=False))
+        parts = [oracle.attention_partial(q, k, v, s, 1.0) for s in np.split(perm, cuts)]
+        parts.append(oracle.attention_partial(q, k, v, np.zeros(0, dtype=int), 1.0))  # empty split
+        o, lse = lse_combine(parts)
+        assert np.abs(o - o_ref).max() <= 1e-12 and abs(lse - lse_ref) <= 1e-12
+
+
+def test_F9_golden_lse_combine():
+    g = _gold("lse_combine.json")
+    o, lse = lse_combine([(m, l, np.array(o)) for m, l, o in g["parts"]])
+    assert np.abs(o - np.array(g["o"])).max() <= 1e-15 and abs(lse - g["lse"]) <= 1e-15
+
+
+# ---------------------------------------------------------------- F10 ------
+def test_F10_paged_gather_identity_vs_shuffled():
+    rng = _rng(17)
+    P, Hkv, D, n_pages = 16, 3, 8, 40
+    seq = rng.standard_normal((n_pages * P, Hkv, D))
+    ident = seq.reshape(n_pages, P, Hkv, D).transpose(0, 2, 1, 3).copy()
+    perm = rng.permutation(n_pages)
+    shuf = np.zeros_like(ident)
+    shuf[perm] = ident                 # logical page p is stored at physical perm[p]
+    for g in range(Hkv):
+        for n in (1, 17, 300, n_pages * P):
+            a = gather_pages(ident, np.arange(n_pages), n, g)
+            b = gather_pages(shuf, perm, n, g)
+            assert (a == b).all() and (a == seq[:n, g]).all()
+
+
+# ---------------------------------------------------------------- F11 ------
+def test_F11_density_bookkeeping():
+    rng = _rng(18)
+    nB, T, D = 20, 4, 6
+    q, k = rng.standard_normal((nB * T, D)), rng.standard_normal((nB * T, D))
+    c, r = block_stats(k, T)
+    sel = select_blocks(pool_queries(q, T), c, r, 0.2, 0.08)
+    M = sel["M"]
+    executed = sum(int(M[i, j]) for i in range(nB) for j in range(nB))
+    assert executed == int(M.sum())
+    assert oracle.visible_count(nB) == sum(i + 1 for i in range(nB))
+    assert not np.triu(M, 1).any()
+    # every row keeps at least one visible block
+    assert (M.sum(1) >= 1).all()
+
+
+# ---------------------------------------------------------------- F12 ------
+def test_F12_causality():
+    rng = _rng(19)
+    S, D, T = 96, 8, 16
+    q, k, v = (rng.standard_normal((S, D)) for _ in range(3))
+    mask = rng.random((S // T, S // T)) < 0.5
+    np.fill_diagonal(mask, True)
+    o1, _ = masked_attention(q, k, v, mask, T, 0.4)
+    t = 37
+    k2, v2 = k.copy(), v.copy()
+    k2[t + 1:] = rng.standard_normal((S - t - 1, D))
+    v2[t + 1:] = rng.standard_normal((S - t - 1, D))
+    o2, _ = masked_attention(q, k2, v2, mask, T, 0.4)
+    assert (o1[:t + 1] == o2[:t + 1]).all()
+    assert np.abs(o1[t + 1:] - o2[t + 1:]).max() > 1e-3
+
+
+def test_masked_attention_equals_sdpa_with_explicit_mask():
+    """Block mask expanded to a token mask, run through the library routine."""
+    rng = _rng(20)
+    S, D, T = 128, 16, 16
+    q, k, v = (rng.standard_normal((S, D)) for _ in range(3))
+    mask = rng.random((S // T, S // T)) < 0.4
+    np.fill_diagonal(mask, True)
+    o, _ = masked_attention(q, k, v, mask, T, 0.25)
+    tok = np.kron(mask, np.ones((T, T), dtype=bool)) & np.tril(np.ones((S, S), dtype=bool))
+    t = lambda x: torch.from_numpy(x)[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=torch.from_numpy(tok)[None, None], scale=0.25)[0, 0].numpy()
+    assert np.abs(o - ref).max() <= 1e-12

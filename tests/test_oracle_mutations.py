@@ -1,0 +1,92 @@
+"""Planted mistakes in the oracle must fail at least one pin (CPU only).
+
+Each case swaps one oracle function, inside the pin module's namespace only,
+for a copy with a plausible bug (a dropped term, a flipped sign, an off-by-one
+index, a transposed operand, a wrong tie rule) and runs the pins that should
+catch it.  Nothing here touches the GPU or the HIP library.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as att
+from oracle import blocks as blk
+from tests import test_oracle_facts as pins
+
+
+def _rescue_sign_flipped(qbar, c, r, p_c, p_r, band_blocks=0, sink_blocks=0):
+    return blk.select_blocks(qbar, c, -np.asarray(r), p_c, p_r, band_blocks, sink_blocks)
+
+
+def _radius_is_mean_distance(k, T):
+    c, _ = blk.block_stats(k, T)
+    k = np.asarray(k, dtype=np.float64)
+    r = np.array([np.linalg.norm(k[j * T:(j + 1) * T] - c[j], axis=1).mean() for j in range(c.shape[0])])
+    return c, r
+
+
+def _dense_off_by_one(q, k, v, scale, causal=True):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    o = np.zeros((q.shape[0], v.shape[1])); lse = np.zeros(q.shape[0])
+    for t in range(q.shape[0]):
+        n = max(1, t) if causal else k.shape[0]
+        o[t], lse[t] = att._softmax_row(scale * (k[:n] @ q[t]), v[:n])
+    return o, lse
+
+
+def _topk_ties_high(scores, k):
+    s = np.asarray(scores, dtype=np.float64)
+    order = np.lexsort((-np.arange(s.size), -s))
+    return np.sort(order[:k]), s[order[k - 1]]
+
+
+def _combine_drops_l(parts):
+    return oracle.lse_combine([(m, 1.0 if l > 0 else 0.0, o) for m, l, o in parts])
+
+
+def _gather_ignores_table(pool, page_table, seq_len, g):
+    return oracle.gather_pages(pool, np.arange(len(page_table)), seq_len, g)
+
+
+def _masked_transposed(q, k, v, mask, T, scale):
+    return att.masked_attention(q, k, v, np.asarray(mask).T, T, scale)
+
+
+def _segments_not_rounded(mode, n, chunk_start=0, chunk_len=2048, local_len=1024, n_sink=4, page=16):
+    return oracle.build_segments(mode, n, chunk_start, chunk_len, local_len, n_sink, page=1)
+
+
+def _pool_uses_first_row(q, T):
+    q = np.asarray(q, dtype=np.float64)
+    return q[::T].copy()
+
+
+CASES = [
+    ("select_blocks", _rescue_sign_flipped,
+     [pins.test_F4_planted_spike_dropped_by_centroid_recovered_by_rescue]),
+    ("block_stats", _radius_is_mean_distance,
+     [lambda: pins.test_F3_rescue_bound_never_below_block_max(8, 8)]),
+    ("dense_attention", _dense_off_by_one,
+     [lambda: pins.test_F1_all_blocks_mask_is_dense_causal(8, 4, 2)]),
+    ("topk", _topk_ties_high, [pins.test_F6_topk_special_cases_and_brute_force]),
+    ("lse_combine", _combine_drops_l, [pins.test_F9_lse_combine_partition_invariant]),
+    ("gather_pages", _gather_ignores_table, [pins.test_F10_paged_gather_identity_vs_shuffled]),
+    ("masked_attention", _masked_transposed, [pins.test_masked_attention_equals_sdpa_with_explicit_mask]),
+    ("build_segments", _segments_not_rounded, [pins.test_F8_golden_focus_segments]),
+    ("pool_queries", _pool_uses_first_row, [pins.test_F5_pool_queries_block_means]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,catchers", CASES, ids=[c[0] for c in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant, catchers):
+    monkeypatch.setattr(pins, name, mutant)
+    caught = False
+    for fn in catchers:
+        try:
+            fn()
+        except AssertionError:
+            caught = True
+    assert caught, f"no pin caught a planted mistake in {name}"
