@@ -1,0 +1,325 @@
+// sparse_decode_attn: split-KV decode attention over a paged bf16 KV cache,
+// plus the log-sum-exp combine.
+//
+// Kascade post, "What Kascade got right": reuse layers attend only at the
+// anchor layer's per-head top-k indices (index mode).  Declarative Attention
+// post, "Declarative attention protocol": global / focus / local modes become
+// block-aligned token ranges that an unmodified attention kernel reads
+// (segment mode).  LoZA post, "4. From food delivery to AI":
+// SplitKV-and-Combine splits the KV reads and merges partial results.
+//
+// HBM-bound streaming design (no matrix cores: the contraction per KV row is
+// a handful of dot products):
+//   * a workgroup of 4 waves owns one (sequence, head-or-KV-head, split);
+//   * D/8 lanes share one 256-byte (D=128) key row: every lane issues one
+//     16-byte load for K and one for V, so a row is one contiguous,
+//     fully-used read; each lane group streams RB rows per step with all 2*RB
+//     loads in flight before any arithmetic;
+//   * scores use v_dot2_f32_bf16 on the raw bf16 pairs and a DPP butterfly
+//     across the lane group; in segment/all mode the G query heads of a KV
+//     head share every K/V read;
+//   * the softmax is online per lane group (one rescale per RB-row step);
+//     lane groups and waves merge through LDS at the end of the split and
+//     write an unnormalised (max, sum, output) partial in fp32;
+//   * combine_kernel merges the splits of one (sequence, head).
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace fsa {
+
+constexpr int kDecThreads = 256;
+constexpr int kMaxSeg = 64;  // segments per sequence kept in LDS
+
+template <int D, int NH, int MODE>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
+    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ pt,
+    const int32_t* __restrict__ sl, int Hq, int Hkv, int max_pages, int num_pages,
+    int max_seq_len, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ seg,
+    const int32_t* __restrict__ nseg, int max_seg, int n_split, float scale_log2,
+    float* __restrict__ part) {
+  constexpr int LPR = D / 8;            // lanes per key row
+  constexpr int RG = 64 / LPR;          // row groups per wave
+  constexpr int NSLOT = 4 * RG;         // row groups per workgroup
+  constexpr int RB = 4;                 // rows per row group per step
+  constexpr int NHEAD_ITEM = NH;
+  __shared__ float sm_m[4][NH], sm_l[4][NH];
+  __shared__ float sm_o[4][NH][D];
+  __shared__ int seg_lo[kMaxSeg], seg_pre[kMaxSeg + 1];
+  __shared__ int s_nseg;
+
+  const int G = Hq / Hkv;
+  const int s = blockIdx.x % n_split;
+  const int item = blockIdx.x / n_split;  // b * (heads per item layout) + hh
+  const int per_b = (MODE == FSA_SEL_INDEX) ? Hq : Hkv;
+  const int hh = item % per_b, b = item / per_b;
+  const int g = (MODE == FSA_SEL_INDEX) ? hh / G : hh;
+  const int h0 = (MODE == FSA_SEL_INDEX) ? hh : hh * G;  // first query head of the item
+  const int n = min(max(sl[b], 0), max_seq_len);
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int slot = wave * RG + l / LPR, dl = l % LPR;
+
+  // ---- this split's range of list positions
+  int total;
+  if constexpr (MODE == FSA_SEL_SEGMENT) {
+    if (tid == 0) {
+      int ns = nseg[b];
+      ns = ns < 0 ? 0 : (ns > max_seg ? max_seg : ns);
+      ns = ns > kMaxSeg ? kMaxSeg : ns;
+      int run = 0, c = 0;
+      for (int x = 0; x < ns; ++x) {
+        int a = seg[((size_t)b * max_seg + x) * 2], e = seg[((size_t)b * max_seg + x) * 2 + 1];
+        a = a < 0 ? 0 : a;
+        e = e > n ? n : e;
+        if (e > a) {
+          seg_lo[c] = a;
+          seg_pre[c] = run;
+          run += e - a;
+          ++c;
+        }
+      }
+      seg_pre[c] = run;
+      s_nseg = c;
+    }
+    __syncthreads();
+    total = seg_pre[s_nseg];
+  } else if constexpr (MODE == FSA_SEL_INDEX) {
+    total = k;
+  } else {
+    total = n;
+  }
+  int chunk = (total + n_split - 1) / n_split;
+  chunk = (chunk + 15) & ~15;
+  const int p0 = s * chunk;
+  const int p1 = min(total, p0 + chunk);
+
+  // ---- queries of the item: lane keeps its 8 d values of each head
+  uint4 qv[NH];
+#pragma unroll
+  for (int x = 0; x < NH; ++x)
+    qv[x] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h0 + x) * D + dl * 8);
+
+  float m_run[NH], l_run[NH], o[NH][8];
+#pragma unroll
+  for (int x = 0; x < NH; ++x) {
+    m_run[x] = -INFINITY;
+    l_run[x] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[x][e] = 0.f;
+  }
+  const int32_t* ptb = pt + (size_t)b * max_pages;
+  const int32_t* idxr = (MODE == FSA_SEL_INDEX) ? idx + ((size_t)b * Hq + hh) * k : nullptr;
+
+  for (int base = p0; base < p1; base += NSLOT * RB) {
+    uint4 kr[RB], vr[RB];
+    bool ok[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int pos = base + slot * RB + r;
+      int tok = -1;
+      if (pos < p1) {
+        if constexpr (MODE == FSA_SEL_INDEX) {
+          tok = idxr[pos];
+          if (tok >= n) tok = -1;
+        } else if constexpr (MODE == FSA_SEL_SEGMENT) {
+          int x = 0;
+          while (x + 1 < s_nseg && seg_pre[x + 1] <= pos) ++x;
+          tok = seg_lo[x] + (pos - seg_pre[x]);
+        } else {
+          tok = pos;
+        }
+      }
+      const int page = tok >= 0 ? ptb[tok >> 4] : -1;
+      ok[r] = page >= 0 && page < num_pages;  // bad page ids are skipped, never read
+      if (ok[r]) {
+        const size_t row = ((size_t)page * Hkv + g) * 16 + (tok & 15);
+        kr[r] = *reinterpret_cast<const uint4*>(kpool + row * D + dl * 8);
+        vr[r] = *reinterpret_cast<const uint4*>(vpool + row * D + dl * 8);
+      } else {
+        kr[r] = make_uint4(0, 0, 0, 0);
+        vr[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < NHEAD_ITEM; ++x) {
+      float sc[RB];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        float d = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
+        sc[r] = ok[r] ? d * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[r]);
+      }
+      const float m_new = fmaxf(m_run[x], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[x] - m_use);
+      m_run[x] = m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[x][e] *= alpha;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sc[r] - m_use);
+        ls += p;
+        const uint32_t w[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[x][2 * e] = fmaf(p, bf16_lo(w[e]), o[x][2 * e]);
+          o[x][2 * e + 1] = fmaf(p, bf16_hi(w[e]), o[x][2 * e + 1]);
+        }
+      }
+      l_run[x] = l_run[x] * alpha + ls;
+    }
+  }
+
+  // ---- merge the row groups of each wave (lanes LPR apart hold the same d
+  // values of different row groups), then the waves through LDS, and write
+  // the split's unnormalised partial (max, sum, output).
+#pragma unroll
+  for (int x = 0; x < NH; ++x) {
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      const float mo = __shfl_xor(m_run[x], off, 64);
+      const float lo = __shfl_xor(l_run[x], off, 64);
+      const float M = fmaxf(m_run[x], mo);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      const float ws = __builtin_amdgcn_exp2f(m_run[x] - Mu);
+      const float wo = __builtin_amdgcn_exp2f(mo - Mu);
+      l_run[x] = l_run[x] * ws + lo * wo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[x][e] = o[x][e] * ws + __shfl_xor(o[x][e], off, 64) * wo;
+      m_run[x] = M;
+    }
+    if (l < LPR) {
+      if (dl == 0) {
+        sm_m[wave][x] = m_run[x];
+        sm_l[wave][x] = l_run[x];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_o[wave][x][dl * 8 + e] = o[x][e];
+    }
+  }
+  __syncthreads();
+  for (int z = tid; z < NH * D; z += kDecThreads) {
+    const int x = z / D, d = z % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) M = fmaxf(M, sm_m[r][x]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f, Ov = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float w = __builtin_amdgcn_exp2f(sm_m[r][x] - Mu);
+      L += w * sm_l[r][x];
+      Ov += w * sm_o[r][x][d];
+    }
+    float* pp = part + (((size_t)b * Hq + h0 + x) * n_split + s) * (D + 2);
+    if (d == 0) {
+      pp[0] = M;
+      pp[1] = L;
+    }
+    pp[2 + d] = Ov;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part, int n_split,
+                                                     uint16_t* __restrict__ out,
+                                                     float* __restrict__ lse) {
+  const int bh = blockIdx.x, l = threadIdx.x;
+  const float* pp = part + (size_t)bh * n_split * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  constexpr int DPL = D / 64;
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const float* ps = pp + (size_t)s * (D + 2);
+    const float w = __builtin_amdgcn_exp2f(ps[0] - Mu);
+    L += w * ps[1];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += w * ps[2 + l * DPL + e];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) out[(size_t)bh * D + l * DPL + e] = f32_to_bf16(acc[e] * inv);
+  if (lse != nullptr && l == 0) lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split) {
+  if (n_split > 0) return n_split;
+  const int items = mode == FSA_SEL_INDEX ? d.B * d.Hq : d.B * d.Hkv;
+  const int len = mode == FSA_SEL_INDEX ? k : d.max_seq_len;
+  // aim for >= 2048 workgroups and >= 256 positions per split
+  int ns = (2048 + items - 1) / items;
+  const int cap = (len + 255) / 256;
+  if (ns > cap) ns = cap;
+  return ns < 1 ? 1 : ns;
+}
+
+size_t decode_ws_bytes(const DecodeDims& d, int mode, int k, int n_split) {
+  const int ns = decode_pick_split(d, mode, k, n_split);
+  return (size_t)d.B * d.Hq * ns * (d.D + 2) * sizeof(float);
+}
+
+template <int D>
+static hipError_t launch_dec_d(const void* q, const void* kp, const void* vp, const int32_t* pt,
+                               const int32_t* sl, const DecodeDims& d, int mode,
+                               const int32_t* idx, int k, const int32_t* seg,
+                               const int32_t* nseg, int max_seg, int ns, float sl2,
+                               void* out, float* lse, float* part, hipStream_t st) {
+  const uint16_t* Q = static_cast<const uint16_t*>(q);
+  const uint16_t* Kp = static_cast<const uint16_t*>(kp);
+  const uint16_t* Vp = static_cast<const uint16_t*>(vp);
+  const int G = d.Hq / d.Hkv;
+  if (mode == FSA_SEL_INDEX) {
+    hipLaunchKernelGGL((decode_split_kernel<D, 1, FSA_SEL_INDEX>), dim3(d.B * d.Hq * ns),
+                       dim3(kDecThreads), 0, st, Q, Kp, Vp, pt, sl, d.Hq, d.Hkv, d.max_pages,
+                       d.num_pages, d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part);
+  } else {
+#define FSA_DEC(GG, MM)                                                                        \
+  hipLaunchKernelGGL((decode_split_kernel<D, GG, MM>), dim3(d.B * d.Hkv * ns), dim3(kDecThreads), \
+                     0, st, Q, Kp, Vp, pt, sl, d.Hq, d.Hkv, d.max_pages, d.num_pages,           \
+                     d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part)
+#define FSA_DEC_G(GG)                         \
+  if (G == GG) {                              \
+    if (mode == FSA_SEL_SEGMENT)              \
+      FSA_DEC(GG, FSA_SEL_SEGMENT);           \
+    else                                      \
+      FSA_DEC(GG, FSA_SEL_ALL);               \
+  } else
+    FSA_DEC_G(1) FSA_DEC_G(2) FSA_DEC_G(4) FSA_DEC_G(8) { return hipErrorInvalidValue; }
+#undef FSA_DEC_G
+#undef FSA_DEC
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_kernel<D>, dim3(d.B * d.Hq), dim3(64), 0, st, part, ns,
+                     static_cast<uint16_t*>(out), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const void* q, const void* kpool, const void* vpool,
+                              const int32_t* pt, const int32_t* sl, const DecodeDims& d,
+                              int mode, const int32_t* idx, int k, const int32_t* seg,
+                              const int32_t* nseg, int max_seg, int n_split, float scale,
+                              void* out, float* lse, void* ws, hipStream_t st) {
+  const int ns = decode_pick_split(d, mode, k, n_split);
+  float* part = static_cast<float*>(ws);
+  const float sl2 = scale * kLog2e;
+  if (d.D == 128)
+    return launch_dec_d<128>(q, kpool, vpool, pt, sl, d, mode, idx, k, seg, nseg, max_seg, ns,
+                             sl2, out, lse, part, st);
+  if (d.D == 64)
+    return launch_dec_d<64>(q, kpool, vpool, pt, sl, d, mode, idx, k, seg, nseg, max_seg, ns,
+                            sl2, out, lse, part, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fsa

@@ -1,0 +1,52 @@
+// Internal launcher declarations shared by the C-ABI layer (fsa_api.cpp) and
+// the kernel translation units.  Host arguments arrive validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fsa.h"
+
+namespace fsa {
+
+struct PrefillDims {
+  int B, S, Hq, Hkv, D, T;
+};
+
+struct DecodeDims {
+  int B, Hq, Hkv, D, num_pages, max_pages, max_seq_len;
+};
+
+// block_stats.hip
+hipError_t launch_block_stats(bool f32, const void* k, float* cen, float* rad,
+                              const PrefillDims& d, hipStream_t st);
+
+// select_blocks.hip
+size_t select_ws_bytes(const PrefillDims& d);
+hipError_t launch_select_blocks(bool f32, const void* q, const float* cen, const float* rad,
+                                const PrefillDims& d, double p_c, double p_r, int band,
+                                int sink, uint32_t* mask, int32_t* bidx, int32_t* bcnt,
+                                float* score_c, float* score_r, void* ws, hipStream_t st);
+
+// prefill_attn.hip
+hipError_t launch_prefill_attn(bool f32, const void* q, const void* k, const void* v,
+                               const PrefillDims& d, const int32_t* bidx, const int32_t* bcnt,
+                               float scale, void* out, float* lse, hipStream_t st);
+
+// topk.hip
+size_t topk_ws_bytes(const DecodeDims& d, int k);
+hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
+                       const DecodeDims& d, int k, int32_t* idx, float* kth, void* ws,
+                       hipStream_t st);
+
+// decode_attn.hip
+int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split);
+size_t decode_ws_bytes(const DecodeDims& d, int mode, int k, int n_split);
+hipError_t launch_decode_attn(const void* q, const void* kpool, const void* vpool,
+                              const int32_t* pt, const int32_t* sl, const DecodeDims& d,
+                              int mode, const int32_t* idx, int k, const int32_t* seg,
+                              const int32_t* nseg, int max_seg, int n_split, float scale,
+                              void* out, float* lse, void* ws, hipStream_t st);
+
+}  // namespace fsa

@@ -1,0 +1,351 @@
+// sparse_prefill_attn: block-sparse causal flash-attention on gfx950 MFMA.
+//
+// RBS-Attention post, "Key technical points" 2: the merged block mask is
+// executed by an otherwise unchanged block-sparse FlashAttention path.
+//
+// Work unit: one workgroup per (batch, query head, query block i), T/32
+// waves, each wave owning 32 query rows.  The workgroup walks the ascending
+// key-block list of its row in 64-key chunks:
+//   * K chunk staged row-major in LDS, V chunk staged transposed (V^T) in LDS,
+//     the next chunk's global loads issued into registers before the current
+//     chunk's MFMAs (register double buffering);
+//   * S^T = K Q^T with the wave's Q tile resident in registers as the MFMA B
+//     operand, so each lane ends up holding one query row's scores: the row
+//     max needs one cross-half swap, the row sum none until the epilogue;
+//   * online softmax in fp32 with exp2 and log2(e) folded into the scale;
+//   * O^T += V^T P^T with P^T taken straight from registers as the B operand
+//     (the key order inside a 16-key MFMA step follows the S^T register
+//     layout; V^T is read from LDS in that same order).
+// bf16 inputs: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV step.
+// fp32 inputs: v_mfma_f32_32x32x2_f32, everything in fp32 (V kept row-major).
+// The diagonal block applies the element-wise causal mask; list entries
+// outside [0, i] are skipped.  Workgroups are mapped so that each XCD works
+// on a contiguous range of heads (shared K/V of a KV head stays in that XCD's
+// L2) and, within a head, the longest rows start first.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace fsa {
+
+template <typename TI, int D, int BLK>
+struct PrefillTraits {
+  static constexpr bool F32 = sizeof(TI) == 4;
+  static constexpr int NW = BLK / 32;  // waves per workgroup
+  static constexpr int NT = NW * 64;   // threads per workgroup
+  static constexpr int KC = 64;        // keys per chunk
+  static constexpr int NCH = BLK / KC; // chunks per key block
+  // LDS row pitches (elements), padded against bank conflicts
+  static constexpr int KP = F32 ? D + 4 : D + 8;
+  static constexpr int VP = F32 ? D + 4 : KC + 4;
+  static constexpr int VROWS = F32 ? KC : D;
+  static constexpr size_t LDS = (size_t)(KC * KP + VROWS * VP) * sizeof(TI);
+  // global->register staging work per thread
+  static constexpr int KPIECES = KC * D * sizeof(TI) / 16 / NT;  // 16-byte K pieces
+  static constexpr int VUNITS = F32 ? KPIECES : (KC / 4) * (D / 4) / NT;
+  static_assert(KPIECES >= 1 && VUNITS >= 1, "tile shape");
+};
+
+template <typename TI, int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) void prefill_attn_kernel(
+    const TI* __restrict__ Q, const TI* __restrict__ K, const TI* __restrict__ V,
+    const int32_t* __restrict__ bidx, const int32_t* __restrict__ bcnt, TI* __restrict__ O,
+    float* __restrict__ LSE, int S, int Hq, int Hkv, float scale_log2, int total) {
+  using Tr = PrefillTraits<TI, D, BLK>;
+  constexpr bool F32 = Tr::F32;
+  constexpr int KC = Tr::KC, NCH = Tr::NCH, KP = Tr::KP, VP = Tr::VP;
+  extern __shared__ __align__(16) unsigned char smem[];
+  TI* Ks = reinterpret_cast<TI*>(smem);
+  TI* Vs = Ks + KC * KP;
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= total) return;
+  const int nB = S / BLK;
+  const int i = nB - 1 - (L % nB);  // longest rows of a head first
+  const int bh = L / nB;
+  const int h = bh % Hq, b = bh / Hq;
+  const int g = h / (Hq / Hkv);
+  const int row = bh * nB + i;
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int lq = l & 31, lg = l >> 5;  // lane's query column / lane half
+  const int qrow = wave * 32 + lq;     // query row inside the block
+  const size_t kv_stride = (size_t)Hkv * D;
+  const TI* Kb = K + ((size_t)b * S * Hkv + g) * D;
+  const TI* Vb = V + ((size_t)b * S * Hkv + g) * D;
+
+  // ---- Q tile -> registers (MFMA B operand, lane = query row)
+  constexpr int QREG = F32 ? D / 2 : D / 16;
+  using QFrag = typename std::conditional<F32, float, bf16x8>::type;
+  QFrag qf[QREG];
+  {
+    const TI* qp = Q + (((size_t)b * S + (size_t)i * BLK + qrow) * Hq + h) * D;
+    if constexpr (F32) {
+      // lane half lg covers d in [lg*D/2, lg*D/2 + D/2)
+#pragma unroll
+      for (int kk = 0; kk < D / 2; kk += 4) {
+        float4 v4 = *reinterpret_cast<const float4*>(qp + lg * (D / 2) + kk);
+        qf[kk] = v4.x; qf[kk + 1] = v4.y; qf[kk + 2] = v4.z; qf[kk + 3] = v4.w;
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kk * 16 + lg * 8));
+    }
+  }
+
+  const int32_t* lst = bidx ? bidx + (size_t)row * nB : nullptr;
+  const int cnt = bidx ? min(max(bcnt[row], 0), nB) : i + 1;
+  const int nchunks = cnt * NCH;
+  auto block_of = [&](int c) -> int { return lst ? lst[c / NCH] : c / NCH; };
+  auto next_valid = [&](int c) -> int {
+    for (++c; c < nchunks; ++c) {
+      const int j = block_of(c);
+      if (j >= 0 && j <= i) break;
+    }
+    return c;
+  };
+
+  // ---- register staging of one chunk
+  uint4 kreg[Tr::KPIECES];
+  typename std::conditional<F32, uint4, uint2>::type vreg[Tr::VUNITS][F32 ? 1 : 4];
+  auto load_chunk = [&](int c) {
+    const int s0 = block_of(c) * BLK + (c % NCH) * KC;
+#pragma unroll
+    for (int m = 0; m < Tr::KPIECES; ++m) {
+      constexpr int PPR = D * sizeof(TI) / 16;  // pieces per key row
+      const int p = tid + m * Tr::NT;
+      const int key = p / PPR, pc = p % PPR;
+      kreg[m] = *reinterpret_cast<const uint4*>(Kb + (size_t)(s0 + key) * kv_stride +
+                                                pc * (16 / sizeof(TI)));
+    }
+    if constexpr (F32) {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        constexpr int PPR = D / 4;
+        const int p = tid + m * Tr::NT;
+        const int key = p / PPR, pc = p % PPR;
+        vreg[m][0] = *reinterpret_cast<const uint4*>(Vb + (size_t)(s0 + key) * kv_stride + pc * 4);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        const int u = tid + m * Tr::NT;
+        const int kq = u / (D / 4), dq = u % (D / 4);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          vreg[m][rr] = *reinterpret_cast<const uint2*>(Vb + (size_t)(s0 + kq * 4 + rr) * kv_stride +
+                                                         dq * 4);
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int m = 0; m < Tr::KPIECES; ++m) {
+      constexpr int PPR = D * sizeof(TI) / 16;
+      const int p = tid + m * Tr::NT;
+      const int key = p / PPR, pc = p % PPR;
+      *reinterpret_cast<uint4*>(Ks + key * KP + pc * (16 / sizeof(TI))) = kreg[m];
+    }
+    if constexpr (F32) {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        constexpr int PPR = D / 4;
+        const int p = tid + m * Tr::NT;
+        const int key = p / PPR, pc = p % PPR;
+        *reinterpret_cast<uint4*>(Vs + key * VP + pc * 4) = vreg[m][0];
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        const int u = tid + m * Tr::NT;
+        const int kq = u / (D / 4), dq = u % (D / 4);
+        const uint2 r0 = vreg[m][0], r1 = vreg[m][1], r2 = vreg[m][2], r3 = vreg[m][3];
+        uint2 c0, c1, c2, c3;  // column e of the 4x4 bf16 block = keys kq*4..+3 at d = dq*4+e
+        c0.x = (r0.x & 0xffffu) | (r1.x << 16);
+        c0.y = (r2.x & 0xffffu) | (r3.x << 16);
+        c1.x = (r0.x >> 16) | (r1.x & 0xffff0000u);
+        c1.y = (r2.x >> 16) | (r3.x & 0xffff0000u);
+        c2.x = (r0.y & 0xffffu) | (r1.y << 16);
+        c2.y = (r2.y & 0xffffu) | (r3.y << 16);
+        c3.x = (r0.y >> 16) | (r1.y & 0xffff0000u);
+        c3.y = (r2.y >> 16) | (r3.y & 0xffff0000u);
+        TI* vt = Vs + (dq * 4) * VP + kq * 4;
+        *reinterpret_cast<uint2*>(vt) = c0;
+        *reinterpret_cast<uint2*>(vt + VP) = c1;
+        *reinterpret_cast<uint2*>(vt + 2 * VP) = c2;
+        *reinterpret_cast<uint2*>(vt + 3 * VP) = c3;
+      }
+    }
+  };
+
+  floatx16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int c = next_valid(-1);
+  if (c < nchunks) load_chunk(c);
+  while (c < nchunks) {
+    __syncthreads();
+    store_chunk();
+    __syncthreads();
+    const int cn = next_valid(c);
+    if (cn < nchunks) load_chunk(cn);
+
+    const int j = block_of(c);
+    const int koff = (c % NCH) * KC;  // chunk's first key inside the block
+    const bool diag = (j == i);
+    // a wave whose queries all precede the chunk's keys has nothing to do
+    if (!(diag && koff > wave * 32 + 31)) {
+      floatx16 s[2];
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[tl][r] = 0.f;
+        const TI* kr = Ks + (tl * 32 + lq) * KP;
+        if constexpr (F32) {
+#pragma unroll
+          for (int kk = 0; kk < D / 2; kk += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(kr + lg * (D / 2) + kk);
+            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, qf[kk], s[tl], 0, 0, 0);
+            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, qf[kk + 1], s[tl], 0, 0, 0);
+            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, qf[kk + 2], s[tl], 0, 0, 0);
+            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, qf[kk + 3], s[tl], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + kk * 16 + lg * 8));
+            s[tl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[tl], 0, 0, 0);
+          }
+        }
+      }
+      // scale, causal mask, running max.  Register r of tile tl holds key
+      // koff + tl*32 + (r/4)*8 + lg*4 + r%4 for query qrow.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[tl][r] * scale_log2;
+          if (diag) {
+            const int key = koff + tl * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+            if (key > qrow) x = -INFINITY;
+          }
+          s[tl][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[tl][r] - m_use);
+          s[tl][r] = p;
+          l_run += p;
+        }
+      // O^T += V^T P^T
+      if constexpr (F32) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = tl * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+              const float a = Vs[key * VP + dt * 32 + lq];
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[tl][r], oacc[dt], 0, 0, 0);
+            }
+      } else {
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][(kc & 1) * 8 + e];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const TI* vr = Vs + (dt * 32 + lq) * VP;
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(vr + kc * 16 + lg * 4);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vr + kc * 16 + 8 + lg * 4);
+            const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kc],
+                                                                oacc[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    c = cn;
+  }
+
+  // ---- epilogue: O = O^T / l, LSE
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int t = i * BLK + qrow;
+  TI* op = O + (((size_t)b * S + t) * Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = dt * 32 + rg * 8 + lg * 4;
+      const float o0 = oacc[dt][rg * 4] * inv, o1 = oacc[dt][rg * 4 + 1] * inv;
+      const float o2 = oacc[dt][rg * 4 + 2] * inv, o3 = oacc[dt][rg * 4 + 3] * inv;
+      if constexpr (F32) {
+        *reinterpret_cast<float4*>(op + d0) = make_float4(o0, o1, o2, o3);
+      } else {
+        *reinterpret_cast<uint2*>(op + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      }
+    }
+  if (LSE != nullptr && lg == 0)
+    LSE[((size_t)b * Hq + h) * S + t] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+template <typename TI, int D, int BLK>
+static hipError_t launch_pa(const void* q, const void* k, const void* v, const PrefillDims& d,
+                            const int32_t* bidx, const int32_t* bcnt, float scale, void* out,
+                            float* lse, hipStream_t st) {
+  using Tr = PrefillTraits<TI, D, BLK>;
+  auto kern = prefill_attn_kernel<TI, D, BLK>;
+  if (Tr::LDS > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Tr::LDS);
+    if (e != hipSuccess) return e;
+  }
+  const int total = d.B * d.Hq * (d.S / BLK);
+  const int padded = (total + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(kern, dim3(padded), dim3(Tr::NT), Tr::LDS, st, static_cast<const TI*>(q),
+                     static_cast<const TI*>(k), static_cast<const TI*>(v), bidx, bcnt,
+                     static_cast<TI*>(out), lse, d.S, d.Hq, d.Hkv, scale * kLog2e, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(bool f32, const void* q, const void* k, const void* v,
+                               const PrefillDims& d, const int32_t* bidx, const int32_t* bcnt,
+                               float scale, void* out, float* lse, hipStream_t st) {
+#define FSA_PA(TY, DD, TT) \
+  if (d.D == DD && d.T == TT) return launch_pa<TY, DD, TT>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (f32) {
+    FSA_PA(float, 64, 64) FSA_PA(float, 64, 128) FSA_PA(float, 128, 64) FSA_PA(float, 128, 128)
+  } else {
+    FSA_PA(uint16_t, 64, 64) FSA_PA(uint16_t, 64, 128) FSA_PA(uint16_t, 128, 64)
+    FSA_PA(uint16_t, 128, 128)
+  }
+#undef FSA_PA
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fsa

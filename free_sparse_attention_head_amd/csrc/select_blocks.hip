@@ -1,0 +1,329 @@
+// select_blocks: RBS-style two-branch block selection and mask merge.
+//
+// RBS-Attention post, "Key technical points" 1-2: a centroid base branch and
+// a radius rescue branch, each thresholded independently, masks merged, and
+// the block-sparse attention path left unchanged.
+//
+// Three kernels, all stream-ordered:
+//   1. pool_queries_kernel: qbar[b,h,i,:] = mean of the T query rows of block i
+//      (one workgroup per (b, i): the T x Hq x D slab is contiguous in HBM and
+//      read once with 16-byte loads).
+//   2. centroid_score_kernel: Sc[b,h,i,j] = qbar_i . c_j for j <= i, as 64x64
+//      fp32 register-blocked tiles of the lower triangle (LDS-staged operands,
+//      4x4 outputs per thread, sequential accumulation over d).
+//   3. select_rows_kernel: one workgroup per row (b,h,i): Sr = Sc + ||qbar||*r,
+//      exact top-k of each branch by a 4-pass 8-bit radix select on
+//      order-preserving keys held in registers (ties go to the lower block
+//      index through an exclusive scan of the equal-key flags), union with
+//      the forced sink/band blocks, compaction into an ascending block list
+//      with a workgroup scan, and the bitmask row.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace fsa {
+
+// ---------------------------------------------------------------- pooling
+template <typename TI>
+__global__ __launch_bounds__(256) void pool_queries_kernel(const TI* __restrict__ Q,
+                                                           float* __restrict__ qbar, int S,
+                                                           int Hq, int D, int T) {
+  constexpr int VPT = 16 / sizeof(TI);
+  const int nB = S / T;
+  const int i = blockIdx.x % nB, b = blockIdx.x / nB;
+  const int NC = Hq * D / VPT;  // 16-byte column groups of one token row
+  const size_t row_elems = (size_t)Hq * D;
+  const TI* base = Q + ((size_t)b * S + (size_t)i * T) * row_elems;
+  for (int cg = threadIdx.x; cg < NC; cg += blockDim.x) {
+    float acc[VPT];
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) acc[e] = 0.f;
+    for (int t = 0; t < T; ++t) {
+      uint4 w = *reinterpret_cast<const uint4*>(base + t * row_elems + cg * VPT);
+      if constexpr (sizeof(TI) == 2) {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_lo(ws[e]);
+          acc[2 * e + 1] += bf16_hi(ws[e]);
+        }
+      } else {
+        acc[0] += __uint_as_float(w.x);
+        acc[1] += __uint_as_float(w.y);
+        acc[2] += __uint_as_float(w.z);
+        acc[3] += __uint_as_float(w.w);
+      }
+    }
+    const int h = (cg * VPT) / D, d0 = (cg * VPT) % D;
+    float* out = qbar + (((size_t)b * Hq + h) * nB + i) * D + d0;
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) out[e] = acc[e] / (float)T;
+  }
+}
+
+// ---------------------------------------------------------------- scores
+constexpr int kTile = 64, kDc = 32;
+
+__global__ __launch_bounds__(256) void centroid_score_kernel(const float* __restrict__ qbar,
+                                                             const float* __restrict__ cen,
+                                                             float* __restrict__ sc, int Hq,
+                                                             int Hkv, int nB, int D, int tiles) {
+  __shared__ float As[kDc][kTile + 4];
+  __shared__ float Bs[kDc][kTile + 4];
+  const int x = blockIdx.x % tiles, bh = blockIdx.x / tiles;
+  const int h = bh % Hq, b = bh / Hq, g = h / (Hq / Hkv);
+  // x -> (it, jt) with jt <= it, row-major over the lower triangle
+  int it = (int)((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
+  while ((it + 1) * (it + 2) / 2 <= x) ++it;
+  while (it * (it + 1) / 2 > x) --it;
+  const int jt = x - it * (it + 1) / 2;
+  const float* A = qbar + ((size_t)b * Hq + h) * nB * D;
+  const float* Bm = cen + ((size_t)b * Hkv + g) * nB * D;
+  const int t = threadIdx.x, ty = t / 16, tx = t % 16;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
+  for (int d0 = 0; d0 < D; d0 += kDc) {
+    // stage 64 rows x 32 d of each operand, transposed to [d][row]
+    for (int e = t; e < kTile * kDc; e += 256) {
+      const int r = e / kDc, dd = e % kDc;
+      const int ia = it * kTile + r, jb = jt * kTile + r;
+      As[dd][r] = ia < nB ? A[(size_t)ia * D + d0 + dd] : 0.f;
+      Bs[dd][r] = jb < nB ? Bm[(size_t)jb * D + d0 + dd] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int dd = 0; dd < kDc; ++dd) {
+      const float4 av = *reinterpret_cast<const float4*>(&As[dd][ty * 4]);
+      const float4 bv = *reinterpret_cast<const float4*>(&Bs[dd][tx * 4]);
+      const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(ar[a], br[c], acc[a][c]);
+    }
+    __syncthreads();
+  }
+  float* out = sc + ((size_t)b * Hq + h) * nB * nB;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = it * kTile + ty * 4 + a;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = jt * kTile + tx * 4 + c;
+      if (i < nB && j <= i) out[(size_t)i * nB + j] = acc[a][c];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- selection
+struct SelShared {
+  uint32_t hist[256];
+  int misc[2];
+  int scan[17];
+  uint32_t words[128];
+  float qn;
+};
+
+// Exact k-th largest key among the valid entries (4 passes of 8-bit digits).
+// Returns the key value K* and how many entries equal to K* are still needed.
+template <int E>
+__device__ void radix_kth(const uint32_t (&key)[E], const bool (&valid)[E], int k, SelShared& sh,
+                          uint32_t& kstar, int& need_eq) {
+  uint32_t prefix = 0, pmask = 0;
+  int kk = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int q = threadIdx.x; q < 256; q += blockDim.x) sh.hist[q] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (valid[e] && (key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      const int c0 = sh.hist[255 - 4 * l], c1 = sh.hist[254 - 4 * l];
+      const int c2 = sh.hist[253 - 4 * l], c3 = sh.hist[252 - 4 * l];
+      const int s = c0 + c1 + c2 + c3;
+      const int inc = wave_incl_scan(s);
+      const int exc = inc - s;
+      if (exc < kk && kk <= inc) {
+        int above = exc, d;
+        if (kk <= above + c0) {
+          d = 255 - 4 * l;
+        } else if (kk <= above + c0 + c1) {
+          above += c0;
+          d = 254 - 4 * l;
+        } else if (kk <= above + c0 + c1 + c2) {
+          above += c0 + c1;
+          d = 253 - 4 * l;
+        } else {
+          above += c0 + c1 + c2;
+          d = 252 - 4 * l;
+        }
+        sh.misc[0] = d;
+        sh.misc[1] = above;
+      }
+    }
+    __syncthreads();
+    kk -= sh.misc[1];
+    prefix |= (uint32_t)sh.misc[0] << shift;
+    pmask |= 255u << shift;
+  }
+  kstar = prefix;
+  need_eq = kk;
+}
+
+// Top-k membership flags, ties to the lower index (entries are contiguous per
+// thread, so a workgroup exclusive scan of equal-key counts ranks ties in
+// index order).
+template <int E>
+__device__ void topk_flags(const uint32_t (&key)[E], const bool (&valid)[E], int k, SelShared& sh,
+                           bool (&sel)[E]) {
+  if (k <= 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sel[e] = false;
+    return;
+  }
+  uint32_t ks;
+  int need;
+  radix_kth<E>(key, valid, k, sh, ks, need);
+  int neq = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) neq += (valid[e] && key[e] == ks) ? 1 : 0;
+  int tot;
+  int rank = block_excl_scan(neq, sh.scan, &tot);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    bool eq = valid[e] && key[e] == ks;
+    sel[e] = valid[e] && (key[e] > ks || (eq && rank < need));
+    rank += eq ? 1 : 0;
+  }
+}
+
+__device__ __forceinline__ int k_of(double p, int n) {
+  if (p < 0.0) return 0;
+  double x = ceil(p * (double)n);
+  int k = x < 1.0 ? 1 : (x > (double)n ? n : (int)x);
+  return k;
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void select_rows_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ sc, const float* __restrict__ rad,
+    uint32_t* __restrict__ mask, int32_t* __restrict__ bidx, int32_t* __restrict__ bcnt,
+    float* __restrict__ score_r, int Hq, int Hkv, int nB, int D, double p_c, double p_r,
+    int band, int sink) {
+  __shared__ SelShared sh;
+  const int row = blockIdx.x;  // (b*Hq + h)*nB + i
+  const int i = row % nB, bh = row / nB, h = bh % Hq, b = bh / Hq;
+  const int g = h / (Hq / Hkv);
+  const int n = i + 1;
+  const int t = threadIdx.x;
+  const int nw = (nB + 31) / 32;
+
+  if (t < 64) {
+    const float* qr = qbar + (size_t)row * D;
+    float s = 0.f;
+    for (int d = t; d < D; d += 64) s += qr[d] * qr[d];
+    s = wave_sum(s);
+    if (t == 0) sh.qn = sqrtf(s);
+  }
+  for (int w = t; w < nw; w += blockDim.x) sh.words[w] = 0u;
+  __syncthreads();
+  const float qn = sh.qn;
+
+  uint32_t kc[E], kr[E];
+  bool valid[E];
+  const float* scr = sc + (size_t)row * nB;
+  const float* rr = rad + ((size_t)b * Hkv + g) * nB;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = t * E + e;
+    valid[e] = j < n;
+    const float s = valid[e] ? scr[j] : 0.f;
+    const float r = valid[e] ? fmaf(qn, rr[j], s) : 0.f;
+    kc[e] = order_key(s);
+    kr[e] = order_key(r);
+    if (score_r != nullptr && valid[e]) score_r[(size_t)row * nB + j] = r;
+  }
+  bool selc[E], selr[E];
+  topk_flags<E>(kc, valid, k_of(p_c, n), sh, selc);
+  topk_flags<E>(kr, valid, k_of(p_r, n), sh, selr);
+
+  int cnt = 0;
+  bool m[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = t * E + e;
+    const bool forced = (j < sink) || (band > 0 && j > i - band);
+    m[e] = valid[e] && (selc[e] || selr[e] || forced);
+    cnt += m[e] ? 1 : 0;
+  }
+  int tot;
+  int pos = block_excl_scan(cnt, sh.scan, &tot);
+  int32_t* lst = bidx + (size_t)row * nB;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (m[e]) {
+      const int j = t * E + e;
+      lst[pos++] = j;
+      atomicOr(&sh.words[j >> 5], 1u << (j & 31));
+    }
+  }
+  if (t == 0) bcnt[row] = tot;
+  __syncthreads();
+  for (int w = t; w < nw; w += blockDim.x) mask[(size_t)row * nw + w] = sh.words[w];
+}
+
+size_t select_ws_bytes(const PrefillDims& d) {
+  const size_t nB = d.S / d.T;
+  const size_t qb = (size_t)d.B * d.Hq * nB * d.D * sizeof(float);
+  const size_t sc = (size_t)d.B * d.Hq * nB * nB * sizeof(float);
+  return ((qb + 255) / 256) * 256 + sc;
+}
+
+hipError_t launch_select_blocks(bool f32, const void* q, const float* cen, const float* rad,
+                                const PrefillDims& d, double p_c, double p_r, int band,
+                                int sink, uint32_t* mask, int32_t* bidx, int32_t* bcnt,
+                                float* score_c, float* score_r, void* ws, hipStream_t st) {
+  const int nB = d.S / d.T;
+  float* qbar = static_cast<float*>(ws);
+  const size_t qb = (size_t)d.B * d.Hq * nB * d.D * sizeof(float);
+  float* sc = score_c ? score_c
+                      : reinterpret_cast<float*>(static_cast<char*>(ws) + ((qb + 255) / 256) * 256);
+  if (f32)
+    hipLaunchKernelGGL(pool_queries_kernel<float>, dim3(d.B * nB), dim3(256), 0, st,
+                       static_cast<const float*>(q), qbar, d.S, d.Hq, d.D, d.T);
+  else
+    hipLaunchKernelGGL(pool_queries_kernel<uint16_t>, dim3(d.B * nB), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), qbar, d.S, d.Hq, d.D, d.T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nt = (nB + kTile - 1) / kTile;
+  const int tiles = nt * (nt + 1) / 2;
+  hipLaunchKernelGGL(centroid_score_kernel, dim3(d.B * d.Hq * tiles), dim3(256), 0, st, qbar, cen,
+                     sc, d.Hq, d.Hkv, nB, d.D, tiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(d.B * d.Hq * nB);
+#define FSA_SEL(EE)                                                                            \
+  hipLaunchKernelGGL(select_rows_kernel<EE>, grid, dim3(256), 0, st, qbar, sc, rad, mask, bidx, \
+                     bcnt, score_r, d.Hq, d.Hkv, nB, d.D, p_c, p_r, band, sink)
+  if (nB <= 256)
+    FSA_SEL(1);
+  else if (nB <= 512)
+    FSA_SEL(2);
+  else if (nB <= 1024)
+    FSA_SEL(4);
+  else if (nB <= 2048)
+    FSA_SEL(8);
+  else
+    FSA_SEL(16);
+#undef FSA_SEL
+  return hipGetLastError();
+}
+
+}  // namespace fsa

@@ -1,0 +1,278 @@
+// topk_indices: exact per-head top-k over a paged bf16 key cache.
+//
+// Kascade post, "What Kascade got right": an anchor layer computes exact
+// Top-k key indices; "Head-aware is the key to accuracy": one set per
+// attention head.  Raw scores q.k in fp32; ties go to the lower token index;
+// the index set is written ascending.
+//
+// Kernels (stream-ordered):
+//   1. fill_kernel: clears the per-row digit histograms (a plain store kernel,
+//      safe under graph capture).
+//   2. topk_score_kernel: streams K once from HBM through the page table; the
+//      G query heads of a KV head share every 256-byte key row (16 lanes x
+//      16 bytes, v_dot2_f32_bf16 + DPP butterfly).  Writes the fp32 score row
+//      of every query head and accumulates, in LDS, a histogram of the top 11
+//      bits of the order-preserving score key, flushed with one global atomic
+//      per non-empty bin.
+//   3. topk_select_kernel: one 1024-thread workgroup per (sequence, head).
+//      Digit 1 comes from the fused histogram; digits 2 (11 bits) and 3
+//      (10 bits) are histogrammed over the candidates sharing the prefix.
+//      This yields the exact k-th key K* and how many keys equal to K* are
+//      taken.  A final pass in index order keeps key > K*, plus the first keys
+//      equal to K*, compacting positions with workgroup scans so that the
+//      output is ascending.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace fsa {
+
+constexpr int kTopkTile = 4096;   // tokens per score workgroup
+constexpr int kBins1 = 2048;      // digit 1: key bits 31..21
+constexpr int kSelThreads = 1024;
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
+       x += (size_t)gridDim.x * blockDim.x)
+    p[x] = v;
+}
+
+static inline int seq_stride(int max_seq_len) { return (max_seq_len + 15) & ~15; }
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void topk_score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ sl, int Hq, int Hkv,
+    int max_pages, int num_pages, int max_seq_len, int stride, int tiles,
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  constexpr int LPR = D / 8, RG = 64 / LPR, NSLOT = 4 * RG, RB = 4;
+  __shared__ uint32_t lh[G][kBins1];
+  const int tile = blockIdx.x % tiles;
+  const int bg = blockIdx.x / tiles;
+  const int g = bg % Hkv, b = bg / Hkv;
+  const int n = min(max(sl[b], 0), max_seq_len);
+  const int t0 = tile * kTopkTile;
+  if (t0 >= n) return;
+  const int t1 = min(n, t0 + kTopkTile);
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int slot = wave * RG + l / LPR, dl = l % LPR;
+  for (int x = tid; x < G * kBins1; x += 256) (&lh[0][0])[x] = 0u;
+
+  uint4 qv[G];
+#pragma unroll
+  for (int x = 0; x < G; ++x)
+    qv[x] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * G + x) * D + dl * 8);
+  const int32_t* ptb = pt + (size_t)b * max_pages;
+  __syncthreads();
+
+  for (int base = t0; base < t1; base += NSLOT * RB) {
+    uint4 kr[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int tok = base + slot * RB + r;
+      const int page = tok < t1 ? ptb[tok >> 4] : -1;
+      if (page >= 0 && page < num_pages) {  // a bad page id scores as a zero key
+        const size_t row = ((size_t)page * Hkv + g) * 16 + (tok & 15);
+        kr[r] = *reinterpret_cast<const uint4*>(kpool + row * D + dl * 8);
+      } else {
+        kr[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float sc[G][RB];
+#pragma unroll
+    for (int x = 0; x < G; ++x)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) sc[x][r] = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
+    // lane dl writes score (x, r) for z = x*RB + r = dl, dl + LPR, ...
+#pragma unroll
+    for (int z = 0; z < G * RB; ++z) {
+      if (z % LPR != dl) continue;
+      const int x = z / RB, r = z % RB;
+      const int tok = base + slot * RB + r;
+      if (tok < t1) {
+        const float v = sc[x][r] + 0.0f;
+        scores[((size_t)b * Hq + g * G + x) * stride + tok] = v;
+        atomicAdd(&lh[x][order_key(v) >> 21], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < G * kBins1; x += 256) {
+    const uint32_t c = (&lh[0][0])[x];
+    if (c) atomicAdd(&hist[((size_t)b * Hq + g * G + x / kBins1) * kBins1 + x % kBins1], c);
+  }
+}
+
+struct TopkShared {
+  uint32_t hist[kBins1];
+  int scan[17];
+  int dig, above;
+};
+
+// Among nbins (1024 or 2048) histogram bins in LDS, find the bin holding the
+// kk-th largest element (bins scanned from the top).  Every thread calls it.
+__device__ void find_digit(TopkShared& sh, int nbins, int kk, int& digit, int& above) {
+  const int t = threadIdx.x;
+  const int per = nbins / kSelThreads;  // 1 or 2, bins owned by thread t, descending
+  const int top = nbins - 1 - per * t;
+  int c0 = (int)sh.hist[top];
+  int c1 = per == 2 ? (int)sh.hist[top - 1] : 0;
+  int tot;
+  const int exc = block_excl_scan(c0 + c1, sh.scan, &tot);
+  if (exc < kk && kk <= exc + c0 + c1) {
+    if (kk <= exc + c0) {
+      sh.dig = top;
+      sh.above = exc;
+    } else {
+      sh.dig = top - 1;
+      sh.above = exc + c0;
+    }
+  }
+  __syncthreads();
+  digit = sh.dig;
+  above = sh.above;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ sl, int Hq, int max_seq_len, int stride, int k,
+    int32_t* __restrict__ idx, float* __restrict__ kth) {
+  __shared__ TopkShared sh;
+  const int row = blockIdx.x, b = row / Hq;
+  const int n = min(max(sl[b], 0), max_seq_len);
+  const int t = threadIdx.x;
+  int32_t* out = idx + (size_t)row * k;
+  const float* sr = scores + (size_t)row * stride;
+  if (n < k) {
+    for (int x = t; x < k; x += kSelThreads) out[x] = x < n ? x : -1;
+    if (kth != nullptr && t == 0) kth[row] = -INFINITY;
+    return;
+  }
+  // digit 1 from the fused histogram
+  for (int x = t; x < kBins1; x += kSelThreads) sh.hist[x] = hist[(size_t)row * kBins1 + x];
+  __syncthreads();
+  int kk = k, d, above;
+  find_digit(sh, kBins1, kk, d, above);
+  kk -= above;
+  uint32_t prefix = (uint32_t)d << 21, pmask = 0xffe00000u;
+  // digits 2 and 3 over the candidates sharing the prefix
+  const int shifts[2] = {10, 0};
+  const int nbins[2] = {2048, 1024};
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int x = t; x < nbins[pass]; x += kSelThreads) sh.hist[x] = 0u;
+    __syncthreads();
+    const uint32_t dmask = (uint32_t)nbins[pass] - 1u;
+    for (int j0 = 4 * t; j0 < n; j0 += 4 * kSelThreads) {
+      float v[4];
+      if (j0 + 3 < n) {
+        const float4 f = *reinterpret_cast<const float4*>(sr + j0);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = j0 + e < n ? sr[j0 + e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key(v[e]);
+        if (j0 + e < n && (key & pmask) == prefix)
+          atomicAdd(&sh.hist[(key >> shifts[pass]) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    find_digit(sh, nbins[pass], kk, d, above);
+    kk -= above;
+    prefix |= (uint32_t)d << shifts[pass];
+    pmask |= dmask << shifts[pass];
+  }
+  const uint32_t kstar = prefix;
+  const int need_eq = kk;
+  // output pass in index order: keep key > K*, and the first need_eq keys == K*
+  int eq_before = 0, out_before = 0;
+  for (int base = 0; base < n; base += 4 * kSelThreads) {
+    const int j0 = base + 4 * t;
+    uint32_t key[4];
+    bool valid[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      valid[e] = j0 + e < n;
+      key[e] = valid[e] ? order_key(sr[j0 + e]) : 0u;
+    }
+    int neq = 0, ngt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      neq += (valid[e] && key[e] == kstar) ? 1 : 0;
+      ngt += (valid[e] && key[e] > kstar) ? 1 : 0;
+    }
+    // one scan carries both counts: equal keys in the high half
+    int tot;
+    const int ex = block_excl_scan((neq << 16) | ngt, sh.scan, &tot);
+    int eq_rank = eq_before + (ex >> 16);
+    int gt_rank = ex & 0xffff;
+    // output position = keys kept before this thread's first element: all of
+    // out_before, this iteration's greater keys before it, and the equal keys
+    // before it that still fit under need_eq
+    int pos = out_before + gt_rank + min(eq_rank, need_eq) - min(eq_before, need_eq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!valid[e]) continue;
+      if (key[e] > kstar) {
+        if (pos < k) out[pos] = j0 + e;
+        ++pos;
+      } else if (key[e] == kstar) {
+        if (eq_rank < need_eq) {
+          if (pos < k) out[pos] = j0 + e;
+          ++pos;
+        }
+        ++eq_rank;
+      }
+    }
+    const int teq = tot >> 16, tgt = tot & 0xffff;
+    out_before += tgt + max(0, min(teq, need_eq - eq_before));
+    eq_before += teq;
+  }
+  if (kth != nullptr && t == 0) kth[row] = key_to_float(kstar);
+}
+
+size_t topk_ws_bytes(const DecodeDims& d, int k) {
+  (void)k;
+  const size_t sc = (size_t)d.B * d.Hq * seq_stride(d.max_seq_len) * sizeof(float);
+  const size_t hs = (size_t)d.B * d.Hq * kBins1 * sizeof(uint32_t);
+  return ((sc + 255) / 256) * 256 + hs;
+}
+
+hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
+                       const DecodeDims& d, int k, int32_t* idx, float* kth, void* ws,
+                       hipStream_t st) {
+  const int stride = seq_stride(d.max_seq_len);
+  float* scores = static_cast<float*>(ws);
+  const size_t sc = (size_t)d.B * d.Hq * stride * sizeof(float);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + ((sc + 255) / 256) * 256);
+  const size_t nh = (size_t)d.B * d.Hq * kBins1;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + 255) / 256 < 4096 ? (nh + 255) / 256 : 4096)),
+                     dim3(256), 0, st, hist, nh, 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tiles = (d.max_seq_len + kTopkTile - 1) / kTopkTile;
+  const int G = d.Hq / d.Hkv;
+  const uint16_t* Q = static_cast<const uint16_t*>(q);
+  const uint16_t* Kp = static_cast<const uint16_t*>(kpool);
+  const dim3 grid(d.B * d.Hkv * tiles);
+#define FSA_TS(DD, GG)                                                                      \
+  if (d.D == DD && G == GG) {                                                               \
+    hipLaunchKernelGGL((topk_score_kernel<DD, GG>), grid, dim3(256), 0, st, Q, Kp, pt, sl, d.Hq, \
+                       d.Hkv, d.max_pages, d.num_pages, d.max_seq_len, stride, tiles, scores, \
+                       hist);                                                               \
+  } else
+  FSA_TS(128, 1) FSA_TS(128, 2) FSA_TS(128, 4) FSA_TS(128, 8) FSA_TS(64, 1) FSA_TS(64, 2)
+  FSA_TS(64, 4) FSA_TS(64, 8) { return hipErrorInvalidValue; }
+#undef FSA_TS
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * d.Hq), dim3(kSelThreads), 0, st, scores, hist,
+                     sl, d.Hq, d.max_seq_len, stride, k, idx, kth);
+  return hipGetLastError();
+}
+
+}  // namespace fsa

@@ -1,0 +1,223 @@
+/*
+ * fsa.h -- C ABI of the head-aware sparse attention library for AMD MI355X
+ * (gfx950).  Five entry points run the hot path on the GPU; three helpers
+ * size workspaces, build decode segment masks on the host and name status
+ * codes.
+ *
+ * Conventions shared by every call
+ *   - Pointers marked (device) are HIP device memory owned by the caller;
+ *     the library never allocates, frees or keeps them.  Pointers marked
+ *     (host) are ordinary host memory read before the call returns.
+ *   - Tensors are dense, row-major (C order), with the shapes given below;
+ *     bf16 is IEEE bfloat16 stored in 16 bits, fp32 is IEEE binary32.
+ *   - Every entry point validates its host-side arguments before any launch
+ *     and returns FSA_OK (0) or a negative FSA_ERR_* code; nothing aborts,
+ *     exits or throws across the ABI.  Kernel work is enqueued
+ *     asynchronously on the caller's stream `st` (0 = the null stream);
+ *     launch failures are reported as FSA_ERR_LAUNCH, device faults surface
+ *     at the caller's next synchronisation.
+ *   - Calls are re-entrant; consecutive calls on one stream see each other's
+ *     results (stream order).  The library keeps no mutable global state.
+ *
+ * Prefill shapes: batch B, prompt length S, query heads Hq, KV heads Hkv
+ * (Hq % Hkv == 0, G = Hq / Hkv, query head h reads KV head h / G), head dim
+ * D in {64, 128}, block size T in {64, 128} (query block = key block),
+ * S % T == 0, nB = S / T <= 4096.
+ * Decode shapes: page size 16 tokens, KV pool [num_pages, Hkv, 16, D] bf16,
+ * token j of sequence b at pool[page_table[b * max_pages + j / 16], g,
+ * j % 16, :].
+ */
+#ifndef FSA_H
+#define FSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  FSA_OK = 0,
+  FSA_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  FSA_ERR_SHAPE = -2,     /* a shape or size rule is violated                    */
+  FSA_ERR_DTYPE = -3,     /* dtype not supported by this call                    */
+  FSA_ERR_WORKSPACE = -4, /* ws_bytes smaller than fsa_workspace_size() asks for */
+  FSA_ERR_NO_DEVICE = -5, /* no usable gfx950 device is current                  */
+  FSA_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch            */
+  FSA_ERR_ARG = -7        /* another argument is out of range                    */
+};
+
+typedef enum { FSA_BF16 = 0, FSA_F32 = 1 } fsa_dtype;
+
+typedef struct {
+  int32_t B, S, Hq, Hkv, D, T;
+} fsa_prefill_shape;
+
+/* Two-branch selector parameters (host struct).
+ * Branch keep counts per query block i with n_i = i + 1 visible key blocks:
+ * k = max(1, ceil(p * n_i)) capped at n_i, the product formed in IEEE
+ * double; p < 0 switches that branch off.  Forced blocks: key blocks
+ * j < sink_blocks and i - band_blocks < j <= i. */
+typedef struct {
+  double p_centroid;
+  double p_rescue;
+  int32_t band_blocks;
+  int32_t sink_blocks;
+} fsa_select_params;
+
+typedef struct {
+  int32_t B, Hq, Hkv, D;
+  int32_t page_size;   /* must be 16                                   */
+  int32_t num_pages;   /* pages in each pool                           */
+  int32_t max_pages;   /* row stride of page_table (pages per sequence) */
+  int32_t max_seq_len; /* upper bound of seq_lens[b], <= 16*max_pages   */
+} fsa_decode_shape;
+
+enum { FSA_SEL_ALL = 0, FSA_SEL_INDEX = 1, FSA_SEL_SEGMENT = 2 };
+
+/* Which cached tokens a decode query reads (host struct).
+ *   FSA_SEL_ALL:     tokens [0, seq_lens[b]).
+ *   FSA_SEL_INDEX:   idx (device) int32 [B, Hq, k], per query head; entries
+ *                    outside [0, seq_lens[b]) are skipped.
+ *   FSA_SEL_SEGMENT: segments (device) int32 [B, max_seg, 2] token ranges
+ *                    [start, end), n_seg (device) int32 [B]; ranges of one
+ *                    sequence must be sorted and disjoint, and are clipped
+ *                    to [0, seq_lens[b]); shared by all heads.
+ * n_split: split-KV factor per (sequence, head); 0 picks one. */
+typedef struct {
+  int32_t mode;
+  const int32_t* idx;
+  int32_t k;
+  const int32_t* segments;
+  const int32_t* n_seg;
+  int32_t max_seg;
+  int32_t n_split;
+} fsa_kv_select;
+
+/* ---- entry points -------------------------------------------------------- */
+
+/* block_stats -- key-block centroid and radius.
+ * RBS-Attention post, "Key technical points" 1: the centroid base branch
+ * scores a block by its average key; the rescue branch uses the maximum
+ * key-block radius.  centroid[b,g,j,:] = mean of the T keys K[b, jT..jT+T-1,
+ * g, :]; radius[b,g,j] = max over those keys of ||k - centroid||_2 (whole
+ * block, causality ignored).  Computed in fp32.
+ *   k        (device) [B, S, Hkv, D] bf16 or fp32 (dt)
+ *   centroid (device) fp32 [B, Hkv, nB, D]   written
+ *   radius   (device) fp32 [B, Hkv, nB]      written */
+int block_stats(fsa_dtype dt, const void* k, const fsa_prefill_shape* s, float* centroid,
+                float* radius, hipStream_t st);
+
+/* select_blocks -- two-branch block selection and mask merge.
+ * RBS-Attention post, "Key technical points" 1-2: centroid and rescue
+ * branches are thresholded independently and their masks merged.  With
+ * qbar = mean of the T queries of query block i (head h) and j <= i:
+ *   Sc[i,j] = qbar . centroid[g(h), j]
+ *   Sr[i,j] = Sc[i,j] + ||qbar|| * radius[g(h), j]
+ * C = top k(p_centroid) by Sc, R = top k(p_rescue) by Sr (ties to the lower
+ * j), M = C u R u forced, j <= i.  Scores in fp32.
+ *   q          (device) [B, S, Hq, D] bf16 or fp32
+ *   centroid, radius (device) from block_stats
+ *   p          (host) selector parameters
+ *   mask_bits  (device) uint32 [B, Hq, nB, ceil(nB/32)]; bit j%32 of word j/32
+ *              set iff M[i,j]; every word written
+ *   block_idx  (device) int32 [B, Hq, nB, nB]; the j with M[i,j], ascending;
+ *              entries past block_cnt are not written
+ *   block_cnt  (device) int32 [B, Hq, nB]
+ *   score_c, score_r (device, nullable) fp32 [B, Hq, nB, nB]; j <= i written
+ *   ws         (device) at least fsa_workspace_size(FSA_OP_SELECT_BLOCKS) bytes */
+int select_blocks(fsa_dtype dt, const void* q, const float* centroid, const float* radius,
+                  const fsa_prefill_shape* s, const fsa_select_params* p, uint32_t* mask_bits,
+                  int32_t* block_idx, int32_t* block_cnt, float* score_c, float* score_r,
+                  void* ws, size_t ws_bytes, hipStream_t st);
+
+/* sparse_prefill_attn -- block-sparse causal flash-attention.
+ * RBS-Attention post, "Key technical points" 2: the merged mask runs on an
+ * unchanged block-sparse FlashAttention path.  For token t of query block i
+ * and head h: O[b,t,h,:] = sum over s in A softmax(scale * Q.K_s) V_s with
+ * A = {s <= t : s / T listed in block_idx[b,h,i,0..block_cnt)}; list entries
+ * outside [0, i] are skipped.  block_idx == NULL (and block_cnt == NULL)
+ * means every causal block (dense causal attention).  bf16 inputs use bf16
+ * MFMA with fp32 accumulation and an fp32 online softmax; fp32 inputs use
+ * fp32 MFMA throughout.  An empty list gives O = 0, lse = -inf.
+ *   q (device) [B,S,Hq,D]; k, v (device) [B,S,Hkv,D]; all of dtype dt
+ *   out (device) [B,S,Hq,D] dtype dt; lse (device, nullable) fp32 [B,Hq,S]
+ *   (natural log).  ws may be NULL when the workspace size is 0. */
+int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* v,
+                        const fsa_prefill_shape* s, const int32_t* block_idx,
+                        const int32_t* block_cnt, float scale, void* out, float* lse, void* ws,
+                        size_t ws_bytes, hipStream_t st);
+
+/* topk_indices -- exact per-head top-k over the whole paged context.
+ * Kascade post, "What Kascade got right": an anchor layer computes exact
+ * Top-k key indices that later layers reuse; "Head-aware is the key to
+ * accuracy": one index set per attention (query) head.  Scores are raw
+ * q . k in fp32 over tokens [0, seq_lens[b]); the k largest are kept, ties
+ * to the lower token index, written ascending.  If seq_lens[b] < k the
+ * missing entries are -1 and kth is -inf.
+ *   q (device) bf16 [B, Hq, D]; k_pool (device) bf16 [num_pages, Hkv, 16, D]
+ *   page_table (device) int32 [B, max_pages]; seq_lens (device) int32 [B]
+ *   idx (device) int32 [B, Hq, k]; kth (device, nullable) fp32 [B, Hq]
+ *   ws (device) at least fsa_workspace_size(FSA_OP_TOPK) bytes */
+int topk_indices(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
+                 const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
+                 float* kth, void* ws, size_t ws_bytes, hipStream_t st);
+
+/* sparse_decode_attn -- split-KV decode attention over a paged cache.
+ * Kascade post, "What Kascade got right" (reuse layers attend only at the
+ * anchor's indices); Declarative Attention post, "Declarative attention
+ * protocol" (block-aligned global/focus/local token ranges over a paged
+ * cache); LoZA post, "4. From food delivery to AI" (SplitKV-and-Combine).
+ * o[b,h,:] = sum over admitted tokens j softmax(scale * q.K_j) V_j; the key
+ * set is split, each split writes (max, sum, output) partials in fp32, and
+ * a log-sum-exp combine merges them.  An empty key set gives o = 0 and
+ * lse = -inf.
+ *   q (device) bf16 [B, Hq, D]; k_pool, v_pool (device) bf16 pools
+ *   sel (host) key selection, see fsa_kv_select
+ *   out (device) bf16 [B, Hq, D]; lse (device, nullable) fp32 [B, Hq]
+ *   ws (device) at least fsa_workspace_size(FSA_OP_DECODE_ATTN) bytes */
+int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       const fsa_decode_shape* s, const fsa_kv_select* sel, float scale,
+                       void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st);
+
+/* ---- helpers --------------------------------------------------------------- */
+
+enum { FSA_OP_SELECT_BLOCKS = 1, FSA_OP_PREFILL_ATTN = 2, FSA_OP_TOPK = 3, FSA_OP_DECODE_ATTN = 4 };
+
+/* Workspace bytes a call needs.  shape: fsa_prefill_shape* for ops 1-2,
+ * fsa_decode_shape* for ops 3-4; params: NULL for ops 1-2, int* k for op 3,
+ * fsa_kv_select* for op 4.  Returns 0 for an unknown op or bad arguments. */
+size_t fsa_workspace_size(int op, const void* shape, const void* params);
+
+enum { FSA_SEG_GLOBAL = 0, FSA_SEG_FOCUS = 1, FSA_SEG_LOCAL = 2, FSA_SEG_STREAMING = 3 };
+
+/* fsa_build_segments -- host-only segment builder for one sequence of n
+ * cached tokens.  Declarative Attention post, "Declarative attention
+ * protocol" (global / focus / local; kept ranges rounded outward to
+ * KV-block boundaries) and LoZA post, "2. ZigZag architecture" (streaming
+ * window).  Ranges written to out (host) int32 [*n_seg, 2], sorted, merged:
+ *   GLOBAL    [0, n)
+ *   FOCUS     [chunk_start, chunk_start + chunk_len) u [n - local_len, n),
+ *             each rounded outward to `page`, clipped to [0, n)
+ *   LOCAL     [n - local_len, n) rounded outward to `page`
+ *   STREAMING [0, n_sink) u [n - local_len, n), token-exact
+ * out must hold 2 ranges.  Returns FSA_ERR_ARG for a bad mode or sizes. */
+int fsa_build_segments(int mode, int n, int chunk_start, int chunk_len, int local_len,
+                       int n_sink, int page, int32_t* out, int* n_seg);
+
+/* Static text for a status code. */
+const char* fsa_status_string(int status);
+
+/* FSA_OK when the current HIP device is a gfx950 GPU, else FSA_ERR_NO_DEVICE. */
+int fsa_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H */

@@ -1,0 +1,182 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+* libfsa.so loads and exports every function declared in include/fsa.h;
+* host validation returns the documented status codes before any device
+  work (so these calls are safe without a GPU);
+* the host segment builder agrees with the oracle's builder and with the
+  block-alignment facts.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from free_sparse_attention_head_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        from free_sparse_attention_head_amd import build
+        build.build()
+    return L, L.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "fsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "return")))
+
+
+def test_library_exports_every_declared_symbol():
+    L, lib = _lib()
+    names = _declared_functions()
+    for required in ("block_stats", "select_blocks", "sparse_prefill_attn", "topk_indices",
+                     "sparse_decode_attn", "fsa_workspace_size", "fsa_build_segments",
+                     "fsa_status_string", "fsa_device_check"):
+        assert required in names
+    for n in names:
+        assert hasattr(lib, n), f"libfsa.so does not export {n}"
+        assert n in L.SIGNATURES, f"binding lacks a signature for {n}"
+
+
+def test_status_strings():
+    L, lib = _lib()
+    for code in range(0, -8, -1):
+        assert lib.fsa_status_string(code)
+    assert lib.fsa_status_string(-99) == b"unknown status"
+
+
+def _shape(L, **kw):
+    d = dict(B=1, S=1024, Hq=2, Hkv=2, D=64, T=64)
+    d.update(kw)
+    return L.PrefillShape(*[d[k] for k in ("B", "S", "Hq", "Hkv", "D", "T")])
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), -2), (dict(T=32), -2), (dict(S=1000), -2), (dict(Hq=3, Hkv=2), -2),
+    (dict(B=0), -2), (dict(S=64 * 5000), -2)])
+def test_prefill_shape_validation(kw, code):
+    L, lib = _lib()
+    s = _shape(L, **kw)
+    rc = lib.block_stats(L.FSA_BF16, FAKE, ctypes.byref(s), FAKE, FAKE, None)
+    assert rc == code
+    rc = lib.sparse_prefill_attn(L.FSA_BF16, FAKE, FAKE, FAKE, ctypes.byref(s), None, None,
+                                 0.125, FAKE, None, None, 0, None)
+    assert rc == code
+
+
+def test_prefill_null_and_dtype_validation():
+    L, lib = _lib()
+    s = _shape(L)
+    assert lib.block_stats(L.FSA_BF16, None, ctypes.byref(s), FAKE, FAKE, None) == L.FSA_ERR_NULL
+    assert lib.block_stats(7, FAKE, ctypes.byref(s), FAKE, FAKE, None) == L.FSA_ERR_DTYPE
+    assert lib.block_stats(L.FSA_BF16, FAKE, None, FAKE, FAKE, None) == L.FSA_ERR_NULL
+    # block_idx without block_cnt
+    assert lib.sparse_prefill_attn(L.FSA_BF16, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, None,
+                                   0.125, FAKE, None, None, 0, None) == L.FSA_ERR_NULL
+    assert lib.sparse_prefill_attn(L.FSA_BF16, FAKE, FAKE, FAKE, ctypes.byref(s), None, None,
+                                   float("inf"), FAKE, None, None, 0, None) == L.FSA_ERR_ARG
+
+
+def test_select_validation_and_workspace():
+    L, lib = _lib()
+    s = _shape(L)
+    ws = lib.fsa_workspace_size(L.FSA_OP_SELECT_BLOCKS, ctypes.byref(s), None)
+    nB = 1024 // 64
+    assert ws >= 2 * nB * 64 * 4 + 2 * nB * nB * 4
+    p = L.SelectParams(0.25, 0.1, 0, 0)
+    args = lambda wsb, pp=p: (L.FSA_F32, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(pp),
+                              FAKE, FAKE, FAKE, None, None, FAKE, wsb, None)
+    assert lib.select_blocks(*args(ws - 1)) == L.FSA_ERR_WORKSPACE
+    bad = L.SelectParams(float("nan"), 0.1, 0, 0)
+    assert lib.select_blocks(*args(ws, bad)) == L.FSA_ERR_ARG
+    neg = L.SelectParams(0.25, 0.1, -1, 0)
+    assert lib.select_blocks(*args(ws, neg)) == L.FSA_ERR_ARG
+    assert lib.fsa_workspace_size(L.FSA_OP_PREFILL_ATTN, ctypes.byref(s), None) == 0
+    assert lib.fsa_workspace_size(99, ctypes.byref(s), None) == 0
+
+
+def _dshape(L, **kw):
+    d = dict(B=2, Hq=8, Hkv=2, D=128, page_size=16, num_pages=64, max_pages=32, max_seq_len=512)
+    d.update(kw)
+    return L.DecodeShape(*[d[k] for k in ("B", "Hq", "Hkv", "D", "page_size", "num_pages",
+                                          "max_pages", "max_seq_len")])
+
+
+@pytest.mark.parametrize("kw", [dict(page_size=32), dict(Hq=6, Hkv=4), dict(Hq=32, Hkv=2),
+                                dict(D=80), dict(max_seq_len=16 * 32 + 1), dict(B=0)])
+def test_decode_shape_validation(kw):
+    L, lib = _lib()
+    s = _dshape(L, **kw)
+    rc = lib.topk_indices(L.FSA_BF16, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), 8, FAKE, None,
+                          FAKE, 1 << 30, None)
+    assert rc == L.FSA_ERR_SHAPE
+
+
+def test_topk_and_decode_argument_validation():
+    L, lib = _lib()
+    s = _dshape(L)
+    k = ctypes.c_int(16)
+    ws = lib.fsa_workspace_size(L.FSA_OP_TOPK, ctypes.byref(s), ctypes.byref(k))
+    assert ws >= 2 * 8 * 512 * 4
+    call = lambda dt, kk, wsb: lib.topk_indices(dt, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), kk,
+                                                FAKE, None, FAKE, wsb, None)
+    assert call(L.FSA_F32, 16, ws) == L.FSA_ERR_DTYPE
+    assert call(L.FSA_BF16, 0, ws) == L.FSA_ERR_ARG
+    assert call(L.FSA_BF16, 513, ws) == L.FSA_ERR_ARG
+    assert call(L.FSA_BF16, 16, ws - 1) == L.FSA_ERR_WORKSPACE
+
+    sel = L.KvSelect(L.FSA_SEL_INDEX, None, 16, None, None, 0, 0)
+    dcall = lambda sl, wsb=1 << 30, dt=L.FSA_BF16: lib.sparse_decode_attn(
+        dt, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(sl), 0.1, FAKE, None,
+        FAKE, wsb, None)
+    assert dcall(sel) == L.FSA_ERR_NULL                      # index mode without idx
+    sel = L.KvSelect(L.FSA_SEL_SEGMENT, None, 0, FAKE.value, FAKE.value, 0, 0)
+    assert dcall(sel) == L.FSA_ERR_ARG                       # max_seg 0
+    sel = L.KvSelect(9, None, 0, None, None, 0, 0)
+    assert dcall(sel) == L.FSA_ERR_ARG                       # unknown mode
+    sel = L.KvSelect(L.FSA_SEL_ALL, None, 0, None, None, 0, -1)
+    assert dcall(sel) == L.FSA_ERR_ARG                       # negative split
+    sel = L.KvSelect(L.FSA_SEL_ALL, None, 0, None, None, 0, 4)
+    assert dcall(sel, dt=L.FSA_F32) == L.FSA_ERR_DTYPE
+    need = lib.fsa_workspace_size(L.FSA_OP_DECODE_ATTN, ctypes.byref(s), ctypes.byref(sel))
+    assert need == 2 * 8 * 4 * (128 + 2) * 4
+    assert dcall(sel, wsb=need - 1) == L.FSA_ERR_WORKSPACE
+
+
+SEG_CASES = [(oracle.SEG_GLOBAL, 1 << 20, 0), (oracle.SEG_LOCAL, 1 << 20, 0),
+             (oracle.SEG_LOCAL, 1000, 0), (oracle.SEG_LOCAL, 3000, 0),
+             (oracle.SEG_STREAMING, 1 << 20, 0), (oracle.SEG_STREAMING, 600, 0),
+             (oracle.SEG_STREAMING, 3, 0)] + \
+            [(oracle.SEG_FOCUS, 1 << 20, s) for s in (0, 1, 15, 16, 100003, (1 << 20) - 2048,
+                                                        (1 << 20) - 3000)] + \
+            [(oracle.SEG_FOCUS, 5000, s) for s in (0, 2000, 2950, 3100)]
+
+
+@pytest.mark.parametrize("mode,n,start", SEG_CASES)
+def test_build_segments_matches_oracle(mode, n, start):
+    import free_sparse_attention_head_amd as fsa
+    got = fsa.build_segments(mode, n, chunk_start=start, chunk_len=2048, local_len=1024,
+                             n_sink=4, page=16)
+    want = oracle.build_segments(mode, n, start, 2048, 1024, 4, 16)
+    assert got == [tuple(int(x) for x in r) for r in want]
+
+
+def test_build_segments_errors():
+    L, lib = _lib()
+    buf = (ctypes.c_int32 * 4)()
+    cnt = ctypes.c_int(0)
+    assert lib.fsa_build_segments(7, 100, 0, 10, 10, 0, 16, buf, ctypes.byref(cnt)) == L.FSA_ERR_ARG
+    assert lib.fsa_build_segments(0, 100, 0, 10, 10, 0, 0, buf, ctypes.byref(cnt)) == L.FSA_ERR_ARG
+    assert lib.fsa_build_segments(0, 100, 0, 10, 10, 0, 16, None, ctypes.byref(cnt)) == L.FSA_ERR_NULL

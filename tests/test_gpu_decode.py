@@ -1,0 +1,200 @@
+"""GPU parity of the decode path (topk_indices, sparse_decode_attn in index,
+segment and all modes) against the fp64 oracle, through the C ABI.
+
+The paged pools are shuffled, sequences are ragged (one shorter than k, one
+not a multiple of the page size), split counts vary (1, odd, automatic) and a
+GQA group of 8 with D = 64 is covered besides the 4 x D = 128 shape.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._parity import TOL_BF16, topk_diff_excused
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    # name: (B, N, Hq, Hkv, D, seq_lens, k)
+    "gqa4_d128": (3, 8192, 8, 2, 128, [8192, 5003, 100], 256),
+    "gqa8_d64": (2, 4096, 8, 1, 64, [4096, 2048 + 7], 128),
+}
+
+_cache = {}
+
+
+def inputs(name):
+    if name not in _cache:
+        B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+        print(f"[decode case {name}] B={B} N={N} Hq={Hq} Hkv={Hkv} D={D} k={k}", flush=True)
+        d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=2, seq_lens=sl, seed=77,
+                                    device="cpu")
+        gpu = {"page_table": d["page_table"].cuda(), "seq_lens": d["seq_lens"].cuda(),
+               "layers": [{x: t.cuda() for x, t in L.items()} for L in d["layers"]]}
+        _cache[name] = (d, gpu)
+    return _cache[name]
+
+
+def seq_kv(d, layer, b, g, n=None):
+    n = int(d["seq_lens"][b]) if n is None else n
+    pt = d["page_table"][b].numpy()
+    K = oracle.gather_pages(workloads.to_f64(d["layers"][layer]["k"]), pt, n, g)
+    V = oracle.gather_pages(workloads.to_f64(d["layers"][layer]["v"]), pt, n, g)
+    return K, V
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_topk_parity(name):
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L0 = gpu["layers"][0]
+    idx, kth = fsa.topk_indices(L0["q"], L0["k"], gpu["page_table"], gpu["seq_lens"], k,
+                                max_seq_len=N)
+    idx, kth = idx.cpu().numpy(), kth.cpu().numpy()
+    q = workloads.to_f64(d["layers"][0]["q"])
+    G = Hq // Hkv
+    n_diff = n_exc = 0
+    for b in range(B):
+        n = sl[b]
+        for h in range(Hq):
+            row = idx[b, h]
+            if n < k:
+                assert (row[:n] == np.arange(n)).all() and (row[n:] == -1).all()
+                assert np.isneginf(kth[b, h])
+                continue
+            assert (np.diff(row) > 0).all() and row.min() >= 0 and row.max() < n
+            K, _ = seq_kv(d, 0, b, h // G)
+            scores = K @ q[b, h]
+            ref_idx, ref_kth = oracle.topk(scores, k)
+            dd, ee = topk_diff_excused(row, ref_idx, scores, ref_kth)
+            n_diff += dd
+            n_exc += ee
+            assert abs(kth[b, h] - ref_kth) <= 1e-3
+    print(f"[{name}] top-k entries differing {n_diff}, excused near k-th value {n_exc}")
+    assert n_diff == n_exc
+
+
+def test_topk_k_equals_n_and_k_one():
+    import free_sparse_attention_head_amd as fsa
+    d, gpu = inputs("gqa4_d128")
+    L0 = gpu["layers"][0]
+    sl = torch.tensor([3000, 3000, 3000], dtype=torch.int32, device="cuda")
+    idx, kth = fsa.topk_indices(L0["q"], L0["k"], gpu["page_table"], sl, 3000, max_seq_len=8192)
+    assert (idx.cpu() == torch.arange(3000, dtype=torch.int32)).all()
+    idx1, kth1 = fsa.topk_indices(L0["q"], L0["k"], gpu["page_table"], sl, 1, max_seq_len=8192)
+    q = workloads.to_f64(d["layers"][0]["q"])
+    for b in range(3):
+        for h in range(8):
+            K, _ = seq_kv(d, 0, b, h // 4, n=3000)
+            s = K @ q[b, h]
+            assert abs(kth[b, h].item() - s.min()) <= 1e-3
+            assert abs(kth1[b, h].item() - s.max()) <= 1e-3
+            am = int(idx1[b, h, 0])
+            assert abs(s[am] - s.max()) <= 1e-3
+
+
+def test_topk_ties_go_to_lower_index():
+    """All keys of a sequence identical -> all scores equal (bit-identical on
+    the GPU too) -> the k lowest indices, exactly."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D = 1, 2048, 4, 1, 128
+    d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=1, seed=3, device="cpu")
+    kp = d["layers"][0]["k"].clone()
+    kp[:] = kp[0, 0, 0]
+    idx, kth = fsa.topk_indices(d["layers"][0]["q"].cuda(), kp.cuda(), d["page_table"].cuda(),
+                                d["seq_lens"].cuda(), 100)
+    assert (idx.cpu() == torch.arange(100, dtype=torch.int32)).all()
+    # half the keys duplicated on the top: positions 1000..1099 get the best key
+    kp2 = d["layers"][0]["k"].clone()
+    q = d["layers"][0]["q"]
+    best = q[0, 0].clone()
+    pt = d["page_table"][0]
+    for j in range(1000, 1200):
+        kp2[pt[j // 16], 0, j % 16] = best
+    idx2, _ = fsa.topk_indices(q.cuda(), kp2.cuda(), d["page_table"].cuda(), d["seq_lens"].cuda(), 150)
+    assert (idx2.cpu()[0, 0] == torch.arange(1000, 1150, dtype=torch.int32)).all()
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("n_split", [0, 1, 3])
+def test_index_decode_parity(name, n_split):
+    """Kascade reuse layer: layer 1 attends at layer 0's per-head indices."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L0, L1 = gpu["layers"]
+    idx, _ = fsa.topk_indices(L0["q"], L0["k"], gpu["page_table"], gpu["seq_lens"], k, max_seq_len=N)
+    out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"], gpu["seq_lens"],
+                                      mode=fsa.SEL_INDEX, idx=idx, n_split=n_split, max_seq_len=N)
+    out, lse, idx = out.cpu(), lse.cpu(), idx.cpu().numpy()
+    q1 = workloads.to_f64(d["layers"][1]["q"])
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(D)
+    for b in range(B):
+        for h in range(Hq):
+            K, V = seq_kv(d, 1, b, h // G)
+            o, l = oracle.index_attention(q1[b, h], K, V, idx[b, h], scale)
+            assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
+            assert abs(lse[b, h].item() - l) <= 1e-2
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("mode", ["all", "global", "focus", "local", "streaming"])
+def test_segment_decode_parity(name, mode):
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L1 = gpu["layers"][1]
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(D)
+    ranges = []
+    rng = np.random.default_rng(5)
+    for b in range(B):
+        n = sl[b]
+        if mode in ("all", "global"):
+            ranges.append(oracle.build_segments(oracle.SEG_GLOBAL, n))
+        elif mode == "focus":
+            s = int(rng.integers(0, max(1, n - 2048)))
+            ranges.append(oracle.build_segments(oracle.SEG_FOCUS, n, s, 2048, 1024))
+        elif mode == "local":
+            ranges.append(oracle.build_segments(oracle.SEG_LOCAL, n, local_len=1024))
+        else:
+            ranges.append(oracle.build_segments(oracle.SEG_STREAMING, n, local_len=1024, n_sink=4))
+    if mode == "all":
+        out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"],
+                                          gpu["seq_lens"], mode=fsa.SEL_ALL, max_seq_len=N)
+    else:
+        segs = torch.zeros((B, 4, 2), dtype=torch.int32)
+        nseg = torch.zeros(B, dtype=torch.int32)
+        for b, rs in enumerate(ranges):
+            nseg[b] = len(rs)
+            for x, (a, e) in enumerate(rs):
+                segs[b, x, 0], segs[b, x, 1] = a, e
+        out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"],
+                                          gpu["seq_lens"], mode=fsa.SEL_SEGMENT, segments=segs.cuda(),
+                                          n_seg=nseg.cuda(), n_split=5 if mode == "focus" else 0,
+                                          max_seq_len=N)
+    out, lse = out.cpu(), lse.cpu()
+    q1 = workloads.to_f64(d["layers"][1]["q"])
+    for b in range(B):
+        for h in range(Hq):
+            K, V = seq_kv(d, 1, b, h // G)
+            o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
+            assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
+            assert abs(lse[b, h].item() - l) <= 1e-2
+
+
+def test_empty_segment_gives_zero_output():
+    import free_sparse_attention_head_amd as fsa
+    d, gpu = inputs("gqa4_d128")
+    L1 = gpu["layers"][1]
+    segs = torch.zeros((3, 1, 2), dtype=torch.int32, device="cuda")
+    nseg = torch.zeros(3, dtype=torch.int32, device="cuda")
+    out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"], gpu["seq_lens"],
+                                      mode=fsa.SEL_SEGMENT, segments=segs, n_seg=nseg, max_seq_len=8192)
+    assert (out.cpu() == 0).all() and torch.isinf(lse.cpu()).all()
