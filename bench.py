@@ -1,0 +1,441 @@
+"""Benchmark of the head-aware sparse attention hot path on one MI355X.
+
+One step runs every row of the hot path once over resident synthetic inputs:
+  prefill, 128K prompt (B=1, S=131072, 32 query / 4 KV heads, D=128, bf16,
+    key/query block 128, low-rank keys with 1% planted spikes, a kept
+    1024-token diagonal band and the sink block): block_stats ->
+    select_blocks (two-branch selector tuned to the target density) ->
+    sparse_prefill_attn;
+  Kascade decode group, 128K context (B=32, 32 query / 8 KV heads, D=128,
+    bf16 KV in shuffled 16-token pages, 4 layers): topk_indices (k=2048) at
+    the anchor layer, then sparse_decode_attn at those indices for the anchor
+    and the three reuse layers;
+  segment decode, 1M context (B=4, same heads, shuffled pages): global, focus
+    (2048-token chunk + 1024 local tail), local (1024) and streaming
+    (4 sinks + 1024 window) masks, caches flushed before each small mode.
+Kernel times come from HIP events on the launch stream.  The headline value
+is the sparse prefill attention kernel's effective TFLOP/s on executed
+blocks (4*T*T*D FLOP per executed query-block/key-block pair); decode is
+reported as admitted KV bytes per second.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--density 0.06]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+PREFILL = dict(B=1, S=131072, Hq=32, Hkv=4, D=128, T=128, band=8, sink=1)
+DECODE = dict(B=32, N=131072, Hq=32, Hkv=8, D=128, k=2048, layers=4)
+SEGMENT = dict(B=4, N=1 << 20, Hq=32, Hkv=8, D=128)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Per-kernel HIP-event timing on the current stream."""
+
+    def __init__(self):
+        self.ev = {}
+
+    def run(self, name, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn()
+        e.record()
+        self.ev.setdefault(name, []).append((s, e))
+        return r
+
+    def ms(self, name, skip=0):
+        xs = [s.elapsed_time(e) for s, e in self.ev[name][skip:]]
+        return float(np.mean(xs)), float(np.min(xs))
+
+    def clear(self):
+        self.ev = {}
+
+
+def make_prefill(fsa, workloads, density, seed=1002):
+    P = PREFILL
+    log(f"[bench] generating prefill inputs S={P['S']} Hq={P['Hq']} Hkv={P['Hkv']}")
+    inp = workloads.prefill_inputs(1, P["S"], P["Hq"], P["Hkv"], P["D"], P["T"], model="lowrank",
+                                   seed=seed, device="cuda")
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    c, r = fsa.block_stats(k, P["T"])
+    nB = P["S"] // P["T"]
+    visible = P["Hq"] * nB * (nB + 1) // 2
+    out = None
+    lo, hi = 0.0, 1.0
+    best = None
+    for it in range(30):
+        pc = 0.5 * (lo + hi)
+        out = fsa.select_blocks(q, c, r, P["T"], pc, 0.4 * pc, P["band"], P["sink"], out=out)
+        dens = out["block_cnt"].sum().item() / visible
+        best = (pc, dens)
+        if abs(dens - density) <= 0.0025:
+            break
+        if dens < density:
+            lo = pc
+        else:
+            hi = pc
+    pc, dens = best
+    log(f"[bench] selector p_c={pc:.5f} p_r={0.4 * pc:.5f} density={dens:.4f}")
+    return dict(q=q, k=k, v=v, p_c=pc, p_r=0.4 * pc, density=dens, sel=out, c=c, r=r,
+                o=torch.empty_like(q), lse=torch.empty((1, P["Hq"], P["S"]), dtype=torch.float32,
+                                                      device="cuda"))
+
+
+def make_decode(fsa, workloads, seed=1003):
+    D = DECODE
+    log(f"[bench] generating Kascade decode group B={D['B']} N={D['N']} layers={D['layers']}")
+    d = workloads.decode_inputs(D["B"], D["N"], D["Hq"], D["Hkv"], D["D"], layers=D["layers"],
+                                seed=seed, device="cuda")
+    d["idx"] = torch.empty((D["B"], D["Hq"], D["k"]), dtype=torch.int32, device="cuda")
+    d["kth"] = torch.empty((D["B"], D["Hq"]), dtype=torch.float32, device="cuda")
+    d["out"] = [torch.empty((D["B"], D["Hq"], D["D"]), dtype=torch.bfloat16, device="cuda")
+                for _ in range(D["layers"])]
+    return d
+
+
+def make_segment(fsa, workloads, seed=1004):
+    Sg = SEGMENT
+    log(f"[bench] generating segment decode B={Sg['B']} N={Sg['N']}")
+    d = workloads.decode_inputs(Sg["B"], Sg["N"], Sg["Hq"], Sg["Hkv"], Sg["D"], layers=1, seed=seed,
+                                device="cuda")
+    rng = np.random.default_rng(seed)
+    n = Sg["N"]
+    modes = {}
+    for name, code in (("focus", fsa.SEG_FOCUS), ("local", fsa.SEG_LOCAL),
+                       ("streaming", fsa.SEG_STREAMING)):
+        segs = torch.zeros((Sg["B"], 2, 2), dtype=torch.int32)
+        nseg = torch.zeros(Sg["B"], dtype=torch.int32)
+        admitted = 0
+        for b in range(Sg["B"]):
+            st = int(rng.integers(0, n - 2048))
+            rs = fsa.build_segments(code, n, chunk_start=st, chunk_len=2048, local_len=1024,
+                                    n_sink=4, page=16)
+            nseg[b] = len(rs)
+            for x, (a, e) in enumerate(rs):
+                segs[b, x, 0], segs[b, x, 1] = a, e
+                admitted += e - a
+        modes[name] = dict(segs=segs.cuda(), nseg=nseg.cuda(), admitted=admitted)
+    d["modes"] = modes
+    d["out"] = torch.empty((Sg["B"], Sg["Hq"], Sg["D"]), dtype=torch.bfloat16, device="cuda")
+    d["flush"] = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    return d
+
+
+def kv_row_bytes(D):
+    return 2 * D * 2  # one K row + one V row, bf16
+
+
+def step(fsa, pf, dc, sg, tm, parts=("prefill", "decode", "segment")):
+    P, Dd, Sg = PREFILL, DECODE, SEGMENT
+    if "prefill" in parts:
+        step_prefill(fsa, pf, tm)
+    if "decode" in parts:
+        step_decode(fsa, dc, tm)
+    if "segment" in parts:
+        step_segment(fsa, sg, tm)
+
+
+def step_prefill(fsa, pf, tm):
+    P = PREFILL
+    tm.run("block_stats", lambda: fsa.block_stats(pf["k"], P["T"], pf["c"], pf["r"]))
+    tm.run("select_blocks", lambda: fsa.select_blocks(pf["q"], pf["c"], pf["r"], P["T"], pf["p_c"],
+                                                      pf["p_r"], P["band"], P["sink"],
+                                                      out=pf["sel"], ws=pf.get("sel_ws")))
+    tm.run("sparse_prefill_attn", lambda: fsa.sparse_prefill_attn(
+        pf["q"], pf["k"], pf["v"], P["T"], pf["sel"]["block_idx"], pf["sel"]["block_cnt"],
+        out=pf["o"], lse=pf["lse"]))
+
+
+def step_decode(fsa, dc, tm):
+    """Kascade group: anchor top-k, then index decode for anchor + reuse layers."""
+    Dd = DECODE
+    L = dc["layers"]
+    tm.run("topk_indices", lambda: fsa.topk_indices(L[0]["q"], L[0]["k"], dc["page_table"],
+                                                    dc["seq_lens"], Dd["k"], idx=dc["idx"],
+                                                    kth=dc["kth"], ws=dc.get("topk_ws")))
+    for li in range(Dd["layers"]):
+        tm.run("decode_index" if li else "decode_index_anchor", lambda li=li: fsa.sparse_decode_attn(
+            L[li]["q"], L[li]["k"], L[li]["v"], dc["page_table"], dc["seq_lens"],
+            mode=fsa.SEL_INDEX, idx=dc["idx"], out=dc["out"][li], want_lse=False,
+            ws=dc.get("dec_ws")))
+
+
+def step_segment(fsa, sg, tm):
+    """1M-context segment decode: global, then the small modes after a cache flush."""
+    G = sg["layers"][0]
+    tm.run("decode_global", lambda: fsa.sparse_decode_attn(
+        G["q"], G["k"], G["v"], sg["page_table"], sg["seq_lens"], mode=fsa.SEL_ALL,
+        out=sg["out"], want_lse=False, ws=sg.get("ws")))
+    for name, m in sg["modes"].items():
+        sg["flush"].view(torch.int64).sum()  # read-evict L2 / MALL so the small modes read HBM
+        tm.run("decode_" + name, lambda m=m: fsa.sparse_decode_attn(
+            G["q"], G["k"], G["v"], sg["page_table"], sg["seq_lens"], mode=fsa.SEL_SEGMENT,
+            segments=m["segs"], n_seg=m["nseg"], n_split=m.get("n_split", 0), out=sg["out"],
+            want_lse=False, ws=sg.get("ws")))
+
+
+def prefill_flops(pf):
+    P = PREFILL
+    executed = int(pf["sel"]["block_cnt"].sum().item())
+    return 4.0 * P["T"] * P["T"] * P["D"] * executed, executed
+
+
+def cpu_baseline(pf, budget_s=15.0):
+    """fp64 oracle timed on a bounded sample of the prefill workload: whole
+    query blocks of head 0 at the benchmark's mask, from the last block
+    backwards, until about budget_s seconds of compute."""
+    import oracle
+    import workloads
+    P = PREFILL
+    T = P["T"]
+    nB = P["S"] // T
+    h, g = 0, 0
+    q = workloads.to_f64(pf["q"][0, :, h])
+    k = workloads.to_f64(pf["k"][0, :, g])
+    v = workloads.to_f64(pf["v"][0, :, g])
+    cnt = pf["sel"]["block_cnt"][0, h].cpu().numpy()
+    lst = pf["sel"]["block_idx"][0, h].cpu().numpy()
+    scale = 1 / math.sqrt(P["D"])
+    done_blocks = 0
+    t_cpu = 0.0
+    rows = 0
+    for i in range(nB - 1, -1, -1):
+        m = np.zeros((nB, nB), dtype=bool)
+        m[i, lst[i, :cnt[i]]] = True
+        t0 = time.perf_counter()
+        oracle.masked_attention_rows(q, k, v, m, T, scale, np.arange(i * T, (i + 1) * T))
+        t_cpu += time.perf_counter() - t0
+        done_blocks += int(cnt[i])
+        rows += 1
+        if t_cpu >= budget_s:
+            break
+    flops = 4.0 * T * T * P["D"] * done_blocks
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    cores = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": flops / t_cpu / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 masked attention, head 0, last {rows} of {nb_str(nB)} query blocks "
+                      f"({done_blocks} executed blocks, {t_cpu:.1f} s)"}
+
+
+def nb_str(n):
+    return str(n)
+
+
+def attach_workspaces(fsa, pf, dc, sg):
+    """Pre-allocate every workspace so the timed region allocates nothing."""
+    P, Dd, Sg = PREFILL, DECODE, SEGMENT
+    if pf is not None:
+        pshape = fsa._lib.PrefillShape(1, P["S"], P["Hq"], P["Hkv"], P["D"], P["T"])
+        pf["sel_ws"] = torch.empty(fsa.workspace_size("select", pshape), dtype=torch.uint8,
+                                   device="cuda")
+    if dc is not None:
+        dshape = fsa._lib.DecodeShape(Dd["B"], Dd["Hq"], Dd["Hkv"], Dd["D"], 16,
+                                      dc["num_pages"], dc["max_pages"], Dd["N"])
+        dc["topk_ws"] = torch.empty(fsa.workspace_size("topk", dshape, Dd["k"]), dtype=torch.uint8,
+                                    device="cuda")
+        sel = fsa._lib.KvSelect(fsa.SEL_INDEX, None, Dd["k"], None, None, 0, 0)
+        dc["dec_ws"] = torch.empty(fsa.workspace_size("decode", dshape, sel), dtype=torch.uint8,
+                                   device="cuda")
+    if sg is not None:
+        sshape = fsa._lib.DecodeShape(Sg["B"], Sg["Hq"], Sg["Hkv"], Sg["D"], 16, sg["num_pages"],
+                                      sg["max_pages"], Sg["N"])
+        ssel = fsa._lib.KvSelect(fsa.SEL_ALL, None, 0, None, None, 0, 0)
+        wsb = fsa.workspace_size("decode", sshape, ssel)
+        sg["ws"] = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        # small modes: one split per 128 admitted tokens of a sequence, within the workspace
+        for name, m in sg["modes"].items():
+            per_seq = m["admitted"] // Sg["B"]
+            m["n_split"] = max(1, min(wsb // (Sg["B"] * Sg["Hq"] * (Sg["D"] + 2) * 4), per_seq // 128))
+
+
+def profile_only(fsa, workloads, args):
+    """Run one part of the step (for profilers); prints per-kernel times."""
+    pf = make_prefill(fsa, workloads, args.density) if args.only == "prefill" else None
+    dc = make_decode(fsa, workloads) if args.only == "decode" else None
+    sg = make_segment(fsa, workloads) if args.only == "segment" else None
+    attach_workspaces(fsa, pf, dc, sg)
+    tm = Timer()
+    for _ in range(args.warmup):
+        step(fsa, pf, dc, sg, tm, parts=(args.only,))
+    torch.cuda.synchronize()
+    tm.clear()
+    for _ in range(args.steps):
+        step(fsa, pf, dc, sg, tm, parts=(args.only,))
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "kernel_ms": {n: round(tm.ms(n)[0], 4) for n in tm.ev}}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--density", type=float, default=0.06)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "segment"], default=None,
+                    help="profile one part of the step only (not a benchmark result)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a 1 GiB device copy at the end (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the hot path here is a single-GPU kernel library; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import workloads
+    from free_sparse_attention_head_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from free_sparse_attention_head_amd import build
+        build.build()
+    import free_sparse_attention_head_amd as fsa
+    torch.cuda.set_device(0)
+
+    if args.only:
+        return profile_only(fsa, workloads, args)
+    pf = make_prefill(fsa, workloads, args.density)
+    dc = make_decode(fsa, workloads)
+    sg = make_segment(fsa, workloads)
+    attach_workspaces(fsa, pf, dc, sg)
+    P, Dd, Sg = PREFILL, DECODE, SEGMENT
+    tm = Timer()
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(fsa, pf, dc, sg, tm)
+    torch.cuda.synchronize()
+    tm.clear()
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(fsa, pf, dc, sg, tm)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    log("[bench] timed region done")
+
+    k_ms = {n: tm.ms(n) for n in tm.ev}
+    flops, executed = prefill_flops(pf)
+    attn_ms = k_ms["sparse_prefill_attn"][0]
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    path_ms = sum(k_ms[n][0] for n in ("block_stats", "select_blocks", "sparse_prefill_attn"))
+    idx_bytes = Dd["B"] * Dd["Hq"] * Dd["k"] * kv_row_bytes(Dd["D"])
+    reuse_ms = k_ms["decode_index"][0]
+    reuse_gbps = idx_bytes / (reuse_ms * 1e-3) / 1e9
+    scan_bytes = Dd["B"] * Dd["N"] * Dd["Hkv"] * Dd["D"] * 2
+    topk_ms = k_ms["topk_indices"][0]
+    group_ms = topk_ms + k_ms["decode_index_anchor"][0] + 3 * reuse_ms
+    group_bytes = scan_bytes + 4 * idx_bytes - Dd["B"] * Dd["Hq"] * Dd["k"] * Dd["D"] * 2
+    seg = {}
+    for name in ("global", "focus", "local", "streaming"):
+        if name == "global":
+            admitted = Sg["B"] * Sg["N"]
+        else:
+            admitted = sg["modes"][name]["admitted"]
+        byts = admitted * Sg["Hkv"] * kv_row_bytes(Sg["D"])
+        ms = k_ms["decode_" + name][0]
+        seg[name] = {"ms": round(ms, 4), "GB": round(byts / 1e9, 4),
+                     "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+    dense = {}
+    if not args.no_dense:
+        log("[bench] own dense baselines")
+        tmd = Timer()
+        for _ in range(2):
+            tmd.run("dense_prefill", lambda: fsa.sparse_prefill_attn(pf["q"], pf["k"], pf["v"], P["T"],
+                                                                      out=pf["o"], lse=pf["lse"]))
+            for li in range(Dd["layers"]):
+                tmd.run("dense_decode", lambda li=li: fsa.sparse_decode_attn(
+                    dc["layers"][li]["q"], dc["layers"][li]["k"], dc["layers"][li]["v"],
+                    dc["page_table"], dc["seq_lens"], mode=fsa.SEL_ALL, out=dc["out"][li],
+                    want_lse=False, ws=dc.get("dense_ws")))
+        torch.cuda.synchronize()
+        nB = P["S"] // P["T"]
+        dflops = 4.0 * P["T"] ** 2 * P["D"] * P["Hq"] * nB * (nB + 1) // 2
+        dms = tmd.ms("dense_prefill", skip=1)[0]
+        ddec = tmd.ms("dense_decode", skip=4)[0] * 4
+        dense = {"prefill_ms": round(dms, 3), "prefill_TFLOPs": round(dflops / dms / 1e9, 1),
+                 "prefill_speedup": round(dms / attn_ms, 2),
+                 "decode_4layers_ms": round(ddec, 3),
+                 "decode_4layers_GBps": round(4 * Dd["B"] * Dd["N"] * Dd["Hkv"] * kv_row_bytes(Dd["D"]) /
+                                              (ddec * 1e-3) / 1e9, 1),
+                 "decode_group_speedup": round(ddec / group_ms, 2)}
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu oracle baseline")
+        cpu = cpu_baseline(pf)
+
+    res = {
+        "metric": "sparse prefill TFLOP/s & decode KV GB/s at 128K ctx, % roofline, 1 MI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sparse prefill 128K (B=1, 32q/4kv heads, D=128, block 128, "
+                               f"density {pf['density']:.4f}) + Kascade decode 128K (B=32, 32q/8kv, "
+                               "k=2048, 4 layers) + segment decode 1M (B=4)",
+                   "global_batch": 1, "seq_len": P["S"], "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_attn_kernel<bf16,128,128>",
+                     "flop_per_launch": flops, "executed_blocks": executed,
+                     "avg_launch_ms": round(attn_ms, 4)},
+        "roofline_decode": {"bound": "hbm", "achieved": round(reuse_gbps, 1), "peak": PEAK_HBM_GBPS,
+                            "unit": "GB/s", "frac": round(reuse_gbps / PEAK_HBM_GBPS, 4),
+                            "kernel": "decode_split_kernel<128,1,INDEX> + combine",
+                            "bytes_per_launch": idx_bytes, "avg_launch_ms": round(reuse_ms, 4)},
+        "prefill": {"density": round(pf["density"], 4), "p_c": pf["p_c"], "p_r": pf["p_r"],
+                    "attn_ms": round(attn_ms, 4), "attn_min_ms": round(k_ms["sparse_prefill_attn"][1], 4),
+                    "block_stats_ms": round(k_ms["block_stats"][0], 4),
+                    "select_ms": round(k_ms["select_blocks"][0], 4),
+                    "path_ms": round(path_ms, 4), "path_TFLOPs": round(flops / path_ms / 1e9, 2)},
+        "decode": {"topk_ms": round(topk_ms, 4),
+                   "topk_scan_GBps": round(scan_bytes / (topk_ms * 1e-3) / 1e9, 1),
+                   "anchor_decode_ms": round(k_ms["decode_index_anchor"][0], 4),
+                   "reuse_decode_ms": round(reuse_ms, 4), "reuse_GBps": round(reuse_gbps, 1),
+                   "group_ms": round(group_ms, 4),
+                   "group_GBps": round(group_bytes / (group_ms * 1e-3) / 1e9, 1)},
+        "segment_1M": seg,
+        "dense": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -124,8 +124,12 @@ size_t fsa_workspace_size(int op, const void* shape, const void* params) {
     return fsa::topk_ws_bytes(d, k);
   }
   if (op == FSA_OP_DECODE_ATTN) {
+    // sizing depends on mode, k and n_split only; pointers are not needed yet
     const fsa_kv_select* sel = static_cast<const fsa_kv_select*>(params);
-    if (sel == nullptr || check_kv_select(sel, d) != FSA_OK) return 0;
+    if (sel == nullptr || sel->n_split < 0 || sel->n_split > kMaxSplit) return 0;
+    if (sel->mode != FSA_SEL_ALL && sel->mode != FSA_SEL_INDEX && sel->mode != FSA_SEL_SEGMENT)
+      return 0;
+    if (sel->mode == FSA_SEL_INDEX && sel->k < 1) return 0;
     return fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split);
   }
   return 0;
