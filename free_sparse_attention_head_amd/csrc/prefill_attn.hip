@@ -29,6 +29,8 @@
 
 namespace fsa {
 
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, log2 units
+
 template <typename TI, int D, int BLK>
 struct PrefillTraits {
   static constexpr bool F32 = sizeof(TI) == 4;
@@ -48,7 +50,7 @@ struct PrefillTraits {
 };
 
 template <typename TI, int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void prefill_attn_kernel(
+__global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
     const TI* __restrict__ Q, const TI* __restrict__ K, const TI* __restrict__ V,
     const int32_t* __restrict__ bidx, const int32_t* __restrict__ bcnt, TI* __restrict__ O,
     float* __restrict__ LSE, int S, int Hq, int Hkv, float scale_log2, int total) {
@@ -224,41 +226,47 @@ __global__ __launch_bounds__(BLK * 2) void prefill_attn_kernel(
           }
         }
       }
-      // scale, causal mask, running max.  Register r of tile tl holds key
+      // causal mask on the diagonal block and the chunk's row max, in raw
+      // score units.  Register r of tile tl holds key
       // koff + tl*32 + (r/4)*8 + lg*4 + r%4 for query qrow.
       float mx = -INFINITY;
 #pragma unroll
       for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[tl][r] * scale_log2;
           if (diag) {
             const int key = koff + tl * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-            if (key > qrow) x = -INFINITY;
+            if (key > qrow) s[tl][r] = -INFINITY;
           }
-          s[tl][r] = x;
-          mx = fmaxf(mx, x);
+          mx = fmaxf(mx, s[tl][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
+      // Lazy rescale: a row's reference max m_run moves only when the row max
+      // exceeds it by more than kRescaleLog2 (log2 units).  exp2 arguments then
+      // stay <= kRescaleLog2 (p <= 256, exact in fp32 and bf16 range) and the
+      // O^T rescale is skipped on every chunk where no row of the wave grows.
+      const bool grow = (mx - m_run) * scale_log2 > kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
 #pragma unroll
       for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[tl][r] - m_use);
-          s[tl][r] = p;
-          l_run += p;
-        }
+        for (int r = 0; r < 16; ++r) s[tl][r] = __builtin_amdgcn_exp2f(fmaf(s[tl][r], scale_log2, -mc));
       // O^T += V^T P^T
       if constexpr (F32) {
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) l_run += s[tl][r];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -275,6 +283,16 @@ __global__ __launch_bounds__(BLK * 2) void prefill_attn_kernel(
         for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][(kc & 1) * 8 + e];
+        // row sum of the bf16-rounded P that the PV step multiplies (v_dot2 with ones)
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const uint4 w = __builtin_bit_cast(uint4, pf[kc]);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), ones, l_run, false);
+        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const TI* vr = Vs + (dt * 32 + lq) * VP;
@@ -311,7 +329,8 @@ __global__ __launch_bounds__(BLK * 2) void prefill_attn_kernel(
       }
     }
   if (LSE != nullptr && lg == 0)
-    LSE[((size_t)b * Hq + h) * S + t] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    LSE[((size_t)b * Hq + h) * S + t] =
+        l_tot > 0.f ? (m_run * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <typename TI, int D, int BLK>
