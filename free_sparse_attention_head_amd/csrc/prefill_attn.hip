@@ -19,9 +19,8 @@
 // bf16 inputs: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV step.
 // fp32 inputs: v_mfma_f32_32x32x2_f32, everything in fp32 (V kept row-major).
 // The diagonal block applies the element-wise causal mask; list entries
-// outside [0, i] are skipped.  Workgroups are mapped so that each XCD works
-// on a contiguous range of heads (shared K/V of a KV head stays in that XCD's
-// L2) and, within a head, the longest rows start first.
+// outside [0, i] are skipped.  Workgroups sweep one KV head at a time,
+// longest rows first (see the work-order note in the kernel).
 #include <math.h>
 
 #include "common.h"
@@ -49,6 +48,113 @@ struct PrefillTraits {
   static_assert(KPIECES >= 1 && VUNITS >= 1, "tile shape");
 };
 
+// Next chunk after c whose key block j = list[chunk / nch] is causal for
+// query block i (0 <= j <= i); returns nchunks when none is left.
+__device__ __forceinline__ int next_valid_chunk(const int32_t* list, int c, int nchunks, int nch,
+                                                int i) {
+  for (++c; c < nchunks; ++c) {
+    const int j = list[c / nch];
+    if (j >= 0 && j <= i) break;
+  }
+  return c;
+}
+
+// Global -> register -> LDS staging of one 64-key chunk of K and V.  K is
+// copied row-major; bf16 V is transposed 4x4 in registers and written as V^T
+// (fp32 V stays row-major).  All loops are fully unrolled over fixed-size
+// member arrays so the staging lives in VGPRs.
+template <typename TI, int D, int BLK>
+struct Stage {
+  using Tr = PrefillTraits<TI, D, BLK>;
+  static constexpr bool F32 = Tr::F32;
+  static constexpr int KC = Tr::KC, KP = Tr::KP, VP = Tr::VP, NT = Tr::NT;
+  static constexpr int PPR = D * (int)sizeof(TI) / 16;  // 16-byte pieces per key row
+  // K (and fp32 V) pieces are held in wide vector types: an array of uint4
+  // here is not split into registers and ends up in scratch memory.
+  typedef uint32_t kvec_t __attribute__((ext_vector_type(4 * Tr::KPIECES)));
+  typedef uint32_t vvec_t __attribute__((ext_vector_type(4 * (F32 ? Tr::VUNITS : 1))));
+  kvec_t k;
+  vvec_t vf;                           // fp32 V pieces
+  uint2 vb[F32 ? 1 : Tr::VUNITS][4];   // bf16 V: 4 keys x 4 d per unit
+
+  __device__ __forceinline__ void load(const TI* Kb, const TI* Vb, int s0, size_t kv_stride,
+                                       int tid) {
+#pragma unroll
+    for (int m = 0; m < Tr::KPIECES; ++m) {
+      const int p = tid + m * NT;
+      const int key = p / PPR, pc = p % PPR;
+      const uint4 w = *reinterpret_cast<const uint4*>(Kb + (size_t)(s0 + key) * kv_stride +
+                                                      pc * (16 / sizeof(TI)));
+      k[4 * m] = w.x;
+      k[4 * m + 1] = w.y;
+      k[4 * m + 2] = w.z;
+      k[4 * m + 3] = w.w;
+    }
+    if constexpr (F32) {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        const int p = tid + m * NT;
+        const int key = p / PPR, pc = p % PPR;
+        const uint4 w = *reinterpret_cast<const uint4*>(Vb + (size_t)(s0 + key) * kv_stride + pc * 4);
+        vf[4 * m] = w.x;
+        vf[4 * m + 1] = w.y;
+        vf[4 * m + 2] = w.z;
+        vf[4 * m + 3] = w.w;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        const int u = tid + m * NT;
+        const int kq = u / (D / 4), dq = u % (D / 4);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          vb[m][rr] = *reinterpret_cast<const uint2*>(Vb + (size_t)(s0 + kq * 4 + rr) * kv_stride +
+                                                      dq * 4);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(TI* Ks, TI* Vs, int tid) const {
+#pragma unroll
+    for (int m = 0; m < Tr::KPIECES; ++m) {
+      const int p = tid + m * NT;
+      const int key = p / PPR, pc = p % PPR;
+      *reinterpret_cast<uint4*>(Ks + key * KP + pc * (16 / sizeof(TI))) =
+          make_uint4(k[4 * m], k[4 * m + 1], k[4 * m + 2], k[4 * m + 3]);
+    }
+    if constexpr (F32) {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        const int p = tid + m * NT;
+        const int key = p / PPR, pc = p % PPR;
+        *reinterpret_cast<uint4*>(Vs + key * VP + pc * 4) =
+            make_uint4(vf[4 * m], vf[4 * m + 1], vf[4 * m + 2], vf[4 * m + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < Tr::VUNITS; ++m) {
+        const int u = tid + m * NT;
+        const int kq = u / (D / 4), dq = u % (D / 4);
+        const uint2 r0 = vb[m][0], r1 = vb[m][1], r2 = vb[m][2], r3 = vb[m][3];
+        uint2 c0, c1, c2, c3;  // column e of the 4x4 bf16 block = keys kq*4..+3 at d = dq*4+e
+        c0.x = (r0.x & 0xffffu) | (r1.x << 16);
+        c0.y = (r2.x & 0xffffu) | (r3.x << 16);
+        c1.x = (r0.x >> 16) | (r1.x & 0xffff0000u);
+        c1.y = (r2.x >> 16) | (r3.x & 0xffff0000u);
+        c2.x = (r0.y & 0xffffu) | (r1.y << 16);
+        c2.y = (r2.y & 0xffffu) | (r3.y << 16);
+        c3.x = (r0.y >> 16) | (r1.y & 0xffff0000u);
+        c3.y = (r2.y >> 16) | (r3.y & 0xffff0000u);
+        TI* vt = Vs + (dq * 4) * VP + kq * 4;
+        *reinterpret_cast<uint2*>(vt) = c0;
+        *reinterpret_cast<uint2*>(vt + VP) = c1;
+        *reinterpret_cast<uint2*>(vt + 2 * VP) = c2;
+        *reinterpret_cast<uint2*>(vt + 3 * VP) = c3;
+      }
+    }
+  }
+};
+
 template <typename TI, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
     const TI* __restrict__ Q, const TI* __restrict__ K, const TI* __restrict__ V,
@@ -60,14 +166,25 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   TI* Ks = reinterpret_cast<TI*>(smem);
   TI* Vs = Ks + KC * KP;
+  int32_t* Ls = reinterpret_cast<int32_t*>(smem + Tr::LDS);  // the row's block list
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // Work order: KV head major, then query blocks longest-first, then the G
+  // query heads sharing that KV head.  The running window of workgroups
+  // therefore touches one KV head's K/V at a time (so it stays resident in
+  // the Infinity Cache), and since dispatch deals workgroups round-robin over
+  // the 8 XCDs, each XCD sees the same query head for consecutive query
+  // blocks, whose diagonal bands and sink blocks then hit in its L2.
+  const int L = blockIdx.x;
   if (L >= total) return;
   const int nB = S / BLK;
-  const int i = nB - 1 - (L % nB);  // longest rows of a head first
-  const int bh = L / nB;
-  const int h = bh % Hq, b = bh / Hq;
-  const int g = h / (Hq / Hkv);
+  const int G = Hq / Hkv;
+  const int hh = L % G;
+  const int rest = L / G;
+  const int i = nB - 1 - (rest % nB);
+  const int bg = rest / nB;
+  const int g = bg % Hkv, b = bg / Hkv;
+  const int h = g * G + hh;
+  const int bh = b * Hq + h;
   const int row = bh * nB + i;
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
@@ -97,90 +214,22 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
     }
   }
 
-  const int32_t* lst = bidx ? bidx + (size_t)row * nB : nullptr;
+  // stage the row's block list in LDS once: the loop then never waits on a
+  // global load that could also cover the K/V prefetch
   const int cnt = bidx ? min(max(bcnt[row], 0), nB) : i + 1;
+  if (bidx) {
+    const int32_t* lst = bidx + (size_t)row * nB;
+    for (int e = tid; e < cnt; e += Tr::NT) Ls[e] = lst[e];
+  } else {
+    for (int e = tid; e < cnt; e += Tr::NT) Ls[e] = e;
+  }
+  __syncthreads();
   const int nchunks = cnt * NCH;
-  auto block_of = [&](int c) -> int { return lst ? lst[c / NCH] : c / NCH; };
-  auto next_valid = [&](int c) -> int {
-    for (++c; c < nchunks; ++c) {
-      const int j = block_of(c);
-      if (j >= 0 && j <= i) break;
-    }
-    return c;
-  };
 
-  // ---- register staging of one chunk
-  uint4 kreg[Tr::KPIECES];
-  typename std::conditional<F32, uint4, uint2>::type vreg[Tr::VUNITS][F32 ? 1 : 4];
-  auto load_chunk = [&](int c) {
-    const int s0 = block_of(c) * BLK + (c % NCH) * KC;
-#pragma unroll
-    for (int m = 0; m < Tr::KPIECES; ++m) {
-      constexpr int PPR = D * sizeof(TI) / 16;  // pieces per key row
-      const int p = tid + m * Tr::NT;
-      const int key = p / PPR, pc = p % PPR;
-      kreg[m] = *reinterpret_cast<const uint4*>(Kb + (size_t)(s0 + key) * kv_stride +
-                                                pc * (16 / sizeof(TI)));
-    }
-    if constexpr (F32) {
-#pragma unroll
-      for (int m = 0; m < Tr::VUNITS; ++m) {
-        constexpr int PPR = D / 4;
-        const int p = tid + m * Tr::NT;
-        const int key = p / PPR, pc = p % PPR;
-        vreg[m][0] = *reinterpret_cast<const uint4*>(Vb + (size_t)(s0 + key) * kv_stride + pc * 4);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < Tr::VUNITS; ++m) {
-        const int u = tid + m * Tr::NT;
-        const int kq = u / (D / 4), dq = u % (D / 4);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          vreg[m][rr] = *reinterpret_cast<const uint2*>(Vb + (size_t)(s0 + kq * 4 + rr) * kv_stride +
-                                                         dq * 4);
-      }
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int m = 0; m < Tr::KPIECES; ++m) {
-      constexpr int PPR = D * sizeof(TI) / 16;
-      const int p = tid + m * Tr::NT;
-      const int key = p / PPR, pc = p % PPR;
-      *reinterpret_cast<uint4*>(Ks + key * KP + pc * (16 / sizeof(TI))) = kreg[m];
-    }
-    if constexpr (F32) {
-#pragma unroll
-      for (int m = 0; m < Tr::VUNITS; ++m) {
-        constexpr int PPR = D / 4;
-        const int p = tid + m * Tr::NT;
-        const int key = p / PPR, pc = p % PPR;
-        *reinterpret_cast<uint4*>(Vs + key * VP + pc * 4) = vreg[m][0];
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < Tr::VUNITS; ++m) {
-        const int u = tid + m * Tr::NT;
-        const int kq = u / (D / 4), dq = u % (D / 4);
-        const uint2 r0 = vreg[m][0], r1 = vreg[m][1], r2 = vreg[m][2], r3 = vreg[m][3];
-        uint2 c0, c1, c2, c3;  // column e of the 4x4 bf16 block = keys kq*4..+3 at d = dq*4+e
-        c0.x = (r0.x & 0xffffu) | (r1.x << 16);
-        c0.y = (r2.x & 0xffffu) | (r3.x << 16);
-        c1.x = (r0.x >> 16) | (r1.x & 0xffff0000u);
-        c1.y = (r2.x >> 16) | (r3.x & 0xffff0000u);
-        c2.x = (r0.y & 0xffffu) | (r1.y << 16);
-        c2.y = (r2.y & 0xffffu) | (r3.y << 16);
-        c3.x = (r0.y >> 16) | (r1.y & 0xffff0000u);
-        c3.y = (r2.y >> 16) | (r3.y & 0xffff0000u);
-        TI* vt = Vs + (dq * 4) * VP + kq * 4;
-        *reinterpret_cast<uint2*>(vt) = c0;
-        *reinterpret_cast<uint2*>(vt + VP) = c1;
-        *reinterpret_cast<uint2*>(vt + 2 * VP) = c2;
-        *reinterpret_cast<uint2*>(vt + 3 * VP) = c3;
-      }
-    }
-  };
+  // ---- register staging of one chunk (fixed-size arrays, fully unrolled)
+  Stage<TI, D, BLK> stg;
+  const int cs = next_valid_chunk(Ls, -1, nchunks, NCH, i);
+  if (cs < nchunks) stg.load(Kb, Vb, Ls[cs / NCH] * BLK + (cs % NCH) * KC, kv_stride, tid);
 
   floatx16 oacc[D / 32];
 #pragma unroll
@@ -189,16 +238,15 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  int c = next_valid(-1);
-  if (c < nchunks) load_chunk(c);
+  int c = cs;
   while (c < nchunks) {
+    const int j = Ls[c / NCH];
     __syncthreads();
-    store_chunk();
+    stg.store(Ks, Vs, tid);
     __syncthreads();
-    const int cn = next_valid(c);
-    if (cn < nchunks) load_chunk(cn);
+    const int cn = next_valid_chunk(Ls, c, nchunks, NCH, i);
+    if (cn < nchunks) stg.load(Kb, Vb, Ls[cn / NCH] * BLK + (cn % NCH) * KC, kv_stride, tid);
 
-    const int j = block_of(c);
     const int koff = (c % NCH) * KC;  // chunk's first key inside the block
     const bool diag = (j == i);
     // a wave whose queries all precede the chunk's keys has nothing to do
@@ -229,17 +277,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
       // causal mask on the diagonal block and the chunk's row max, in raw
       // score units.  Register r of tile tl holds key
       // koff + tl*32 + (r/4)*8 + lg*4 + r%4 for query qrow.
+      if (diag) {
+        // keys after the query row: key - qrow > 0 with key = koff + tl*32 +
+        // (r/4)*8 + lg*4 + r%4
+        const int rel = koff + lg * 4 - qrow;
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (rel + tl * 32 + (r >> 2) * 8 + (r & 3) > 0) s[tl][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (diag) {
-            const int key = koff + tl * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-            if (key > qrow) s[tl][r] = -INFINITY;
-          }
-          mx = fmaxf(mx, s[tl][r]);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tl][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // Lazy rescale: a row's reference max m_run moves only when the row max
       // exceeds it by more than kRescaleLog2 (log2 units).  exp2 arguments then
@@ -339,14 +391,15 @@ static hipError_t launch_pa(const void* q, const void* k, const void* v, const P
                             float* lse, hipStream_t st) {
   using Tr = PrefillTraits<TI, D, BLK>;
   auto kern = prefill_attn_kernel<TI, D, BLK>;
-  if (Tr::LDS > 64 * 1024) {
+  const size_t lds = Tr::LDS + (size_t)(d.S / BLK) * sizeof(int32_t);
+  if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Tr::LDS);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int total = d.B * d.Hq * (d.S / BLK);
   const int padded = (total + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(kern, dim3(padded), dim3(Tr::NT), Tr::LDS, st, static_cast<const TI*>(q),
+  hipLaunchKernelGGL(kern, dim3(padded), dim3(Tr::NT), lds, st, static_cast<const TI*>(q),
                      static_cast<const TI*>(k), static_cast<const TI*>(v), bidx, bcnt,
                      static_cast<TI*>(out), lse, d.S, d.Hq, d.Hkv, scale * kLog2e, total);
   return hipGetLastError();
