@@ -46,17 +46,20 @@ struct PrefillTraits {
   static constexpr int KPIECES = KC * D * sizeof(TI) / 16 / NT;  // 16-byte K pieces
   static constexpr int VUNITS = F32 ? KPIECES : (KC / 4) * (D / 4) / NT;
   static_assert(KPIECES >= 1 && VUNITS >= 1, "tile shape");
+  // two staging sets in flight when one set is small enough
+  static constexpr bool DEEP = !F32 && KPIECES <= 4;
 };
 
-// Next chunk after c whose key block j = list[chunk / nch] is causal for
-// query block i (0 <= j <= i); returns nchunks when none is left.
-__device__ __forceinline__ int next_valid_chunk(const int32_t* list, int c, int nchunks, int nch,
-                                                int i) {
-  for (++c; c < nchunks; ++c) {
-    const int j = list[c / nch];
-    if (j >= 0 && j <= i) break;
-  }
-  return c;
+// V^T fragment (MFMA A operand) of step m = kc * ndt + dt: d row dt*32 + lq,
+// keys kc*16 + lg*4 + {0..3} and kc*16 + 8 + lg*4 + {0..3} (vbase already
+// points at row lq, column lg*4).
+template <typename TI, int VP, int NDT>
+__device__ __forceinline__ uint4 vt_frag(const TI* vbase, int m) {
+  const int kc = m / NDT, dt = m % NDT;
+  const TI* p = vbase + dt * 32 * VP + kc * 16;
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // Global -> register -> LDS staging of one 64-key chunk of K and V.  K is
@@ -214,22 +217,24 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
     }
   }
 
-  // stage the row's block list in LDS once: the loop then never waits on a
-  // global load that could also cover the K/V prefetch
+  // Stage the row's list of causal key blocks (entries outside [0, i]
+  // dropped, order kept) in LDS once; the loop then reads the list from LDS
+  // and never waits on a global load that could also cover the K/V prefetch.
+  __shared__ int scan_tmp[17];
   const int cnt = bidx ? min(max(bcnt[row], 0), nB) : i + 1;
-  if (bidx) {
-    const int32_t* lst = bidx + (size_t)row * nB;
-    for (int e = tid; e < cnt; e += Tr::NT) Ls[e] = lst[e];
-  } else {
-    for (int e = tid; e < cnt; e += Tr::NT) Ls[e] = e;
+  int nvalid = 0;
+  for (int e0 = 0; e0 < cnt; e0 += Tr::NT) {
+    const int e = e0 + tid;
+    int j = -1;
+    if (e < cnt) j = bidx ? bidx[(size_t)row * nB + e] : e;
+    const int ok = (j >= 0 && j <= i) ? 1 : 0;
+    int tot;
+    const int pos = block_excl_scan(ok, scan_tmp, &tot);
+    if (ok) Ls[nvalid + pos] = j;
+    nvalid += tot;
   }
   __syncthreads();
-  const int nchunks = cnt * NCH;
-
-  // ---- register staging of one chunk (fixed-size arrays, fully unrolled)
-  Stage<TI, D, BLK> stg;
-  const int cs = next_valid_chunk(Ls, -1, nchunks, NCH, i);
-  if (cs < nchunks) stg.load(Kb, Vb, Ls[cs / NCH] * BLK + (cs % NCH) * KC, kv_stride, tid);
+  const int nchunks = nvalid * NCH;
 
   floatx16 oacc[D / 32];
 #pragma unroll
@@ -238,128 +243,185 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  int c = cs;
-  while (c < nchunks) {
+  // One 64-key chunk: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
+  auto compute = [&](int c) {
     const int j = Ls[c / NCH];
-    __syncthreads();
-    stg.store(Ks, Vs, tid);
-    __syncthreads();
-    const int cn = next_valid_chunk(Ls, c, nchunks, NCH, i);
-    if (cn < nchunks) stg.load(Kb, Vb, Ls[cn / NCH] * BLK + (cn % NCH) * KC, kv_stride, tid);
-
-    const int koff = (c % NCH) * KC;  // chunk's first key inside the block
-    const bool diag = (j == i);
-    // a wave whose queries all precede the chunk's keys has nothing to do
-    if (!(diag && koff > wave * 32 + 31)) {
-      floatx16 s[2];
-#pragma unroll
-      for (int tl = 0; tl < 2; ++tl) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[tl][r] = 0.f;
-        const TI* kr = Ks + (tl * 32 + lq) * KP;
-        if constexpr (F32) {
-#pragma unroll
-          for (int kk = 0; kk < D / 2; kk += 4) {
-            const float4 a4 = *reinterpret_cast<const float4*>(kr + lg * (D / 2) + kk);
-            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, qf[kk], s[tl], 0, 0, 0);
-            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, qf[kk + 1], s[tl], 0, 0, 0);
-            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, qf[kk + 2], s[tl], 0, 0, 0);
-            s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, qf[kk + 3], s[tl], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + kk * 16 + lg * 8));
-            s[tl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[tl], 0, 0, 0);
-          }
-        }
-      }
-      // causal mask on the diagonal block and the chunk's row max, in raw
-      // score units.  Register r of tile tl holds key
-      // koff + tl*32 + (r/4)*8 + lg*4 + r%4 for query qrow.
-      if (diag) {
-        // keys after the query row: key - qrow > 0 with key = koff + tl*32 +
-        // (r/4)*8 + lg*4 + r%4
-        const int rel = koff + lg * 4 - qrow;
-#pragma unroll
-        for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (rel + tl * 32 + (r >> 2) * 8 + (r & 3) > 0) s[tl][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tl][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy rescale: a row's reference max m_run moves only when the row max
-      // exceeds it by more than kRescaleLog2 (log2 units).  exp2 arguments then
-      // stay <= kRescaleLog2 (p <= 256, exact in fp32 and bf16 range) and the
-      // O^T rescale is skipped on every chunk where no row of the wave grows.
-      const bool grow = (mx - m_run) * scale_log2 > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-      const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
-#pragma unroll
-      for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[tl][r] = __builtin_amdgcn_exp2f(fmaf(s[tl][r], scale_log2, -mc));
-      // O^T += V^T P^T
-      if constexpr (F32) {
-#pragma unroll
-        for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) l_run += s[tl][r];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = tl * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-              const float a = Vs[key * VP + dt * 32 + lq];
-              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[tl][r], oacc[dt], 0, 0, 0);
+      const int koff = (c % NCH) * KC;  // chunk's first key inside the block
+      const bool diag = (j == i);
+      // a wave whose queries all precede the chunk's keys has nothing to do
+      if (!(diag && koff > wave * 32 + 31)) {
+        floatx16 s[2];
+  #pragma unroll
+        for (int tl = 0; tl < 2; ++tl) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) s[tl][r] = 0.f;
+          if constexpr (F32) {
+            const TI* kr = Ks + (tl * 32 + lq) * KP;
+  #pragma unroll
+            for (int kk = 0; kk < D / 2; kk += 4) {
+              const float4 a4 = *reinterpret_cast<const float4*>(kr + lg * (D / 2) + kk);
+              s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, qf[kk], s[tl], 0, 0, 0);
+              s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, qf[kk + 1], s[tl], 0, 0, 0);
+              s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, qf[kk + 2], s[tl], 0, 0, 0);
+              s[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, qf[kk + 3], s[tl], 0, 0, 0);
             }
-      } else {
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][(kc & 1) * 8 + e];
-        // row sum of the bf16-rounded P that the PV step multiplies (v_dot2 with ones)
-        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const uint4 w = __builtin_bit_cast(uint4, pf[kc]);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), ones, l_run, false);
+          }
         }
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const TI* vr = Vs + (dt * 32 + lq) * VP;
-#pragma unroll
+        if constexpr (!F32) {
+          // K fragments of step kk+1 are read before the MFMAs of step kk, and
+          // the two independent 32-key tiles alternate on the matrix pipe, so
+          // LDS latency overlaps MFMA execution.
+          const TI* kr0 = Ks + lq * KP + lg * 8;
+          const TI* kr1 = kr0 + 32 * KP;
+          uint4 a0 = *reinterpret_cast<const uint4*>(kr0);
+          uint4 a1 = *reinterpret_cast<const uint4*>(kr1);
+  #pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            uint4 n0 = a0, n1 = a1;
+            if (kk + 1 < D / 16) {
+              n0 = *reinterpret_cast<const uint4*>(kr0 + (kk + 1) * 16);
+              n1 = *reinterpret_cast<const uint4*>(kr1 + (kk + 1) * 16);
+            }
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), qf[kk], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), qf[kk], s[1], 0, 0, 0);
+            a0 = n0;
+            a1 = n1;
+          }
+          // keep the reads one step ahead of the MFMAs in the final schedule
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  #pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            if (kk + 1 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+        }
+        // causal mask on the diagonal block and the chunk's row max, in raw
+        // score units.  Register r of tile tl holds key
+        // koff + tl*32 + (r/4)*8 + lg*4 + r%4 for query qrow.
+        if (diag) {
+          // keys after the query row: key - qrow > 0 with key = koff + tl*32 +
+          // (r/4)*8 + lg*4 + r%4
+          const int rel = koff + lg * 4 - qrow;
+  #pragma unroll
+          for (int tl = 0; tl < 2; ++tl)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (rel + tl * 32 + (r >> 2) * 8 + (r & 3) > 0) s[tl][r] = -INFINITY;
+        }
+        float mx = -INFINITY;
+  #pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tl][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // Lazy rescale: a row's reference max m_run moves only when the row max
+        // exceeds it by more than kRescaleLog2 (log2 units).  exp2 arguments then
+        // stay <= kRescaleLog2 (p <= 256, exact in fp32 and bf16 range) and the
+        // O^T rescale is skipped on every chunk where no row of the wave grows.
+        const bool grow = (mx - m_run) * scale_log2 > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mx : m_run;
+          const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
+          m_run = m_new;
+          l_run *= alpha;
+  #pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
+        const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+  #pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) s[tl][r] = __builtin_amdgcn_exp2f(fmaf(s[tl][r], scale_log2, -mc));
+        // O^T += V^T P^T
+        if constexpr (F32) {
+  #pragma unroll
+          for (int tl = 0; tl < 2; ++tl)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) l_run += s[tl][r];
+  #pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+  #pragma unroll
+            for (int tl = 0; tl < 2; ++tl)
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = tl * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+                const float a = Vs[key * VP + dt * 32 + lq];
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[tl][r], oacc[dt], 0, 0, 0);
+              }
+        } else {
+          bf16x8 pf[4];
+  #pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][(kc & 1) * 8 + e];
+          // row sum of the bf16-rounded P that the PV step multiplies (v_dot2 with ones)
+          const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  #pragma unroll
           for (int kc = 0; kc < 4; ++kc) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(vr + kc * 16 + lg * 4);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vr + kc * 16 + 8 + lg * 4);
-            const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kc],
-                                                                oacc[dt], 0, 0, 0);
+            const uint4 w = __builtin_bit_cast(uint4, pf[kc]);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), ones, l_run, false);
+          }
+          // 4*(D/32) MFMAs in (kc, dt) order: consecutive MFMAs hit different
+          // accumulators, and each V^T fragment is read two MFMAs ahead.
+          constexpr int NDT = D / 32, NM = 4 * NDT;
+          const TI* vbase = Vs + lq * VP + lg * 4;
+          uint4 f0 = vt_frag<TI, VP, NDT>(vbase, 0), f1 = vt_frag<TI, VP, NDT>(vbase, 1);
+  #pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const uint4 f2 = (m + 2 < NM) ? vt_frag<TI, VP, NDT>(vbase, m + 2) : f0;
+            oacc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f0),
+                                                                    pf[m / NDT], oacc[m % NDT], 0, 0, 0);
+            f0 = f1;
+            f1 = f2;
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  #pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            if (m + 2 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
           }
         }
       }
+  };
+
+  // ---- register prefetch: while chunk c is computed, the loads of chunks
+  // c+1 and c+2 are in flight (two staging register sets, loop unrolled by
+  // two so each set keeps fixed registers).
+  // Shapes whose staging set is larger (fewer threads per chunk, or fp32)
+  // keep a one-deep prefetch so the registers still fit two waves per SIMD.
+  auto chunk_s0 = [&](int c) { return Ls[c / NCH] * BLK + (c % NCH) * KC; };
+  if constexpr (Tr::DEEP) {
+    Stage<TI, D, BLK> stA, stB;
+    if (0 < nchunks) stA.load(Kb, Vb, chunk_s0(0), kv_stride, tid);
+    if (1 < nchunks) stB.load(Kb, Vb, chunk_s0(1), kv_stride, tid);
+    for (int c = 0; c < nchunks; c += 2) {
+      __syncthreads();
+      stA.store(Ks, Vs, tid);
+      __syncthreads();
+      if (c + 2 < nchunks) stA.load(Kb, Vb, chunk_s0(c + 2), kv_stride, tid);
+      compute(c);
+      if (c + 1 >= nchunks) break;
+      __syncthreads();
+      stB.store(Ks, Vs, tid);
+      __syncthreads();
+      if (c + 3 < nchunks) stB.load(Kb, Vb, chunk_s0(c + 3), kv_stride, tid);
+      compute(c + 1);
     }
-    c = cn;
+  } else {
+    Stage<TI, D, BLK> st;
+    if (0 < nchunks) st.load(Kb, Vb, chunk_s0(0), kv_stride, tid);
+    for (int c = 0; c < nchunks; ++c) {
+      __syncthreads();
+      st.store(Ks, Vs, tid);
+      __syncthreads();
+      if (c + 1 < nchunks) st.load(Kb, Vb, chunk_s0(c + 1), kv_stride, tid);
+      compute(c);
+    }
   }
 
   // ---- epilogue: O = O^T / l, LSE
