@@ -396,21 +396,42 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_kernel(
   // keep a one-deep prefetch so the registers still fit two waves per SIMD.
   auto chunk_s0 = [&](int c) { return Ls[c / NCH] * BLK + (c % NCH) * KC; };
   if constexpr (Tr::DEEP) {
-    Stage<TI, D, BLK> stA, stB;
-    if (0 < nchunks) stA.load(Kb, Vb, chunk_s0(0), kv_stride, tid);
-    if (1 < nchunks) stB.load(Kb, Vb, chunk_s0(1), kv_stride, tid);
-    for (int c = 0; c < nchunks; c += 2) {
-      __syncthreads();
-      stA.store(Ks, Vs, tid);
-      __syncthreads();
-      if (c + 2 < nchunks) stA.load(Kb, Vb, chunk_s0(c + 2), kv_stride, tid);
-      compute(c);
-      if (c + 1 >= nchunks) break;
-      __syncthreads();
-      stB.store(Ks, Vs, tid);
-      __syncthreads();
-      if (c + 3 < nchunks) stB.load(Kb, Vb, chunk_s0(c + 3), kv_stride, tid);
-      compute(c + 1);
+    // sched_barrier(0) keeps set A's loads ahead of set B's in issue order, so
+    // the wait before storing set A leaves set B's loads in flight
+    // The loads are unconditional (past the end they re-read the last chunk,
+    // a cache hit): conditional loads would merge wait-count state at the
+    // joins and force a wait for every outstanding load.
+    if (nchunks > 0) {
+      const int last = nchunks - 1;
+      Stage<TI, D, BLK> stA, stB;
+      stA.load(Kb, Vb, chunk_s0(0), kv_stride, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      stB.load(Kb, Vb, chunk_s0(min(1, last)), kv_stride, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      // pairs of chunks; the loop header is reached only after both halves,
+      // so the wait before storing set A never covers set B's loads
+      const int pairs = nchunks >> 1;
+      for (int pr = 0; pr < pairs; ++pr) {
+        const int c = 2 * pr;
+        __syncthreads();
+        stA.store(Ks, Vs, tid);
+        __syncthreads();
+        stA.load(Kb, Vb, chunk_s0(min(c + 2, last)), kv_stride, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c);
+        __syncthreads();
+        stB.store(Ks, Vs, tid);
+        __syncthreads();
+        stB.load(Kb, Vb, chunk_s0(min(c + 3, last)), kv_stride, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c + 1);
+      }
+      if (nchunks & 1) {  // odd tail: set A holds chunk nchunks - 1
+        __syncthreads();
+        stA.store(Ks, Vs, tid);
+        __syncthreads();
+        compute(last);
+      }
     }
   } else {
     Stage<TI, D, BLK> st;
