@@ -15,8 +15,10 @@
 //      bits of the order-preserving score key, flushed with one global atomic
 //      per non-empty bin.
 //   3. topk_select_kernel: one 1024-thread workgroup per (sequence, head).
-//      Digit 1 comes from the fused histogram; digits 2 (11 bits) and 3
-//      (10 bits) are histogrammed over the candidates sharing the prefix.
+//      Digit 1 comes from the fused histogram.  When few keys lie in or above
+//      the k-th key's bin, one pass copies them to LDS and the rest runs
+//      there; otherwise digits 2 (11 bits) and 3 (10 bits) are histogrammed
+//      over the candidates sharing the prefix by re-reading the row.
 //      This yields the exact k-th key K* and how many keys equal to K* are
 //      taken.  A final pass in index order keeps key > K*, plus the first keys
 //      equal to K*, compacting positions with workgroup scans so that the
@@ -46,8 +48,12 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
     const int32_t* __restrict__ pt, const int32_t* __restrict__ sl, int Hq, int Hkv,
     int max_pages, int num_pages, int max_seq_len, int stride, int tiles,
     float* __restrict__ scores, uint32_t* __restrict__ hist) {
-  constexpr int LPR = D / 8, RG = 64 / LPR, NSLOT = 4 * RG, RB = 4;
+  constexpr int LPR = D / 8, RG = 64 / LPR, NSLOT = 4 * RG;
+  constexpr int RB = 8;                  // rows per lane group per step
+  constexpr int STEP = NSLOT * RB;       // tokens per step
+  constexpr int TPAGES = kTopkTile / 16;
   __shared__ uint32_t lh[G][kBins1];
+  __shared__ int pg[TPAGES];
   const int tile = blockIdx.x % tiles;
   const int bg = blockIdx.x / tiles;
   const int g = bg % Hkv, b = bg / Hkv;
@@ -58,27 +64,34 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int slot = wave * RG + l / LPR, dl = l % LPR;
   for (int x = tid; x < G * kBins1; x += 256) (&lh[0][0])[x] = 0u;
-
+  // the tile's page ids, read once and coalesced: row loads then depend on an
+  // LDS read instead of a second global load (bad ids become -1: skipped)
+  const int32_t* ptb = pt + (size_t)b * max_pages;
+  for (int x = tid; x < TPAGES; x += 256) {
+    const int tok = t0 + x * 16;
+    int p = tok < t1 ? ptb[tok >> 4] : -1;
+    pg[x] = (p >= 0 && p < num_pages) ? p : -1;
+  }
   uint4 qv[G];
 #pragma unroll
   for (int x = 0; x < G; ++x)
     qv[x] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * G + x) * D + dl * 8);
-  const int32_t* ptb = pt + (size_t)b * max_pages;
   __syncthreads();
 
-  for (int base = t0; base < t1; base += NSLOT * RB) {
-    uint4 kr[RB];
+  // a lane group's RB rows are consecutive tokens inside one 16-token page
+  auto load_rows = [&](int base, uint4 (&kr)[RB]) {
+    const int tok0 = base + slot * RB;
+    const int page = tok0 < t1 ? pg[(tok0 - t0) >> 4] : -1;
+    const size_t row0 = ((size_t)(page < 0 ? 0 : page) * Hkv + g) * 16 + (tok0 & 15);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-      const int tok = base + slot * RB + r;
-      const int page = tok < t1 ? ptb[tok >> 4] : -1;
-      if (page >= 0 && page < num_pages) {  // a bad page id scores as a zero key
-        const size_t row = ((size_t)page * Hkv + g) * 16 + (tok & 15);
-        kr[r] = *reinterpret_cast<const uint4*>(kpool + row * D + dl * 8);
-      } else {
+      if (page >= 0 && tok0 + r < t1)
+        kr[r] = *reinterpret_cast<const uint4*>(kpool + (row0 + r) * D + dl * 8);
+      else
         kr[r] = make_uint4(0, 0, 0, 0);
-      }
     }
+  };
+  auto score_rows = [&](int base, const uint4 (&kr)[RB]) {
     float sc[G][RB];
 #pragma unroll
     for (int x = 0; x < G; ++x)
@@ -96,7 +109,18 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
         atomicAdd(&lh[x][order_key(v) >> 21], 1u);
       }
     }
+  };
+  // two row buffers: the next step's rows are in flight while this step is scored
+  uint4 ka[RB], kb[RB];
+  load_rows(t0, ka);
+  int base = t0;
+  for (; base + STEP < t1; base += 2 * STEP) {
+    load_rows(base + STEP, kb);
+    score_rows(base, ka);
+    if (base + 2 * STEP < t1) load_rows(base + 2 * STEP, ka);
+    score_rows(base + STEP, kb);
   }
+  if (base < t1) score_rows(base, ka);
   __syncthreads();
   for (int x = tid; x < G * kBins1; x += 256) {
     const uint32_t c = (&lh[0][0])[x];
@@ -135,6 +159,97 @@ __device__ void find_digit(TopkShared& sh, int nbins, int kk, int& digit, int& a
   __syncthreads();
 }
 
+// Fast path, used when the keys in or above the k-th key's top-11-bit bin
+// number at most kCandCap: one pass over the score row copies them (key,
+// index) into LDS in index order; digits 2-3 and the ordered output then run
+// on LDS only.  `need` = how many keys of bin b1 still have to be taken.
+constexpr int kCandCap = 6144;
+__device__ void select_from_candidates(const float* __restrict__ sr, int n, int k, uint32_t b1,
+                                       int need, TopkShared& sh, int32_t* __restrict__ out,
+                                       float* __restrict__ kth) {
+  __shared__ uint32_t ck[kCandCap];
+  __shared__ int ci[kCandCap];
+  const int t = threadIdx.x;
+  int ncand = 0;
+  for (int base = 0; base < n; base += 4 * kSelThreads) {
+    const int j0 = base + 4 * t;
+    uint32_t key[4];
+    bool f[4];
+    if (j0 + 3 < n) {
+      const float4 v = *reinterpret_cast<const float4*>(sr + j0);
+      key[0] = order_key(v.x); key[1] = order_key(v.y);
+      key[2] = order_key(v.z); key[3] = order_key(v.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[e] = j0 + e < n ? order_key(sr[j0 + e]) : 0u;
+    }
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = j0 + e < n && (key[e] >> 21) >= b1;
+      c += f[e] ? 1 : 0;
+    }
+    int tot;
+    int pos = ncand + block_excl_scan(c, sh.scan, &tot);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (f[e]) {
+        ck[pos] = key[e];
+        ci[pos] = j0 + e;
+        ++pos;
+      }
+    ncand += tot;
+  }
+  __syncthreads();
+  // digits 2 (11 bits) and 3 (10 bits) among the candidates of bin b1
+  const int E = (ncand + kSelThreads - 1) / kSelThreads;
+  const int e0 = min(ncand, t * E), e1 = min(ncand, e0 + E);
+  uint32_t prefix = b1 << 21, pmask = 0xffe00000u;
+  const int shifts[2] = {10, 0};
+  const int nbins[2] = {2048, 1024};
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int x = t; x < nbins[pass]; x += kSelThreads) sh.hist[x] = 0u;
+    __syncthreads();
+    const uint32_t dmask = (uint32_t)nbins[pass] - 1u;
+    for (int e = e0; e < e1; ++e) {
+      const uint32_t key = ck[e];
+      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shifts[pass]) & dmask], 1u);
+    }
+    __syncthreads();
+    int d, above;
+    find_digit(sh, nbins[pass], need, d, above);
+    need -= above;
+    prefix |= (uint32_t)d << shifts[pass];
+    pmask |= dmask << shifts[pass];
+  }
+  const uint32_t ks = prefix;
+  // ordered output: candidates are in index order and each thread owns a
+  // contiguous range, so one scan of (equal, greater) counts places them
+  int neq = 0, ngt = 0;
+  for (int e = e0; e < e1; ++e) {
+    neq += ck[e] == ks ? 1 : 0;
+    ngt += ck[e] > ks ? 1 : 0;
+  }
+  int tot;
+  const int ex = block_excl_scan((neq << 16) | ngt, sh.scan, &tot);
+  int eq_rank = ex >> 16;
+  int pos = (ex & 0xffff) + min(eq_rank, need);
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t key = ck[e];
+    if (key > ks) {
+      if (pos < k) out[pos] = ci[e];
+      ++pos;
+    } else if (key == ks) {
+      if (eq_rank < need) {
+        if (pos < k) out[pos] = ci[e];
+        ++pos;
+      }
+      ++eq_rank;
+    }
+  }
+  if (kth != nullptr && t == 0) *kth = key_to_float(ks);
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist,
     const int32_t* __restrict__ sl, int Hq, int max_seq_len, int stride, int k,
@@ -156,6 +271,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   int kk = k, d, above;
   find_digit(sh, kBins1, kk, d, above);
   kk -= above;
+  const int cand = above + (int)sh.hist[d];
+  __syncthreads();
+  if (cand <= kCandCap) {
+    select_from_candidates(sr, n, k, (uint32_t)d, kk, sh, out, kth ? kth + row : nullptr);
+    return;
+  }
+  // general path: refine digits 2 and 3 by re-reading the score row
   uint32_t prefix = (uint32_t)d << 21, pmask = 0xffe00000u;
   // digits 2 and 3 over the candidates sharing the prefix
   const int shifts[2] = {10, 0};

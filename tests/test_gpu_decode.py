@@ -120,6 +120,32 @@ def test_topk_ties_go_to_lower_index():
     assert (idx2.cpu()[0, 0] == torch.arange(1000, 1150, dtype=torch.int32)).all()
 
 
+def test_topk_many_ties_uses_general_path_exactly():
+    """More keys tie in the k-th key's histogram bin than the LDS candidate
+    buffer holds (all keys identical, 20000 tokens): the row-rereading path
+    must still return exactly the k lowest indices; a second sequence with
+    a handful of distinct key values checks the same path against the oracle."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, k = 2, 20000, 4, 1, 128, 300
+    d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=1, seed=4, device="cpu")
+    kp = d["layers"][0]["k"].clone()
+    pt = d["page_table"]
+    kp[pt[0].long()] = kp[0, 0, 0].clone()              # sequence 0: one key everywhere
+    rng = np.random.default_rng(1)
+    vals = kp[pt[1, 0].long(), 0, :3].clone()           # sequence 1: three distinct keys
+    for j in range(N):
+        kp[pt[1, j // 16], 0, j % 16] = vals[int(rng.integers(0, 3))]
+    q = d["layers"][0]["q"]
+    idx, kth = fsa.topk_indices(q.cuda(), kp.cuda(), pt.cuda(), d["seq_lens"].cuda(), k)
+    idx = idx.cpu().numpy()
+    assert (idx[0] == np.arange(k)).all()
+    qq = workloads.to_f64(q)
+    for h in range(Hq):
+        K = oracle.gather_pages(workloads.to_f64(kp), pt[1].numpy(), N, 0)
+        ref, _ = oracle.topk(K @ qq[1, h], k)
+        assert (idx[1, h] == ref).all()
+
+
 @pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("n_split", [0, 1, 3])
 def test_index_decode_parity(name, n_split):
