@@ -234,12 +234,8 @@ def cpu_baseline(pf, budget_s=15.0):
         threads = 1
     cores = min(threads, len(os.sched_getaffinity(0)))
     return {"value": flops / t_cpu / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 masked attention, head 0, last {rows} of {nb_str(nB)} query blocks "
+            "sample": f"fp64 masked attention, head 0, last {rows} of {nB} query blocks "
                       f"({done_blocks} executed blocks, {t_cpu:.1f} s)"}
-
-
-def nb_str(n):
-    return str(n)
 
 
 def attach_workspaces(fsa, pf, dc, sg):
@@ -283,7 +279,19 @@ def profile_only(fsa, workloads, args):
     for _ in range(args.steps):
         step(fsa, pf, dc, sg, tm, parts=(args.only,))
     torch.cuda.synchronize()
+    if args.copy_probe:
+        copy_probe()
     print(json.dumps({"only": args.only, "kernel_ms": {n: round(tm.ms(n)[0], 4) for n in tm.ev}}))
+
+
+def copy_probe():
+    """A plain 1 GiB device-to-device copy, run 3 times: its FETCH_SIZE /
+    WRITE_SIZE counters calibrate the counter units (known 1 GiB each way)."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -382,11 +390,7 @@ def main():
                  "decode_group_speedup": round(ddec / group_ms, 2)}
 
     if args.copy_probe:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
+        copy_probe()
 
     cpu = None
     if not args.no_cpu_baseline:
