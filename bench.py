@@ -238,6 +238,28 @@ def cpu_baseline(pf, budget_s=15.0):
                       f"({done_blocks} executed blocks, {t_cpu:.1f} s)"}
 
 
+def profiled_traffic(key, source):
+    """HBM bytes per launch recorded by the committed rocprofv3 PMC summary
+    (FETCH_SIZE/WRITE_SIZE, copy-calibrated), or None when the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "hbm_traffic_128k_1m.md")
+    src = os.path.join(ROOT, "free_sparse_attention_head_amd", "csrc", source)
+    try:
+        text = open(prof).read()
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    tag = source + " sha256 prefix: "
+    at = text.find(tag)
+    if at < 0 or text[at + len(tag):at + len(tag) + 16] != cur:
+        return None
+    for line in text.splitlines():
+        if line.startswith(key + ":"):
+            return int(line.split(":")[1])
+    return None
+
+
 def attach_workspaces(fsa, pf, dc, sg):
     """Pre-allocate every workspace so the timed region allocates nothing."""
     P, Dd, Sg = PREFILL, DECODE, SEGMENT
@@ -416,11 +438,15 @@ def main():
                    "global_batch": 1, "seq_len": P["S"], "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_attn_kernel<bf16,128,128>",
+                     "traffic": profiled_traffic("prefill_attn_traffic_bytes_per_launch",
+                                                 "prefill_attn.hip"),
+                     "kernel": "prefill_attn_kernel<bf16,128,128>",
                      "flop_per_launch": flops, "executed_blocks": executed,
                      "avg_launch_ms": round(attn_ms, 4)},
         "roofline_decode": {"bound": "hbm", "achieved": round(reuse_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(reuse_gbps / PEAK_HBM_GBPS, 4),
+                            "traffic": profiled_traffic("decode_index_traffic_bytes_per_launch",
+                                                        "decode_attn.hip"),
                             "kernel": "decode_split_kernel<128,1,INDEX> + combine",
                             "bytes_per_launch": idx_bytes, "avg_launch_ms": round(reuse_ms, 4)},
         "prefill": {"density": round(pf["density"], 4), "p_c": pf["p_c"], "p_r": pf["p_r"],
