@@ -34,6 +34,12 @@ hipError_t launch_prefill_attn(bool f32, const void* q, const void* k, const voi
                                const PrefillDims& d, const int32_t* bidx, const int32_t* bcnt,
                                float scale, void* out, float* lse, hipStream_t st);
 
+// prefill_attn_bf16.hip
+hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
+                                    const PrefillDims& d, const int32_t* bidx,
+                                    const int32_t* bcnt, float scale, void* out, float* lse,
+                                    hipStream_t st);
+
 // topk.hip
 size_t topk_ws_bytes(const DecodeDims& d, int k);
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,

@@ -493,12 +493,8 @@ hipError_t launch_prefill_attn(bool f32, const void* q, const void* k, const voi
                                float scale, void* out, float* lse, hipStream_t st) {
 #define FSA_PA(TY, DD, TT) \
   if (d.D == DD && d.T == TT) return launch_pa<TY, DD, TT>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
-  if (f32) {
-    FSA_PA(float, 64, 64) FSA_PA(float, 64, 128) FSA_PA(float, 128, 64) FSA_PA(float, 128, 128)
-  } else {
-    FSA_PA(uint16_t, 64, 64) FSA_PA(uint16_t, 64, 128) FSA_PA(uint16_t, 128, 64)
-    FSA_PA(uint16_t, 128, 128)
-  }
+  if (!f32) return launch_prefill_attn_bf16(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  FSA_PA(float, 64, 64) FSA_PA(float, 64, 128) FSA_PA(float, 128, 64) FSA_PA(float, 128, 128)
 #undef FSA_PA
   return hipErrorInvalidValue;
 }

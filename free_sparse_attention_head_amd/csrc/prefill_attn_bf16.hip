@@ -1,0 +1,358 @@
+// sparse_prefill_attn, bf16 inputs: block-sparse causal flash-attention with
+// gfx950 direct-to-LDS tile loads and transposing LDS reads.
+//
+// RBS-Attention post, "Key technical points" 2: the merged block mask is
+// executed by an otherwise unchanged block-sparse FlashAttention path.
+//
+// One workgroup per (batch, query head, query block i): T/32 waves of 32
+// query rows.  The workgroup walks the row's causal key blocks in 64-key
+// chunks through two LDS buffers:
+//   * K and V chunks are copied HBM -> LDS with global_load_lds_dwordx4
+//     (each wave instruction lands 64 lanes x 16 B contiguously): no staging
+//     registers, no LDS store instructions, no transposes.  The next chunk's
+//     copies are issued before the current chunk is computed;
+//   * both tiles are row-major (one key per row) with an XOR swizzle of the
+//     16-byte slots, chosen by the source address of each lane, so that the
+//     fragment reads below are bank-conflict free;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the wave's Q tile resident
+//     as the B operand (each lane then holds one query row's scores);
+//   * online softmax in fp32: raw-score row max, exp2 with the scale folded
+//     into an FMA, thresholded lazy rescale of O^T;
+//   * O^T += V^T P^T: P^T comes from registers, V^T fragments come from the
+//     row-major V tile through ds_read_b64_tr_b16, which hands lane i of each
+//     16-lane group column i of the 4 x 16 tile the group addresses.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace fsa {
+
+namespace {
+
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+#define FSA_LDS __attribute__((address_space(3)))
+
+template <int D, int BLK>
+struct DirectTraits {
+  static constexpr int NW = BLK / 32;         // waves
+  static constexpr int NT = NW * 64;          // threads
+  static constexpr int KC = 64;               // keys per chunk
+  static constexpr int NCH = BLK / KC;        // chunks per key block
+  static constexpr int ROWB = D * 2;          // bytes per key row
+  static constexpr int SLOTS = ROWB / 16;     // 16-byte slots per row
+  static constexpr int TILE = KC * ROWB;      // bytes of one K (or V) chunk
+  static constexpr int RPI = 1024 / ROWB;     // rows per 1 KB load instruction
+  static constexpr int IPW = TILE / 1024 / NW;  // load instructions per wave per tile
+  static constexpr int BUF = 2 * TILE;        // K + V
+  static constexpr size_t LDS = 2 * (size_t)BUF;
+  static_assert(IPW >= 1 && TILE % (1024 * NW) == 0, "tile shape");
+};
+
+// slot swizzles: K rows XOR the low slot bits with the row, V rows XOR with
+// 2*(row % 4) so that the four rows of a transposing read hit different banks
+template <int SLOTS>
+__device__ __forceinline__ int k_swz(int row) { return row & (SLOTS - 1); }
+__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
+
+// generic -> LDS address-space pointers (a C-style cast is the supported form)
+template <typename T>
+__device__ __forceinline__ FSA_LDS T* lds_ptr(const void* p) {
+  return (FSA_LDS T*)(const_cast<void*>(p));
+}
+
+__device__ __forceinline__ void copy16_to_lds(const void* g, const void* l) {
+  __builtin_amdgcn_global_load_lds(g, lds_ptr<void>(l), 16, 0, 0);
+}
+
+}  // namespace
+
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ bidx,
+    const int32_t* __restrict__ bcnt, uint16_t* __restrict__ O, float* __restrict__ LSE, int S,
+    int Hq, int Hkv, float scale_log2, int total) {
+  using Tr = DirectTraits<D, BLK>;
+  constexpr int KC = Tr::KC, NCH = Tr::NCH, ROWB = Tr::ROWB, SLOTS = Tr::SLOTS;
+  // Two distinct LDS objects for the double buffer: the compiler can then
+  // tell that fragment reads of one never alias the copies into the other and
+  // keeps the next chunk's copies in flight during the current chunk.
+  __shared__ __align__(16) unsigned char kv0[Tr::BUF];
+  __shared__ __align__(16) unsigned char kv1[Tr::BUF];
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* Ls = reinterpret_cast<int32_t*>(smem);
+  __shared__ int scan_tmp[17];
+
+  // Work order: KV head major, query blocks longest first, then the G query
+  // heads of that KV head (the running window touches one KV head's K/V).
+  const int L = blockIdx.x;
+  if (L >= total) return;
+  const int nB = S / BLK;
+  const int G = Hq / Hkv;
+  const int hh = L % G;
+  const int rest = L / G;
+  const int i = nB - 1 - (rest % nB);
+  const int bg = rest / nB;
+  const int g = bg % Hkv, b = bg / Hkv;
+  const int h = g * G + hh;
+  const int row = (b * Hq + h) * nB + i;
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int lq = l & 31, lg = l >> 5;
+  const int qrow = wave * 32 + lq;
+  const size_t kv_stride = (size_t)Hkv * D;
+  const uint16_t* Kb = K + ((size_t)b * S * Hkv + g) * D;
+  const uint16_t* Vb = V + ((size_t)b * S * Hkv + g) * D;
+
+  // Q tile -> registers (MFMA B operand, lane = query row)
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = Q + (((size_t)b * S + (size_t)i * BLK + qrow) * Hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kk * 16 + lg * 8));
+  }
+
+  // the row's causal key blocks, compacted in order into LDS
+  const int cnt = bidx ? min(max(bcnt[row], 0), nB) : i + 1;
+  int nvalid = 0;
+  for (int e0 = 0; e0 < cnt; e0 += Tr::NT) {
+    const int e = e0 + tid;
+    int j = -1;
+    if (e < cnt) j = bidx ? bidx[(size_t)row * nB + e] : e;
+    const int ok = (j >= 0 && j <= i) ? 1 : 0;
+    int tot;
+    const int pos = block_excl_scan(ok, scan_tmp, &tot);
+    if (ok) Ls[nvalid + pos] = j;
+    nvalid += tot;
+  }
+  __syncthreads();
+  const int nchunks = nvalid * NCH;
+
+  // HBM -> LDS copy of chunk c into buffer `buf` (wave-uniform LDS bases)
+  auto issue = [&](int c, unsigned char* kt) {
+    const int s0 = Ls[c / NCH] * BLK + (c % NCH) * KC;
+    unsigned char* vt = kt + Tr::TILE;
+#pragma unroll
+    for (int m = 0; m < Tr::IPW; ++m) {
+      const int I = wave * Tr::IPW + m;
+      const int r = I * Tr::RPI + l / SLOTS;
+      const int sl = l % SLOTS;
+      const size_t grow = (size_t)(s0 + r) * kv_stride;
+      copy16_to_lds(Kb + grow + (sl ^ k_swz<SLOTS>(r)) * 8, kt + I * 1024);
+      copy16_to_lds(Vb + grow + (sl ^ v_swz(r)) * 8, vt + I * 1024);
+    }
+  };
+
+  floatx16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // per-lane LDS offsets of the fragment reads
+  const int kslot_x = lq & (SLOTS - 1);      // K row swizzle of rows lq, lq+32
+  const int li = l & 15, q16 = (l >> 4) & 1;  // transposing-read lane coordinates
+  const int vrow = lg * 4 + (li >> 2);
+  const int vcol_b = q16 * 32 + 8 * (li & 3);  // byte column inside a 64-byte dt stripe
+  const int vphys_x = 2 * (li >> 2);           // V row swizzle (row % 4 == li >> 2)
+
+  // One 64-key chunk c from tile buffer kt: S^T = K Q^T, masked online
+  // softmax, O^T += V^T P^T.
+  auto compute = [&](int c, const unsigned char* kt) {
+    const unsigned char* vt = kt + Tr::TILE;
+    const int j = Ls[c / NCH];
+    const int koff = (c % NCH) * KC;
+    const bool diag = (j == i);
+    if (diag && koff > wave * 32 + 31) return;  // all keys after this wave's rows
+
+    // ---- S^T = K Q^T, fragments of step kk+1 read before the MFMAs of step kk
+    floatx16 s[2];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[tl][r] = 0.f;
+    {
+      const unsigned char* k0 = kt + lq * ROWB;
+      const unsigned char* k1 = k0 + 32 * ROWB;
+      auto kfrag = [&](const unsigned char* rowp, int kk) {
+        return *reinterpret_cast<const uint4*>(rowp + (((2 * kk + lg) ^ kslot_x) * 16));
+      };
+      uint4 a0 = kfrag(k0, 0), a1 = kfrag(k1, 0);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        uint4 n0 = a0, n1 = a1;
+        if (kk + 1 < D / 16) {
+          n0 = kfrag(k0, kk + 1);
+          n1 = kfrag(k1, kk + 1);
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), qf[kk], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), qf[kk], s[1], 0, 0, 0);
+        a0 = n0;
+        a1 = n1;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    }
+
+    // ---- causal mask (diagonal block only), row max in raw units.
+    // Register r of tile tl holds key koff + tl*32 + (r/4)*8 + lg*4 + r%4.
+    if (diag) {
+      const int rel = koff + lg * 4 - qrow;
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (rel + tl * 32 + (r >> 2) * 8 + (r & 3) > 0) s[tl][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tl][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // lazy rescale: the reference max moves only when a row grows by more
+    // than kRescale (log2 units), so p <= 256 and O^T is rescaled rarely
+    const bool grow = (mx - m_run) * scale_log2 > kRescale;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pf[kc][e] = (__bf16)__builtin_amdgcn_exp2f(
+            fmaf(s[kc >> 1][(kc & 1) * 8 + e], scale_log2, -mc));
+    // row sum of the bf16-rounded P that the PV step multiplies
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const uint4 w = __builtin_bit_cast(uint4, pf[kc]);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), ones, l_run, false);
+    }
+
+    // ---- O^T += V^T P^T.  Step m = kc*NDT + dt; the A fragment holds keys
+    // kc*16 + lg*4 + {0..3} (first transposing read) and +8 (second) at
+    // d = dt*32 + lq; fragments are read two MFMAs ahead.
+    constexpr int NDT = D / 32, NM = 4 * NDT;
+    auto vfrag = [&](int m) {
+      const int kc = m / NDT, dt = m % NDT;
+      const int r0 = kc * 16 + vrow;
+      const int colb = dt * 64 + vcol_b;
+      const int slot = (colb >> 4) ^ vphys_x;
+      // both addresses as one offset from the tile base, so the compiler can
+      // trace them to their LDS buffer
+      const int off = r0 * ROWB + slot * 16 + (colb & 15);
+      const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_ptr<bf16x4v>(vt + off));
+      const bf16x4v hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_ptr<bf16x4v>(vt + (off + 8 * ROWB)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 f0 = vfrag(0), f1 = vfrag(1);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const bf16x8 f2 = (m + 2 < NM) ? vfrag(m + 2) : f0;
+      oacc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, pf[m / NDT], oacc[m % NDT], 0, 0, 0);
+      f0 = f1;
+      f1 = f2;
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (m + 2 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+  };
+
+  if (nchunks > 0) {
+    issue(0, kv0);
+    const int pairs = nchunks >> 1;
+    for (int pr = 0; pr < pairs; ++pr) {
+      const int c = 2 * pr;
+      // this wave's copies of chunk c have landed; the barrier publishes every
+      // wave's copies and retires all reads of the other buffer
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      issue(c + 1, kv1);
+      compute(c, kv0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (c + 2 < nchunks) issue(c + 2, kv0);
+      compute(c + 1, kv1);
+    }
+    if (nchunks & 1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      compute(nchunks - 1, kv0);
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, LSE
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int t = i * BLK + qrow;
+  uint16_t* op = O + (((size_t)b * S + t) * Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = dt * 32 + rg * 8 + lg * 4;
+      *reinterpret_cast<uint2*>(op + d0) =
+          make_uint2(pack_bf16x2(oacc[dt][rg * 4] * inv, oacc[dt][rg * 4 + 1] * inv),
+                     pack_bf16x2(oacc[dt][rg * 4 + 2] * inv, oacc[dt][rg * 4 + 3] * inv));
+    }
+  if (LSE != nullptr && lg == 0)
+    LSE[((size_t)b * Hq + h) * S + t] =
+        l_tot > 0.f ? (m_run * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+template <int D, int BLK>
+static hipError_t launch_direct(const void* q, const void* k, const void* v, const PrefillDims& d,
+                                const int32_t* bidx, const int32_t* bcnt, float scale, void* out,
+                                float* lse, hipStream_t st) {
+  using Tr = DirectTraits<D, BLK>;
+  auto kern = prefill_attn_bf16_kernel<D, BLK>;
+  const size_t lds = (size_t)(d.S / BLK) * sizeof(int32_t);
+  if (lds + Tr::LDS > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int total = d.B * d.Hq * (d.S / BLK);
+  hipLaunchKernelGGL(kern, dim3(total), dim3(Tr::NT), lds, st, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bidx, bcnt,
+                     static_cast<uint16_t*>(out), lse, d.S, d.Hq, d.Hkv, scale * kLog2e, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
+                                    const PrefillDims& d, const int32_t* bidx,
+                                    const int32_t* bcnt, float scale, void* out, float* lse,
+                                    hipStream_t st) {
+  if (d.D == 128 && d.T == 128) return launch_direct<128, 128>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (d.D == 128 && d.T == 64) return launch_direct<128, 64>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (d.D == 64 && d.T == 128) return launch_direct<64, 128>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (d.D == 64 && d.T == 64) return launch_direct<64, 64>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fsa
