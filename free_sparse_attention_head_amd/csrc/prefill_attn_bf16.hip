@@ -31,6 +31,7 @@ namespace fsa {
 namespace {
 
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr int kMaxBlocks = 4096;  // key blocks per sequence (S / T) supported
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 #define FSA_LDS __attribute__((address_space(3)))
 
@@ -50,11 +51,18 @@ struct DirectTraits {
   static_assert(IPW >= 1 && TILE % (1024 * NW) == 0, "tile shape");
 };
 
-// slot swizzles: K rows XOR the low slot bits with the row, V rows XOR with
-// 2*(row % 4) so that the four rows of a transposing read hit different banks
+// Slot swizzles.  K rows XOR the slot with the row.  A transposing V read
+// touches four consecutive rows (row % 4 = 0..3), 32 or 64 bytes of each per
+// 16 or 32 lanes; the V XOR keeps those pieces in distinct banks whether the
+// LDS serves 16 lanes from 32 banks or 32 lanes from 64 banks per cycle.
 template <int SLOTS>
 __device__ __forceinline__ int k_swz(int row) { return row & (SLOTS - 1); }
-__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
+template <int SLOTS>
+__device__ __forceinline__ int v_swz(int row) {
+  const int r = row & 3;
+  if constexpr (SLOTS == 16) return 4 * r ^ 2 * ((r ^ (r >> 1)) & 1);  // 0, 6, 10, 12
+  else return 2 * r;  // 128-byte rows: two rows per 256 bytes already differ
+}
 
 // generic -> LDS address-space pointers (a C-style cast is the supported form)
 template <typename T>
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ bidx,
     const int32_t* __restrict__ bcnt, uint16_t* __restrict__ O, float* __restrict__ LSE, int S,
-    int Hq, int Hkv, float scale_log2, int total) {
+    int Hq, int Hkv, float scale_log2, int units) {
   using Tr = DirectTraits<D, BLK>;
   constexpr int KC = Tr::KC, NCH = Tr::NCH, ROWB = Tr::ROWB, SLOTS = Tr::SLOTS;
   // Two distinct LDS objects for the double buffer: the compiler can then
@@ -81,18 +89,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // keeps the next chunk's copies in flight during the current chunk.
   __shared__ __align__(16) unsigned char kv0[Tr::BUF];
   __shared__ __align__(16) unsigned char kv1[Tr::BUF];
-  extern __shared__ __align__(16) unsigned char smem[];
-  int32_t* Ls = reinterpret_cast<int32_t*>(smem);
+  // the row's key blocks; a static array (not dynamic LDS), so the compiler
+  // can also tell list reads apart from the tile copies in flight
+  __shared__ uint16_t Ls[kMaxBlocks];
   __shared__ int scan_tmp[17];
 
-  // Work order: KV head major, query blocks longest first, then the G query
-  // heads of that KV head (the running window touches one KV head's K/V).
-  const int L = blockIdx.x;
-  if (L >= total) return;
+  // Work order: a unit is one (batch, KV head, query block); units run KV
+  // head major, longest query blocks first.  The G query heads of a unit read
+  // largely the same K/V blocks, so all G workgroups of a unit go to one XCD
+  // (one L2) back to back: workgroups are dealt to the XCDs round-robin, so
+  // XCD x takes every kXcds-th unit and its n-th workgroup is head n % G of
+  // its (n / G)-th unit.  Every XCD walks the unit order at the same pace.
   const int nB = S / BLK;
   const int G = Hq / Hkv;
-  const int hh = L % G;
-  const int rest = L / G;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int rest = (slot / G) * kXcds + xcd;  // unit
+  const int hh = slot % G;
+  if (rest >= units) return;
   const int i = nB - 1 - (rest % nB);
   const int bg = rest / nB;
   const int g = bg % Hkv, b = bg / Hkv;
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     const int ok = (j >= 0 && j <= i) ? 1 : 0;
     int tot;
     const int pos = block_excl_scan(ok, scan_tmp, &tot);
-    if (ok) Ls[nvalid + pos] = j;
+    if (ok) Ls[nvalid + pos] = (uint16_t)j;
     nvalid += tot;
   }
   __syncthreads();
@@ -142,8 +155,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
       const int sl = l % SLOTS;
       const size_t grow = (size_t)(s0 + r) * kv_stride;
       copy16_to_lds(Kb + grow + (sl ^ k_swz<SLOTS>(r)) * 8, kt + I * 1024);
-      copy16_to_lds(Vb + grow + (sl ^ v_swz(r)) * 8, vt + I * 1024);
+      copy16_to_lds(Vb + grow + (sl ^ v_swz<SLOTS>(r)) * 8, vt + I * 1024);
     }
+  };
+
+  // Pipeline barrier: this wave's tile copies have landed and its LDS reads
+  // have retired; the s_barrier then publishes every wave's copies and frees
+  // the other buffer.
+  auto tile_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
   floatx16 oacc[D / 32];
@@ -158,7 +179,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   const int li = l & 15, q16 = (l >> 4) & 1;  // transposing-read lane coordinates
   const int vrow = lg * 4 + (li >> 2);
   const int vcol_b = q16 * 32 + 8 * (li & 3);  // byte column inside a 64-byte dt stripe
-  const int vphys_x = 2 * (li >> 2);           // V row swizzle (row % 4 == li >> 2)
+  const int vphys_x = v_swz<SLOTS>(li >> 2);   // V row swizzle (row % 4 == li >> 2)
 
   // One 64-key chunk c from tile buffer kt: S^T = K Q^T, masked online
   // softmax, O^T += V^T P^T.
@@ -284,25 +305,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   };
 
   if (nchunks > 0) {
+    const int last = nchunks - 1;
     issue(0, kv0);
     const int pairs = nchunks >> 1;
     for (int pr = 0; pr < pairs; ++pr) {
       const int c = 2 * pr;
       // this wave's copies of chunk c have landed; the barrier publishes every
       // wave's copies and retires all reads of the other buffer
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      tile_barrier();
       issue(c + 1, kv1);
       compute(c, kv0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      tile_barrier();
       if (c + 2 < nchunks) issue(c + 2, kv0);
       compute(c + 1, kv1);
     }
     if (nchunks & 1) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      compute(nchunks - 1, kv0);
+      tile_barrier();
+      compute(last, kv0);
     }
   }
 
@@ -331,16 +350,13 @@ static hipError_t launch_direct(const void* q, const void* k, const void* v, con
                                 float* lse, hipStream_t st) {
   using Tr = DirectTraits<D, BLK>;
   auto kern = prefill_attn_bf16_kernel<D, BLK>;
-  const size_t lds = (size_t)(d.S / BLK) * sizeof(int32_t);
-  if (lds + Tr::LDS > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const int total = d.B * d.Hq * (d.S / BLK);
-  hipLaunchKernelGGL(kern, dim3(total), dim3(Tr::NT), lds, st, static_cast<const uint16_t*>(q),
+  if (d.S / BLK > kMaxBlocks) return hipErrorInvalidValue;
+  const size_t lds = 0;
+  const int units = d.B * d.Hkv * (d.S / BLK);
+  const int grid = (units + kXcds - 1) / kXcds * kXcds * (d.Hq / d.Hkv);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Tr::NT), lds, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bidx, bcnt,
-                     static_cast<uint16_t*>(out), lse, d.S, d.Hq, d.Hkv, scale * kLog2e, total);
+                     static_cast<uint16_t*>(out), lse, d.S, d.Hq, d.Hkv, scale * kLog2e, units);
   return hipGetLastError();
 }
 
