@@ -112,7 +112,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   const int h = g * G + hh;
   const int row = (b * Hq + h) * nB + i;
 
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = l & 31, lg = l >> 5;
   const int qrow = wave * 32 + lq;
   const size_t kv_stride = (size_t)Hkv * D;
@@ -144,18 +145,28 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   __syncthreads();
   const int nchunks = nvalid * NCH;
 
-  // HBM -> LDS copy of chunk c into buffer `buf` (wave-uniform LDS bases)
+  // HBM -> LDS copy of chunk c into tile buffer kt: a wave-uniform source
+  // base plus fixed per-lane byte offsets (row, swizzled slot) and a
+  // wave-uniform LDS base per instruction
+  uint32_t kofs[Tr::IPW], vofs[Tr::IPW];
+#pragma unroll
+  for (int m = 0; m < Tr::IPW; ++m) {
+    const int r = (wave * Tr::IPW + m) * Tr::RPI + l / SLOTS;
+    const int sl = l % SLOTS;
+    kofs[m] = (uint32_t)((r * kv_stride + (sl ^ k_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
+    vofs[m] = (uint32_t)((r * kv_stride + (sl ^ v_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
+  }
   auto issue = [&](int c, unsigned char* kt) {
-    const int s0 = Ls[c / NCH] * BLK + (c % NCH) * KC;
+    const int j = __builtin_amdgcn_readfirstlane(Ls[c / NCH]);
+    const size_t base = ((size_t)j * BLK + (c % NCH) * KC) * kv_stride * sizeof(uint16_t);
+    const char* kb = reinterpret_cast<const char*>(Kb) + base;
+    const char* vb = reinterpret_cast<const char*>(Vb) + base;
     unsigned char* vt = kt + Tr::TILE;
 #pragma unroll
     for (int m = 0; m < Tr::IPW; ++m) {
       const int I = wave * Tr::IPW + m;
-      const int r = I * Tr::RPI + l / SLOTS;
-      const int sl = l % SLOTS;
-      const size_t grow = (size_t)(s0 + r) * kv_stride;
-      copy16_to_lds(Kb + grow + (sl ^ k_swz<SLOTS>(r)) * 8, kt + I * 1024);
-      copy16_to_lds(Vb + grow + (sl ^ v_swz<SLOTS>(r)) * 8, vt + I * 1024);
+      copy16_to_lds(kb + kofs[m], kt + I * 1024);
+      copy16_to_lds(vb + vofs[m], vt + I * 1024);
     }
   };
 
