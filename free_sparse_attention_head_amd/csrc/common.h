@@ -49,7 +49,10 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // DPP lane moves inside a 16-lane row (bound_ctrl off, all rows/banks on).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  // old = 0 with bound_ctrl: the form the compiler folds into the consuming
+  // add as a DPP operand (every lane has a valid source for these patterns)
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
 }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]

@@ -91,20 +91,38 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
         kr[r] = make_uint4(0, 0, 0, 0);
     }
   };
+  // Scores leave in a coalesced layout: a wave's RG*RB rows of a step are W
+  // consecutive tokens, so lane l takes token l % W for the head slot l / W
+  // and the heads l / W + k*HS, writing whole lines per head.  After the group
+  // sums every lane of a row group holds all G*RB sums of its RB tokens; lane
+  // dl of group s first picks token s*RB + dl % RB for heads dl / RB + k*HS,
+  // which is exactly what lane ((t / RB)*LPR + hs*RB + t % RB) must hand to the
+  // lane of token t and head slot hs.
+  constexpr int W = RG * RB, HS = 64 / W, NV = (G + HS - 1) / HS;
+  static_assert(LPR == HS * RB, "row group covers the head slots");
+  const int tw = l % W, hs = l / W;
+  const int src = (tw / RB) * LPR + hs * RB + tw % RB;
+  const int pick_r = dl % RB, pick_h = dl / RB;
   auto score_rows = [&](int base, const uint4 (&kr)[RB]) {
     float sc[G][RB];
 #pragma unroll
     for (int x = 0; x < G; ++x)
 #pragma unroll
       for (int r = 0; r < RB; ++r) sc[x][r] = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
-    // lane dl writes score (x, r) for z = x*RB + r = dl, dl + LPR, ...
+    const int tok = base + wave * W + tw;
 #pragma unroll
-    for (int z = 0; z < G * RB; ++z) {
-      if (z % LPR != dl) continue;
-      const int x = z / RB, r = z % RB;
-      const int tok = base + slot * RB + r;
-      if (tok < t1) {
-        const float v = sc[x][r] + 0.0f;
+    for (int k = 0; k < NV; ++k) {
+      float v = 0.f;
+#pragma unroll
+      for (int x = k * HS; x < G && x < (k + 1) * HS; ++x) {
+        float vx = sc[x][0];
+#pragma unroll
+        for (int r = 1; r < RB; ++r) vx = pick_r == r ? sc[x][r] : vx;
+        v = pick_h == x - k * HS ? vx : v;
+      }
+      v = __shfl(v, src, 64) + 0.0f;  // + 0 folds -0 onto +0
+      const int x = hs + k * HS;
+      if (x < G && tok < t1) {
         scores[((size_t)b * Hq + g * G + x) * stride + tok] = v;
         atomicAdd(&lh[x][order_key(v) >> 21], 1u);
       }
