@@ -23,6 +23,8 @@
 //     16-lane group column i of the 4 x 16 tile the group addresses.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -87,8 +89,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // Two distinct LDS objects for the double buffer: the compiler can then
   // tell that fragment reads of one never alias the copies into the other and
   // keeps the next chunk's copies in flight during the current chunk.
-  __shared__ __align__(16) unsigned char kv0[Tr::BUF];
-  __shared__ __align__(16) unsigned char kv1[Tr::BUF];
+  __shared__ __align__(16) unsigned char kb0[Tr::TILE];
+  __shared__ __align__(16) unsigned char kb1[Tr::TILE];
+  __shared__ __align__(16) unsigned char vb0[Tr::TILE];
+  __shared__ __align__(16) unsigned char vb1[Tr::TILE];
   // the row's key blocks; a static array (not dynamic LDS), so the compiler
   // can also tell list reads apart from the tile copies in flight
   __shared__ uint16_t Ls[kMaxBlocks];
@@ -156,19 +160,17 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     kofs[m] = (uint32_t)((r * kv_stride + (sl ^ k_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
     vofs[m] = (uint32_t)((r * kv_stride + (sl ^ v_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
   }
-  auto issue = [&](int c, unsigned char* kt) {
+  auto issue_tile = [&](int c, const uint16_t* src0, const uint32_t (&ofs)[Tr::IPW],
+                        unsigned char* tile) {
     const int j = __builtin_amdgcn_readfirstlane(Ls[c / NCH]);
     const size_t base = ((size_t)j * BLK + (c % NCH) * KC) * kv_stride * sizeof(uint16_t);
-    const char* kb = reinterpret_cast<const char*>(Kb) + base;
-    const char* vb = reinterpret_cast<const char*>(Vb) + base;
-    unsigned char* vt = kt + Tr::TILE;
+    const char* src = reinterpret_cast<const char*>(src0) + base;
 #pragma unroll
-    for (int m = 0; m < Tr::IPW; ++m) {
-      const int I = wave * Tr::IPW + m;
-      copy16_to_lds(kb + kofs[m], kt + I * 1024);
-      copy16_to_lds(vb + vofs[m], vt + I * 1024);
-    }
+    for (int m = 0; m < Tr::IPW; ++m)
+      copy16_to_lds(src + ofs[m], tile + (wave * Tr::IPW + m) * 1024);
   };
+  auto issue_k = [&](int c, unsigned char* kt) { issue_tile(c, Kb, kofs, kt); };
+  auto issue_v = [&](int c, unsigned char* vt) { issue_tile(c, Vb, vofs, vt); };
 
   // Pipeline barrier: this wave's tile copies have landed and its LDS reads
   // have retired; the s_barrier then publishes every wave's copies and frees
@@ -191,52 +193,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   const int vrow = lg * 4 + (li >> 2);
   const int vcol_b = q16 * 32 + 8 * (li & 3);  // byte column inside a 64-byte dt stripe
   const int vphys_x = v_swz<SLOTS>(li >> 2);   // V row swizzle (row % 4 == li >> 2)
+  constexpr int NKK = D / 16;                  // MFMA k-steps of S
+  constexpr int NDT = D / 32, NM = 4 * NDT;    // MFMAs of PV
 
-  // One 64-key chunk c from tile buffer kt: S^T = K Q^T, masked online
-  // softmax, O^T += V^T P^T.
-  auto compute = [&](int c, const unsigned char* kt) {
-    const unsigned char* vt = kt + Tr::TILE;
+  // K fragment of MFMA step kk for key row rowp (two 8-element halves: lg)
+  auto kfrag = [&](const unsigned char* rowp, int kk) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                          rowp + (((2 * kk + lg) ^ kslot_x) * 16)));
+  };
+
+  // Causal mask (diagonal block only), row max in raw units and the lazy
+  // rescale for chunk c; returns the exponent offset of P.  Register r of
+  // tile tl holds key koff + tl*32 + (r/4)*8 + lg*4 + r%4.  Chunks wholly
+  // after this wave's rows come out all masked (P = 0).
+  auto prelude = [&](int c, floatx16 (&s)[2]) -> float {
     const int j = Ls[c / NCH];
     const int koff = (c % NCH) * KC;
-    const bool diag = (j == i);
-    if (diag && koff > wave * 32 + 31) return;  // all keys after this wave's rows
-
-    // ---- S^T = K Q^T, fragments of step kk+1 read before the MFMAs of step kk
-    floatx16 s[2];
-#pragma unroll
-    for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[tl][r] = 0.f;
-    {
-      const unsigned char* k0 = kt + lq * ROWB;
-      const unsigned char* k1 = k0 + 32 * ROWB;
-      auto kfrag = [&](const unsigned char* rowp, int kk) {
-        return *reinterpret_cast<const uint4*>(rowp + (((2 * kk + lg) ^ kslot_x) * 16));
-      };
-      uint4 a0 = kfrag(k0, 0), a1 = kfrag(k1, 0);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        uint4 n0 = a0, n1 = a1;
-        if (kk + 1 < D / 16) {
-          n0 = kfrag(k0, kk + 1);
-          n1 = kfrag(k1, kk + 1);
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), qf[kk], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), qf[kk], s[1], 0, 0, 0);
-        a0 = n0;
-        a1 = n1;
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
-    }
-
-    // ---- causal mask (diagonal block only), row max in raw units.
-    // Register r of tile tl holds key koff + tl*32 + (r/4)*8 + lg*4 + r%4.
-    if (diag) {
+    if (j == i) {
       const int rel = koff + lg * 4 - qrow;
 #pragma unroll
       for (int tl = 0; tl < 2; ++tl)
@@ -263,29 +236,70 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[kc][e] = (__bf16)__builtin_amdgcn_exp2f(
-            fmaf(s[kc >> 1][(kc & 1) * 8 + e], scale_log2, -mc));
-    // row sum of the bf16-rounded P that the PV step multiplies
-    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const uint4 w = __builtin_bit_cast(uint4, pf[kc]);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), ones, l_run, false);
-    }
+    return (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+  };
 
-    // ---- O^T += V^T P^T.  Step m = kc*NDT + dt; the A fragment holds keys
-    // kc*16 + lg*4 + {0..3} (first transposing read) and +8 (second) at
-    // d = dt*32 + lq; fragments are read two MFMAs ahead.
-    constexpr int NDT = D / 32, NM = 4 * NDT;
+  // One sixteenth of the softmax of a chunk: P elements 2q and 2q+1 of the
+  // lane's 32 (bf16, packed into pp[q]) and their share of the row sum.
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  auto p_slice = [&](const floatx16 (&s)[2], float mc, uint32_t (&pp)[16], int q) {
+    const int e0 = 2 * q;  // element index kc*8 + e of P
+    const float x0 = s[e0 >> 4][e0 & 15], x1 = s[(e0 + 1) >> 4][(e0 + 1) & 15];
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, scale_log2, -mc));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, scale_log2, -mc));
+    bf16x2 pb;
+    pb[0] = (__bf16)p0;
+    pb[1] = (__bf16)p1;
+    pp[q] = __builtin_bit_cast(uint32_t, pb);
+    // row sum of the bf16-rounded P that the PV step multiplies
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_run, false);
+  };
+
+  // S^T = K Q^T of the next chunk from K tile kS into sn (two 32x32 tiles:
+  // keys 0-31 and 32-63), interleaved with the softmax of the current chunk
+  // (sc, mc -> pp): after each S MFMA 8 / NKK P slices.  K fragments of step kk+1
+  // are read before the MFMAs of step kk.  Either half may be absent.
+  auto s_and_p = [&](auto has_s, auto has_p, const unsigned char* kS, floatx16 (&sn)[2],
+                     const floatx16 (&sc)[2], float mc, uint32_t (&pp)[16]) {
+    constexpr bool DO_S = decltype(has_s)::value, DO_P = decltype(has_p)::value;
+    constexpr int SPM = 8 / NKK;  // P slices after each S MFMA (16 slices in all)
+    static_assert(SPM * NKK == 8, "head dimension");
+    const unsigned char* k0 = kS + lq * ROWB;
+    const unsigned char* k1 = k0 + 32 * ROWB;
+    const floatx16 zero = {};
+    bf16x8 a0, a1;
+    if constexpr (DO_S) {
+      a0 = kfrag(k0, 0);
+      a1 = kfrag(k1, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8 n0 = a0, n1 = a1;
+      if constexpr (DO_S) {
+        if (kk + 1 < NKK) {
+          n0 = kfrag(k0, kk + 1);
+          n1 = kfrag(k1, kk + 1);
+        }
+        sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], kk ? sn[0] : zero, 0, 0, 0);
+      }
+      if constexpr (DO_P)
+#pragma unroll
+        for (int q = 0; q < SPM; ++q) p_slice(sc, mc, pp, 2 * kk * SPM + q);
+      if constexpr (DO_S)
+        sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], kk ? sn[1] : zero, 0, 0, 0);
+      if constexpr (DO_P)
+#pragma unroll
+        for (int q = 0; q < SPM; ++q) p_slice(sc, mc, pp, (2 * kk + 1) * SPM + q);
+      a0 = n0;
+      a1 = n1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // O^T += V^T P^T from V tile vt.  PV step m = kc*NDT + dt: the A fragment
+  // holds keys kc*16 + lg*4 + {0..3} (first transposing read) and +8
+  // (second) at d = dt*32 + lq; fragments are read two MFMAs ahead.
+  auto pv = [&](const uint32_t (&pp)[16], const unsigned char* vt) {
     auto vfrag = [&](int m) {
       const int kc = m / NDT, dt = m % NDT;
       const int r0 = kc * 16 + vrow;
@@ -303,36 +317,56 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const bf16x8 f2 = (m + 2 < NM) ? vfrag(m + 2) : f0;
-      oacc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, pf[m / NDT], oacc[m % NDT], 0, 0, 0);
+      const int kc = m / NDT;
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, make_uint4(pp[4 * kc], pp[4 * kc + 1], pp[4 * kc + 2], pp[4 * kc + 3]));
+      oacc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, pb, oacc[m % NDT], 0, 0, 0);
       f0 = f1;
       f1 = f2;
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      if (m + 2 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (m + 2 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
 
-  if (nchunks > 0) {
-    const int last = nchunks - 1;
-    issue(0, kv0);
-    const int pairs = nchunks >> 1;
-    for (int pr = 0; pr < pairs; ++pr) {
-      const int c = 2 * pr;
-      // this wave's copies of chunk c have landed; the barrier publishes every
-      // wave's copies and retires all reads of the other buffer
-      tile_barrier();
-      issue(c + 1, kv1);
-      compute(c, kv0);
-      tile_barrier();
-      if (c + 2 < nchunks) issue(c + 2, kv0);
-      compute(c + 1, kv1);
+  // K and V chunks live in separate two-deep rings (chunk c in kb[c%2] and
+  // vb[c%2]).  Step c computes S of chunk c+1 alongside the softmax of chunk
+  // c, then PV of chunk c, so at its start K of c+1 and V of c must have
+  // landed; it then refills the K slot of chunk c (read by the previous step)
+  // with chunk c+2 and the V slot of chunk c-1 with chunk c+1.
+  const int n = nchunks;
+  auto step = [&](auto has_next, int c, const unsigned char* kS, const unsigned char* vP,
+                  unsigned char* kI, unsigned char* vI, floatx16 (&sc)[2], floatx16 (&sn)[2]) {
+    tile_barrier();
+    if (c + 2 < n) issue_k(c + 2, kI);
+    if (c + 1 < n) issue_v(c + 1, vI);
+    const float mc = prelude(c, sc);
+    uint32_t pp[16];
+    s_and_p(has_next, std::true_type{}, kS, sn, sc, mc, pp);
+    pv(pp, vP);
+  };
+
+  if (n > 0) {
+    floatx16 sA[2], sB[2];
+    uint32_t pp0[16];
+    issue_k(0, kb0);
+    issue_v(0, vb0);
+    if (n > 1) issue_k(1, kb1);
+    tile_barrier();
+    s_and_p(std::true_type{}, std::false_type{}, kb0, sA, sB, 0.f, pp0);
+    int c = 0;
+    for (; c + 2 < n; c += 2) {
+      step(std::true_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
+      step(std::true_type{}, c + 1, kb0, vb1, kb1, vb0, sB, sA);
     }
-    if (nchunks & 1) {
-      tile_barrier();
-      compute(last, kv0);
+    if (c + 1 < n) {
+      step(std::true_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
+      step(std::false_type{}, c + 1, kb0, vb1, kb1, vb0, sB, sA);
+    } else {
+      step(std::false_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
     }
   }
 
