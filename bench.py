@@ -439,8 +439,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("prefill_attn_traffic_bytes_per_launch",
-                                                 "prefill_attn.hip"),
-                     "kernel": "prefill_attn_kernel<bf16,128,128>",
+                                                 "prefill_attn_bf16.hip"),
+                     "kernel": "prefill_attn_bf16_kernel<128,128>",
                      "flop_per_launch": flops, "executed_blocks": executed,
                      "avg_launch_ms": round(attn_ms, 4)},
         "roofline_decode": {"bound": "hbm", "achieved": round(reuse_gbps, 1), "peak": PEAK_HBM_GBPS,
