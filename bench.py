@@ -13,7 +13,10 @@ One step runs every row of the hot path once over resident synthetic inputs:
   segment decode, 1M context (B=4, same heads, shuffled pages): global, focus
     (2048-token chunk + 1024 local tail), local (1024) and streaming
     (4 sinks + 1024 window) masks, caches flushed before each small mode.
-Kernel times come from HIP events on the launch stream.  The headline value
+Outside the timed steps: own dense baselines, and the attention kernel at 3%
+and 12% density on the 128K prompt and on the 32K prompt with 64-token blocks
+at 10% (skip with --no-sweep).
+Kernel times (medians) come from HIP events on the launch stream.  The headline value
 is the sparse prefill attention kernel's effective TFLOP/s on executed
 blocks (4*T*T*D FLOP per executed query-block/key-block pair); decode is
 reported as admitted KV bytes per second.
@@ -38,6 +41,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 PREFILL = dict(B=1, S=131072, Hq=32, Hkv=4, D=128, T=128, band=8, sink=1)
+PREFILL_32K = dict(B=1, S=32768, Hq=32, Hkv=8, D=128, T=64, band=0, sink=0)
 DECODE = dict(B=32, N=131072, Hq=32, Hkv=8, D=128, k=2048, layers=4)
 SEGMENT = dict(B=4, N=1 << 20, Hq=32, Hkv=8, D=128)
 
@@ -61,41 +65,78 @@ class Timer:
         return r
 
     def ms(self, name, skip=0):
+        """(median, min) in ms of the recorded launches after the first `skip`."""
         xs = [s.elapsed_time(e) for s, e in self.ev[name][skip:]]
-        return float(np.mean(xs)), float(np.min(xs))
+        return float(np.median(xs)), float(np.min(xs))
 
     def clear(self):
         self.ev = {}
 
 
-def make_prefill(fsa, workloads, density, seed=1002):
-    P = PREFILL
-    log(f"[bench] generating prefill inputs S={P['S']} Hq={P['Hq']} Hkv={P['Hkv']}")
-    inp = workloads.prefill_inputs(1, P["S"], P["Hq"], P["Hkv"], P["D"], P["T"], model="lowrank",
-                                   seed=seed, device="cuda")
-    q, k, v = inp["q"], inp["k"], inp["v"]
-    c, r = fsa.block_stats(k, P["T"])
+def tune_selector(fsa, q, c, r, P, density, out=None):
+    """Bisect p_c (p_r = 0.4 p_c) until the selector's density is within
+    0.25 points of the target; returns (p_c, density, selector outputs)."""
     nB = P["S"] // P["T"]
     visible = P["Hq"] * nB * (nB + 1) // 2
-    out = None
     lo, hi = 0.0, 1.0
-    best = None
-    for it in range(30):
+    pc = dens = None
+    for _ in range(30):
         pc = 0.5 * (lo + hi)
         out = fsa.select_blocks(q, c, r, P["T"], pc, 0.4 * pc, P["band"], P["sink"], out=out)
         dens = out["block_cnt"].sum().item() / visible
-        best = (pc, dens)
         if abs(dens - density) <= 0.0025:
             break
         if dens < density:
             lo = pc
         else:
             hi = pc
-    pc, dens = best
-    log(f"[bench] selector p_c={pc:.5f} p_r={0.4 * pc:.5f} density={dens:.4f}")
+    log(f"[bench] S={P['S']} T={P['T']} selector p_c={pc:.5f} p_r={0.4 * pc:.5f} density={dens:.4f}")
+    return pc, dens, out
+
+
+def make_prefill(fsa, workloads, density, seed=1002, P=None):
+    P = P or PREFILL
+    log(f"[bench] generating prefill inputs S={P['S']} Hq={P['Hq']} Hkv={P['Hkv']} T={P['T']}")
+    inp = workloads.prefill_inputs(1, P["S"], P["Hq"], P["Hkv"], P["D"], P["T"], model="lowrank",
+                                   seed=seed, device="cuda")
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    c, r = fsa.block_stats(k, P["T"])
+    pc, dens, out = tune_selector(fsa, q, c, r, P, density)
     return dict(q=q, k=k, v=v, p_c=pc, p_r=0.4 * pc, density=dens, sel=out, c=c, r=r,
                 o=torch.empty_like(q), lse=torch.empty((1, P["Hq"], P["S"]), dtype=torch.float32,
                                                       device="cuda"))
+
+
+def time_attention(fsa, pf, P, reps=5):
+    """Median / min of `reps` attention launches (after 2 warm-ups) on pf's selection."""
+    tm = Timer()
+    for _ in range(2 + reps):
+        tm.run("a", lambda: fsa.sparse_prefill_attn(pf["q"], pf["k"], pf["v"], P["T"],
+                                                    pf["sel"]["block_idx"], pf["sel"]["block_cnt"],
+                                                    out=pf["o"], lse=pf["lse"]))
+    torch.cuda.synchronize()
+    xs = sorted(s.elapsed_time(e) for s, e in tm.ev["a"][2:])
+    executed = int(pf["sel"]["block_cnt"].sum().item())
+    flops = 4.0 * P["T"] * P["T"] * P["D"] * executed
+    med = xs[len(xs) // 2]
+    return {"density": round(pf["density"], 4), "attn_median_ms": round(med, 4),
+            "attn_min_ms": round(xs[0], 4), "TFLOPs": round(flops / med / 1e9, 1),
+            "frac_peak": round(flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
+def prefill_sweep(fsa, workloads, pf):
+    """Attention timings outside the timed steps: the 128K prompt at 3% and 12%
+    density (the steps run 6%), and the 32K prompt with 64-token blocks at 10%."""
+    res = {}
+    for dens in (0.03, 0.12):
+        pc, d, sel = tune_selector(fsa, pf["q"], pf["c"], pf["r"], PREFILL, dens)
+        res[f"128k_{int(round(dens * 100))}pct"] = time_attention(fsa, dict(pf, sel=sel, density=d), PREFILL)
+        del sel
+    p32 = make_prefill(fsa, workloads, 0.10, seed=1001, P=PREFILL_32K)
+    res["32k_block64_10pct"] = time_attention(fsa, p32, PREFILL_32K)
+    del p32
+    torch.cuda.empty_cache()
+    return res
 
 
 def make_decode(fsa, workloads, seed=1003):
@@ -324,6 +365,7 @@ def main():
     ap.add_argument("--density", type=float, default=0.06)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the prefill density sweep")
     ap.add_argument("--only", choices=["prefill", "decode", "segment"], default=None,
                     help="profile one part of the step only (not a benchmark result)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -411,6 +453,11 @@ def main():
                                               (ddec * 1e-3) / 1e9, 1),
                  "decode_group_speedup": round(ddec / group_ms, 2)}
 
+    sweep = {}
+    if not args.no_sweep:
+        log("[bench] prefill density sweep and 32K prompt")
+        sweep = prefill_sweep(fsa, workloads, pf)
+
     if args.copy_probe:
         copy_probe()
 
@@ -462,6 +509,7 @@ def main():
                    "group_GBps": round(group_bytes / (group_ms * 1e-3) / 1e9, 1)},
         "segment_1M": seg,
         "dense": dense,
+        "prefill_sweep": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

@@ -37,11 +37,12 @@ constexpr int kMaxBlocks = 4096;  // key blocks per sequence (S / T) supported
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 #define FSA_LDS __attribute__((address_space(3)))
 
-template <int D, int BLK>
+template <int D, int BLK, int KCH>
 struct DirectTraits {
   static constexpr int NW = BLK / 32;         // waves
   static constexpr int NT = NW * 64;          // threads
-  static constexpr int KC = 64;               // keys per chunk
+  static constexpr int KC = KCH;              // keys per chunk (32 or 64)
+  static constexpr int NKT = KC / 32;         // 32-key S tiles per chunk
   static constexpr int NCH = BLK / KC;        // chunks per key block
   static constexpr int ROWB = D * 2;          // bytes per key row
   static constexpr int SLOTS = ROWB / 16;     // 16-byte slots per row
@@ -78,14 +79,15 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, const void* l) {
 
 }  // namespace
 
-template <int D, int BLK>
+template <int D, int BLK, int KCH, int LMAX>
 __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ bidx,
     const int32_t* __restrict__ bcnt, uint16_t* __restrict__ O, float* __restrict__ LSE, int S,
     int Hq, int Hkv, float scale_log2, int units) {
-  using Tr = DirectTraits<D, BLK>;
-  constexpr int KC = Tr::KC, NCH = Tr::NCH, ROWB = Tr::ROWB, SLOTS = Tr::SLOTS;
+  using Tr = DirectTraits<D, BLK, KCH>;
+  constexpr int KC = Tr::KC, NKT = Tr::NKT, NCH = Tr::NCH, ROWB = Tr::ROWB, SLOTS = Tr::SLOTS;
+  constexpr int NP = NKT * 8;  // packed bf16 pairs of P per lane per chunk
   // Two distinct LDS objects for the double buffer: the compiler can then
   // tell that fragment reads of one never alias the copies into the other and
   // keeps the next chunk's copies in flight during the current chunk.
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   __shared__ __align__(16) unsigned char vb1[Tr::TILE];
   // the row's key blocks; a static array (not dynamic LDS), so the compiler
   // can also tell list reads apart from the tile copies in flight
-  __shared__ uint16_t Ls[kMaxBlocks];
+  __shared__ uint16_t Ls[LMAX];
   __shared__ int scan_tmp[17];
 
   // Work order: a unit is one (batch, KV head, query block); units run KV
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   const int vcol_b = q16 * 32 + 8 * (li & 3);  // byte column inside a 64-byte dt stripe
   const int vphys_x = v_swz<SLOTS>(li >> 2);   // V row swizzle (row % 4 == li >> 2)
   constexpr int NKK = D / 16;                  // MFMA k-steps of S
-  constexpr int NDT = D / 32, NM = 4 * NDT;    // MFMAs of PV
+  constexpr int NDT = D / 32, NM = (KC / 16) * NDT;  // MFMAs of PV
 
   // K fragment of MFMA step kk for key row rowp (two 8-element halves: lg)
   auto kfrag = [&](const unsigned char* rowp, int kk) {
@@ -206,20 +208,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // rescale for chunk c; returns the exponent offset of P.  Register r of
   // tile tl holds key koff + tl*32 + (r/4)*8 + lg*4 + r%4.  Chunks wholly
   // after this wave's rows come out all masked (P = 0).
-  auto prelude = [&](int c, floatx16 (&s)[2]) -> float {
+  auto prelude = [&](int c, floatx16 (&s)[NKT]) -> float {
     const int j = Ls[c / NCH];
     const int koff = (c % NCH) * KC;
     if (j == i) {
       const int rel = koff + lg * 4 - qrow;
 #pragma unroll
-      for (int tl = 0; tl < 2; ++tl)
+      for (int tl = 0; tl < NKT; ++tl)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (rel + tl * 32 + (r >> 2) * 8 + (r & 3) > 0) s[tl][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int tl = 0; tl < 2; ++tl)
+    for (int tl = 0; tl < NKT; ++tl)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tl][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // One sixteenth of the softmax of a chunk: P elements 2q and 2q+1 of the
   // lane's 32 (bf16, packed into pp[q]) and their share of the row sum.
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  auto p_slice = [&](const floatx16 (&s)[2], float mc, uint32_t (&pp)[16], int q) {
+  auto p_slice = [&](const floatx16 (&s)[NKT], float mc, uint32_t (&pp)[NP], int q) {
     const int e0 = 2 * q;  // element index kc*8 + e of P
     const float x0 = s[e0 >> 4][e0 & 15], x1 = s[(e0 + 1) >> 4][(e0 + 1) & 15];
     const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, scale_log2, -mc));
@@ -255,43 +257,43 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_run, false);
   };
 
-  // S^T = K Q^T of the next chunk from K tile kS into sn (two 32x32 tiles:
-  // keys 0-31 and 32-63), interleaved with the softmax of the current chunk
-  // (sc, mc -> pp): after each S MFMA 8 / NKK P slices.  K fragments of step kk+1
+  // S^T = K Q^T of the next chunk from K tile kS into sn (NKT 32x32 tiles:
+  // keys 0-31, 32-63), interleaved with the softmax of the current chunk (sc,
+  // mc -> pp): after each S MFMA 8 / NKK P slices.  K fragments of step kk+1
   // are read before the MFMAs of step kk.  Either half may be absent.
-  auto s_and_p = [&](auto has_s, auto has_p, const unsigned char* kS, floatx16 (&sn)[2],
-                     const floatx16 (&sc)[2], float mc, uint32_t (&pp)[16]) {
+  auto s_and_p = [&](auto has_s, auto has_p, const unsigned char* kS, floatx16 (&sn)[NKT],
+                     const floatx16 (&sc)[NKT], float mc, uint32_t (&pp)[NP]) {
     constexpr bool DO_S = decltype(has_s)::value, DO_P = decltype(has_p)::value;
-    constexpr int SPM = 8 / NKK;  // P slices after each S MFMA (16 slices in all)
+    constexpr int SPM = 8 / NKK;  // P slices after each S MFMA (NKT * 8 slices in all)
     static_assert(SPM * NKK == 8, "head dimension");
-    const unsigned char* k0 = kS + lq * ROWB;
-    const unsigned char* k1 = k0 + 32 * ROWB;
+    const unsigned char* kr0 = kS + lq * ROWB;
     const floatx16 zero = {};
-    bf16x8 a0, a1;
+    bf16x8 a[NKT];
     if constexpr (DO_S) {
-      a0 = kfrag(k0, 0);
-      a1 = kfrag(k1, 0);
+#pragma unroll
+      for (int tl = 0; tl < NKT; ++tl) a[tl] = kfrag(kr0 + tl * 32 * ROWB, 0);
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      bf16x8 n0 = a0, n1 = a1;
+      bf16x8 nx[NKT];
+#pragma unroll
+      for (int tl = 0; tl < NKT; ++tl) nx[tl] = a[tl];
       if constexpr (DO_S) {
         if (kk + 1 < NKK) {
-          n0 = kfrag(k0, kk + 1);
-          n1 = kfrag(k1, kk + 1);
+#pragma unroll
+          for (int tl = 0; tl < NKT; ++tl) nx[tl] = kfrag(kr0 + tl * 32 * ROWB, kk + 1);
         }
-        sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], kk ? sn[0] : zero, 0, 0, 0);
       }
-      if constexpr (DO_P)
 #pragma unroll
-        for (int q = 0; q < SPM; ++q) p_slice(sc, mc, pp, 2 * kk * SPM + q);
-      if constexpr (DO_S)
-        sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], kk ? sn[1] : zero, 0, 0, 0);
-      if constexpr (DO_P)
+      for (int tl = 0; tl < NKT; ++tl) {
+        if constexpr (DO_S)
+          sn[tl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tl], qf[kk], kk ? sn[tl] : zero, 0, 0, 0);
+        if constexpr (DO_P)
 #pragma unroll
-        for (int q = 0; q < SPM; ++q) p_slice(sc, mc, pp, (2 * kk + 1) * SPM + q);
-      a0 = n0;
-      a1 = n1;
+          for (int q = 0; q < SPM; ++q) p_slice(sc, mc, pp, (NKT * kk + tl) * SPM + q);
+      }
+#pragma unroll
+      for (int tl = 0; tl < NKT; ++tl) a[tl] = nx[tl];
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // O^T += V^T P^T from V tile vt.  PV step m = kc*NDT + dt: the A fragment
   // holds keys kc*16 + lg*4 + {0..3} (first transposing read) and +8
   // (second) at d = dt*32 + lq; fragments are read two MFMAs ahead.
-  auto pv = [&](const uint32_t (&pp)[16], const unsigned char* vt) {
+  auto pv = [&](const uint32_t (&pp)[NP], const unsigned char* vt) {
     auto vfrag = [&](int m) {
       const int kc = m / NDT, dt = m % NDT;
       const int r0 = kc * 16 + vrow;
@@ -339,19 +341,19 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // with chunk c+2 and the V slot of chunk c-1 with chunk c+1.
   const int n = nchunks;
   auto step = [&](auto has_next, int c, const unsigned char* kS, const unsigned char* vP,
-                  unsigned char* kI, unsigned char* vI, floatx16 (&sc)[2], floatx16 (&sn)[2]) {
+                  unsigned char* kI, unsigned char* vI, floatx16 (&sc)[NKT], floatx16 (&sn)[NKT]) {
     tile_barrier();
     if (c + 2 < n) issue_k(c + 2, kI);
     if (c + 1 < n) issue_v(c + 1, vI);
     const float mc = prelude(c, sc);
-    uint32_t pp[16];
+    uint32_t pp[NP];
     s_and_p(has_next, std::true_type{}, kS, sn, sc, mc, pp);
     pv(pp, vP);
   };
 
   if (n > 0) {
-    floatx16 sA[2], sB[2];
-    uint32_t pp0[16];
+    floatx16 sA[NKT], sB[NKT];
+    uint32_t pp0[NP];
     issue_k(0, kb0);
     issue_v(0, vb0);
     if (n > 1) issue_k(1, kb1);
@@ -389,30 +391,43 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
         l_tot > 0.f ? (m_run * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D, int BLK>
+template <int D, int BLK, int KCH, int LMAX>
 static hipError_t launch_direct(const void* q, const void* k, const void* v, const PrefillDims& d,
                                 const int32_t* bidx, const int32_t* bcnt, float scale, void* out,
                                 float* lse, hipStream_t st) {
-  using Tr = DirectTraits<D, BLK>;
-  auto kern = prefill_attn_bf16_kernel<D, BLK>;
-  if (d.S / BLK > kMaxBlocks) return hipErrorInvalidValue;
-  const size_t lds = 0;
+  using Tr = DirectTraits<D, BLK, KCH>;
+  auto kern = prefill_attn_bf16_kernel<D, BLK, KCH, LMAX>;
+  if (d.S / BLK > LMAX) return hipErrorInvalidValue;
   const int units = d.B * d.Hkv * (d.S / BLK);
   const int grid = (units + kXcds - 1) / kXcds * kXcds * (d.Hq / d.Hkv);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(Tr::NT), lds, st, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Tr::NT), 0, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bidx, bcnt,
                      static_cast<uint16_t*>(out), lse, d.S, d.Hq, d.Hkv, scale * kLog2e, units);
   return hipGetLastError();
+}
+
+// Chunk size and list capacity per shape.  Blocks of 128 keys: 64-key chunks
+// (about 73 KB of LDS, two 4-wave workgroups per CU).  Blocks of 64 keys have
+// only two waves per workgroup, so their chunks are 32 keys: with a list of at
+// most 2048 blocks (S <= 128K) a workgroup takes under 40 KB and four fit on a
+// CU; longer prompts take the 4096-entry list and three.
+template <int D>
+static hipError_t launch_for_block(const void* q, const void* k, const void* v,
+                                   const PrefillDims& d, const int32_t* bidx, const int32_t* bcnt,
+                                   float scale, void* out, float* lse, hipStream_t st) {
+  if (d.T == 128) return launch_direct<D, 128, 64, kMaxBlocks>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (d.T == 64 && d.S / 64 <= 2048)
+    return launch_direct<D, 64, 32, 2048>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (d.T == 64) return launch_direct<D, 64, 32, kMaxBlocks>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
                                     const PrefillDims& d, const int32_t* bidx,
                                     const int32_t* bcnt, float scale, void* out, float* lse,
                                     hipStream_t st) {
-  if (d.D == 128 && d.T == 128) return launch_direct<128, 128>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
-  if (d.D == 128 && d.T == 64) return launch_direct<128, 64>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
-  if (d.D == 64 && d.T == 128) return launch_direct<64, 128>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
-  if (d.D == 64 && d.T == 64) return launch_direct<64, 64>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (d.D == 128) return launch_for_block<128>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
+  if (d.D == 64) return launch_for_block<64>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
   return hipErrorInvalidValue;
 }
 
