@@ -14,8 +14,8 @@ One step runs every row of the hot path once over resident synthetic inputs:
     (2048-token chunk + 1024 local tail), local (1024) and streaming
     (4 sinks + 1024 window) masks, caches flushed before each small mode.
 Outside the timed steps: own dense baselines, and the attention kernel at 3%
-and 12% density on the 128K prompt and on the 32K prompt with 64-token blocks
-at 10% (skip with --no-sweep).
+and 12% density and with the band + sink blocks only on the 128K prompt, and on
+the 32K prompt with 64-token blocks at 10% (skip with --no-sweep).
 Kernel times (medians) come from HIP events on the launch stream.  The headline value
 is the sparse prefill attention kernel's effective TFLOP/s on executed
 blocks (4*T*T*D FLOP per executed query-block/key-block pair); decode is
@@ -132,6 +132,14 @@ def prefill_sweep(fsa, workloads, pf):
         pc, d, sel = tune_selector(fsa, pf["q"], pf["c"], pf["r"], PREFILL, dens)
         res[f"128k_{int(round(dens * 100))}pct"] = time_attention(fsa, dict(pf, sel=sel, density=d), PREFILL)
         del sel
+    # both selector branches off: the 1024-token band + sink block only, a
+    # fixed-window mask whose cost grows linearly with the prompt
+    nB = PREFILL["S"] // PREFILL["T"]
+    sel = fsa.select_blocks(pf["q"], pf["c"], pf["r"], PREFILL["T"], -1.0, -1.0, PREFILL["band"],
+                            PREFILL["sink"])
+    d = sel["block_cnt"].sum().item() / (PREFILL["Hq"] * nB * (nB + 1) // 2)
+    res["128k_band_sink_only"] = time_attention(fsa, dict(pf, sel=sel, density=d), PREFILL)
+    del sel
     p32 = make_prefill(fsa, workloads, 0.10, seed=1001, P=PREFILL_32K)
     res["32k_block64_10pct"] = time_attention(fsa, p32, PREFILL_32K)
     del p32

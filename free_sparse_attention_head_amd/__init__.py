@@ -215,12 +215,14 @@ def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, id
     return out, lse
 
 
-def build_segments(mode, n, chunk_start=0, chunk_len=2048, local_len=1024, n_sink=4, page=16):
-    """Host-side segment builder: sorted merged [start, end) token ranges."""
+def build_segments(mode, n, chunk_start=0, chunk_len=2048, local_len=1024, n_sink=4, page=16,
+                   min_neighbourhood=0):
+    """Host-side segment builder: sorted merged [start, end) token ranges.
+    min_neighbourhood widens a focus chunk by that many tokens on each side."""
     lib = L.load()
     buf = (ctypes.c_int32 * 4)()
     cnt = ctypes.c_int(0)
-    L.check("fsa_build_segments", lib.fsa_build_segments(
+    L.check("fsa_build_segments_nb", lib.fsa_build_segments_nb(
         int(mode), int(n), int(chunk_start), int(chunk_len), int(local_len), int(n_sink),
-        int(page), buf, ctypes.byref(cnt)))
+        int(page), int(min_neighbourhood), buf, ctypes.byref(cnt)))
     return [(buf[2 * i], buf[2 * i + 1]) for i in range(cnt.value)]

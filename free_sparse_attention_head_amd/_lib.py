@@ -61,6 +61,8 @@ SIGNATURES = {
     "fsa_workspace_size": (c_size_t, [c_int, c_void_p, c_void_p]),
     "fsa_build_segments": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int32_p,
                                    ctypes.POINTER(c_int)]),
+    "fsa_build_segments_nb": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_int32_p, ctypes.POINTER(c_int)]),
     "fsa_status_string": (ctypes.c_char_p, [c_int]),
     "fsa_device_check": (c_int, []),
 }

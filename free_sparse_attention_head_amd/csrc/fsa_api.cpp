@@ -221,8 +221,15 @@ int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const vo
 
 int fsa_build_segments(int mode, int n, int chunk_start, int chunk_len, int local_len,
                        int n_sink, int page, int32_t* out, int* n_seg) {
+  return fsa_build_segments_nb(mode, n, chunk_start, chunk_len, local_len, n_sink, page, 0, out,
+                               n_seg);
+}
+
+int fsa_build_segments_nb(int mode, int n, int chunk_start, int chunk_len, int local_len,
+                          int n_sink, int page, int min_nb, int32_t* out, int* n_seg) {
   if (!out || !n_seg) return FSA_ERR_NULL;
-  if (n < 0 || page < 1 || local_len < 0 || chunk_len < 0 || n_sink < 0 || chunk_start < 0)
+  if (n < 0 || page < 1 || local_len < 0 || chunk_len < 0 || n_sink < 0 || chunk_start < 0 ||
+      min_nb < 0)
     return FSA_ERR_ARG;
   long long r[2][2];
   int c = 0;
@@ -245,7 +252,7 @@ int fsa_build_segments(int mode, int n, int chunk_start, int chunk_len, int loca
       add(down((long long)n - local_len), n);
       break;
     case FSA_SEG_FOCUS:
-      add(down(chunk_start), up((long long)chunk_start + chunk_len));
+      add(down((long long)chunk_start - min_nb), up((long long)chunk_start + chunk_len + min_nb));
       add(down((long long)n - local_len), n);
       break;
     case FSA_SEG_STREAMING:

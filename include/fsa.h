@@ -210,6 +210,16 @@ enum { FSA_SEG_GLOBAL = 0, FSA_SEG_FOCUS = 1, FSA_SEG_LOCAL = 2, FSA_SEG_STREAMI
 int fsa_build_segments(int mode, int n, int chunk_start, int chunk_len, int local_len,
                        int n_sink, int page, int32_t* out, int* n_seg);
 
+/* fsa_build_segments_nb -- fsa_build_segments with a minimum neighbourhood
+ * around the focused region, one of the safeguards the million-token-context
+ * post lists ("Not a free lunch").  In FOCUS mode the chunk is first widened
+ * to [chunk_start - min_nb, chunk_start + chunk_len + min_nb), then rounded
+ * outward and clipped as above; the other modes ignore min_nb.
+ * fsa_build_segments(...) is fsa_build_segments_nb(..., min_nb = 0, ...).
+ * Returns FSA_ERR_ARG for min_nb < 0 and as fsa_build_segments otherwise. */
+int fsa_build_segments_nb(int mode, int n, int chunk_start, int chunk_len, int local_len,
+                          int n_sink, int page, int min_nb, int32_t* out, int* n_seg);
+
 /* Static text for a status code. */
 const char* fsa_status_string(int status);
 

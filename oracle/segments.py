@@ -10,6 +10,8 @@ Sources:
     same three modes as KV-visibility sets.
   * LoZA post, "2. ZigZag architecture": streaming sparse attention over a
     fixed window (1024 tokens).
+  * Million-token-context post, "Not a free lunch": among the safeguards, a
+    minimum neighbourhood around the focused region.
 Readings taken: "own recent output" = the last local_len cached tokens; focus
 adds that local tail to the chunk; streaming keeps n_sink leading tokens plus
 the last local_len tokens exactly (token level, no rounding); ranges are
@@ -36,15 +38,19 @@ def _round_out(a, b, n, page):
     return lo, hi
 
 
-def build_segments(mode, n, chunk_start=0, chunk_len=2048, local_len=1024, n_sink=4, page=16):
+def build_segments(mode, n, chunk_start=0, chunk_len=2048, local_len=1024, n_sink=4, page=16,
+                   min_nb=0):
     """Sorted, merged [start, end) token ranges that `mode` admits for a
-    sequence of n cached tokens."""
+    sequence of n cached tokens.  min_nb: the focus chunk is first widened by
+    min_nb tokens on each side (million-token-context post, "Not a free
+    lunch": a minimum neighbourhood around the focused region as a
+    safeguard; the post gives no size)."""
     if mode == SEG_GLOBAL:
         return [(0, n)]
     if mode == SEG_LOCAL:
         return _merge([_round_out(n - local_len, n, n, page)])
     if mode == SEG_FOCUS:
-        return _merge([_round_out(chunk_start, chunk_start + chunk_len, n, page),
+        return _merge([_round_out(chunk_start - min_nb, chunk_start + chunk_len + min_nb, n, page),
                        _round_out(n - local_len, n, n, page)])
     if mode == SEG_STREAMING:
         return _merge([(0, min(n_sink, n)), (max(0, n - local_len), n)])

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     for required in ("block_stats", "select_blocks", "sparse_prefill_attn", "topk_indices",
                      "sparse_decode_attn", "fsa_workspace_size", "fsa_build_segments",
-                     "fsa_status_string", "fsa_device_check"):
+                     "fsa_build_segments_nb", "fsa_status_string", "fsa_device_check"):
         assert required in names
     for n in names:
         assert hasattr(lib, n), f"libfsa.so does not export {n}"
@@ -173,6 +173,19 @@ def test_build_segments_matches_oracle(mode, n, start):
     assert got == [tuple(int(x) for x in r) for r in want]
 
 
+@pytest.mark.parametrize("n,start,m", [(1 << 20, 100003, 0), (1 << 20, 100003, 1),
+                                       (1 << 20, 100003, 4096), (1 << 20, 5, 70),
+                                       (1 << 20, (1 << 20) - 2100, 100), (5000, 2000, 3000),
+                                       (5000, 0, 1 << 20)])
+def test_build_segments_neighbourhood_matches_oracle(n, start, m):
+    import free_sparse_attention_head_amd as fsa
+    for mode in (oracle.SEG_GLOBAL, oracle.SEG_FOCUS, oracle.SEG_LOCAL, oracle.SEG_STREAMING):
+        got = fsa.build_segments(mode, n, chunk_start=start, chunk_len=2048, local_len=1024,
+                                 n_sink=4, page=16, min_neighbourhood=m)
+        want = oracle.build_segments(mode, n, start, 2048, 1024, 4, 16, min_nb=m)
+        assert got == [tuple(int(x) for x in r) for r in want]
+
+
 def test_build_segments_errors():
     L, lib = _lib()
     buf = (ctypes.c_int32 * 4)()
@@ -180,3 +193,4 @@ def test_build_segments_errors():
     assert lib.fsa_build_segments(7, 100, 0, 10, 10, 0, 16, buf, ctypes.byref(cnt)) == L.FSA_ERR_ARG
     assert lib.fsa_build_segments(0, 100, 0, 10, 10, 0, 0, buf, ctypes.byref(cnt)) == L.FSA_ERR_ARG
     assert lib.fsa_build_segments(0, 100, 0, 10, 10, 0, 16, None, ctypes.byref(cnt)) == L.FSA_ERR_NULL
+    assert lib.fsa_build_segments_nb(1, 100, 0, 10, 10, 0, 16, -1, buf, ctypes.byref(cnt)) == L.FSA_ERR_ARG

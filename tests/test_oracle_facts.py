@@ -306,6 +306,36 @@ def test_F8_focus_ranges_page_aligned_and_tight(start):
         assert chunk[1] - (start + L) <= P - 1
 
 
+@pytest.mark.parametrize("start,m", [(5000, 0), (5000, 1), (5000, 100), (7, 300), (0, 64),
+                                     (100000 - 2048, 500), (20000, 200000)])
+def test_F8_focus_minimum_neighbourhood(start, m):
+    """The widened focus range covers [start - m, start + L + m) clipped to
+    [0, n), is page-aligned, adds under a page per side beyond it, and m = 0
+    gives the plain focus ranges."""
+    n, L, P = 100000, 2048, 16
+    rs = build_segments(oracle.SEG_FOCUS, n, chunk_start=start, chunk_len=L, local_len=1024,
+                        page=P, min_nb=m)
+    if m == 0:
+        assert rs == build_segments(oracle.SEG_FOCUS, n, start, L, 1024, page=P)
+    lo, hi = max(0, start - m), min(n, start + L + m)
+    covered = np.zeros(n, dtype=bool)
+    for a, b in rs:
+        assert a % P == 0 and (b % P == 0 or b == n)
+        covered[a:b] = True
+    assert covered[lo:hi].all() and covered[n - 1024:].all()
+    first = rs[0]
+    if first[0] <= lo < first[1]:
+        assert lo - first[0] <= P - 1
+    chunk = [r for r in rs if r[0] <= lo < r[1]][0]
+    if chunk[1] < n - 1024:
+        assert chunk[1] - hi <= P - 1
+    # ranges stay merged and sorted; the other modes ignore the option
+    assert all(rs[x][1] < rs[x + 1][0] for x in range(len(rs) - 1))
+    for mode in (oracle.SEG_GLOBAL, oracle.SEG_LOCAL, oracle.SEG_STREAMING):
+        assert build_segments(mode, n, start, L, 1024, page=P, min_nb=m) == \
+            build_segments(mode, n, start, L, 1024, page=P)
+
+
 def test_F8_golden_focus_segments():
     g = _gold("focus_segments.json")
     rs = build_segments(oracle.SEG_FOCUS, g["n"], g["chunk_start"], g["chunk_len"],
@@ -393,6 +423,32 @@ def test_masked_attention_equals_sdpa_with_explicit_mask():
     np.fill_diagonal(mask, True)
     o, _ = masked_attention(q, k, v, mask, T, 0.25)
     tok = np.kron(mask, np.ones((T, T), dtype=bool)) & np.tril(np.ones((S, S), dtype=bool))
+    t = lambda x: torch.from_numpy(x)[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=torch.from_numpy(tok)[None, None], scale=0.25)[0, 0].numpy()
+    assert np.abs(o - ref).max() <= 1e-12
+
+
+# ------------------------------------------------- forced-only (SSA) mask ---
+@pytest.mark.parametrize("band,sink", [(8, 1), (2, 0), (1, 3), (40, 1)])
+def test_forced_only_mask_is_window_plus_sink(band, sink):
+    """Both branches off (p < 0): the mask is exactly the forced blocks (LoZA
+    post, "2. ZigZag architecture": streaming sparse attention over a fixed
+    window, here a band of key blocks plus sink blocks), and attention over it
+    equals a token-level window-plus-sink mask run through the library routine."""
+    rng = _rng(band * 7 + sink)
+    S, D, T = 320, 16, 16
+    nB = S // T
+    q, k, v = (rng.standard_normal((S, D)) for _ in range(3))
+    qbar = oracle.pool_queries(q, T)
+    c, r = oracle.block_stats(k, T)
+    sel = oracle.select_blocks(qbar, c, r, -1.0, -1.0, band, sink)
+    i, j = np.meshgrid(np.arange(nB), np.arange(nB), indexing="ij")
+    want = (j <= i) & ((j < sink) | (j > i - band))
+    assert (sel["M"] == want).all() and not sel["C"].any() and not sel["R"].any()
+    o, _ = masked_attention(q, k, v, sel["M"], T, 0.25)
+    ti, tj = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+    tok = (tj <= ti) & ((tj // T < sink) | (tj // T > ti // T - band))
     t = lambda x: torch.from_numpy(x)[None, None]
     ref = torch.nn.functional.scaled_dot_product_attention(
         t(q), t(k), t(v), attn_mask=torch.from_numpy(tok)[None, None], scale=0.25)[0, 0].numpy()

@@ -59,6 +59,12 @@ def _segments_not_rounded(mode, n, chunk_start=0, chunk_len=2048, local_len=1024
     return oracle.build_segments(mode, n, chunk_start, chunk_len, local_len, n_sink, page=1)
 
 
+def _neighbourhood_one_sided(mode, n, chunk_start=0, chunk_len=2048, local_len=1024, n_sink=4,
+                             page=16, min_nb=0):
+    # widens the focus chunk after it, not before it
+    return oracle.build_segments(mode, n, chunk_start, chunk_len + min_nb, local_len, n_sink, page)
+
+
 def _pool_uses_first_row(q, T):
     q = np.asarray(q, dtype=np.float64)
     return q[::T].copy()
@@ -76,11 +82,13 @@ CASES = [
     ("gather_pages", _gather_ignores_table, [pins.test_F10_paged_gather_identity_vs_shuffled]),
     ("masked_attention", _masked_transposed, [pins.test_masked_attention_equals_sdpa_with_explicit_mask]),
     ("build_segments", _segments_not_rounded, [pins.test_F8_golden_focus_segments]),
+    ("build_segments", _neighbourhood_one_sided,
+     [lambda: pins.test_F8_focus_minimum_neighbourhood(5000, 100)]),
     ("pool_queries", _pool_uses_first_row, [pins.test_F5_pool_queries_block_means]),
 ]
 
 
-@pytest.mark.parametrize("name,mutant,catchers", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("name,mutant,catchers", CASES, ids=[c[1].__name__.strip("_") for c in CASES])
 def test_planted_mistake_is_caught(monkeypatch, name, mutant, catchers):
     monkeypatch.setattr(pins, name, mutant)
     caught = False
