@@ -15,7 +15,8 @@ One step runs every row of the hot path once over resident synthetic inputs:
     (4 sinks + 1024 window) masks, caches flushed before each small mode.
 Outside the timed steps: own dense baselines, and the attention kernel at 3%
 and 12% density and with the band + sink blocks only on the 128K prompt, and on
-the 32K prompt with 64-token blocks at 10% (skip with --no-sweep).
+the 32K prompt with 64-token blocks at 10%, and the Kascade group with one
+pooled index set per KV head shared by its query heads (skip with --no-sweep).
 Kernel times (medians) come from HIP events on the launch stream.  The headline value
 is the sparse prefill attention kernel's effective TFLOP/s on executed
 blocks (4*T*T*D FLOP per executed query-block/key-block pair); decode is
@@ -122,6 +123,33 @@ def time_attention(fsa, pf, P, reps=5):
     return {"density": round(pf["density"], 4), "attn_median_ms": round(med, 4),
             "attn_min_ms": round(xs[0], 4), "TFLOPs": round(flops / med / 1e9, 1),
             "frac_peak": round(flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
+def decode_kv_shared(fsa, dc, reps=5):
+    """The per-KV-head Kascade variant on the decode group's inputs, outside
+    the timed steps: pooled top-k per KV head, then the four layers attending
+    at the shared indices (each K/V row read once for the G query heads)."""
+    Dd = DECODE
+    L = dc["layers"]
+    idx = torch.empty((Dd["B"], Dd["Hkv"], Dd["k"]), dtype=torch.int32, device="cuda")
+    kth = torch.empty((Dd["B"], Dd["Hkv"]), dtype=torch.float32, device="cuda")
+    tm = Timer()
+    for _ in range(2 + reps):
+        tm.run("topk", lambda: fsa.topk_indices_kv(L[0]["q"], L[0]["k"], dc["page_table"],
+                                                   dc["seq_lens"], Dd["k"], idx=idx, kth=kth,
+                                                   ws=dc.get("topk_ws")))
+        for li in range(Dd["layers"]):
+            tm.run("dec", lambda li=li: fsa.sparse_decode_attn(
+                L[li]["q"], L[li]["k"], L[li]["v"], dc["page_table"], dc["seq_lens"],
+                mode=fsa.SEL_INDEX_KV, idx=idx, out=dc["out"][li], want_lse=False))
+    torch.cuda.synchronize()
+    topk_ms = tm.ms("topk", skip=2)[0]
+    dec_ms = tm.ms("dec", skip=2 * Dd["layers"])[0]
+    layer_bytes = Dd["B"] * Dd["Hkv"] * Dd["k"] * kv_row_bytes(Dd["D"])
+    return {"topk_kv_ms": round(topk_ms, 4), "decode_kv_ms": round(dec_ms, 4),
+            "decode_kv_GBps": round(layer_bytes / (dec_ms * 1e-3) / 1e9, 1),
+            "group_ms": round(topk_ms + Dd["layers"] * dec_ms, 4),
+            "bytes_per_layer": layer_bytes}
 
 
 def prefill_sweep(fsa, workloads, pf):
@@ -461,10 +489,12 @@ def main():
                                               (ddec * 1e-3) / 1e9, 1),
                  "decode_group_speedup": round(ddec / group_ms, 2)}
 
-    sweep = {}
+    sweep, kv_shared = {}, {}
     if not args.no_sweep:
         log("[bench] prefill density sweep and 32K prompt")
         sweep = prefill_sweep(fsa, workloads, pf)
+        log("[bench] per-KV-head Kascade variant")
+        kv_shared = decode_kv_shared(fsa, dc)
 
     if args.copy_probe:
         copy_probe()
@@ -518,6 +548,7 @@ def main():
         "segment_1M": seg,
         "dense": dense,
         "prefill_sweep": sweep,
+        "decode_kv_shared": kv_shared,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

@@ -21,11 +21,13 @@ import torch
 from . import _lib as L
 
 __all__ = ["block_stats", "select_blocks", "sparse_prefill_attn", "topk_indices",
-           "sparse_decode_attn", "build_segments", "workspace_size", "FsaError", "SEL_ALL",
-           "SEL_INDEX", "SEL_SEGMENT", "SEG_GLOBAL", "SEG_FOCUS", "SEG_LOCAL", "SEG_STREAMING"]
+           "topk_indices_kv", "sparse_decode_attn", "build_segments", "workspace_size", "FsaError",
+           "SEL_ALL", "SEL_INDEX", "SEL_SEGMENT", "SEL_INDEX_KV", "SEG_GLOBAL", "SEG_FOCUS",
+           "SEG_LOCAL", "SEG_STREAMING"]
 
 FsaError = L.FsaError
-SEL_ALL, SEL_INDEX, SEL_SEGMENT = L.FSA_SEL_ALL, L.FSA_SEL_INDEX, L.FSA_SEL_SEGMENT
+SEL_ALL, SEL_INDEX, SEL_SEGMENT, SEL_INDEX_KV = (L.FSA_SEL_ALL, L.FSA_SEL_INDEX, L.FSA_SEL_SEGMENT,
+                                             L.FSA_SEL_INDEX_KV)
 SEG_GLOBAL, SEG_FOCUS, SEG_LOCAL, SEG_STREAMING = (L.FSA_SEG_GLOBAL, L.FSA_SEG_FOCUS,
                                                    L.FSA_SEG_LOCAL, L.FSA_SEG_STREAMING)
 
@@ -161,39 +163,53 @@ def _decode_shape(q, k_pool, page_table, max_seq_len):
     return L.DecodeShape(B, Hq, Hkv, D, P, num_pages, max_pages, int(max_seq_len))
 
 
+def _topk(name, rows, q, k_pool, page_table, seq_lens, k, max_seq_len, idx, kth, ws):
+    lib = L.load()
+    shape = _decode_shape(q, k_pool, page_table, max_seq_len)
+    B = q.shape[0]
+    if idx is None:
+        idx = torch.empty((B, rows, k), dtype=torch.int32, device=q.device)
+    if kth is None:
+        kth = torch.empty((B, rows), dtype=torch.float32, device=q.device)
+    wsb = workspace_size("topk", shape, int(k))
+    ws, wsn = _ws(wsb, q.device, ws)
+    L.check(name, getattr(lib, name)(
+        _dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(page_table), _ptr(seq_lens),
+        ctypes.byref(shape), int(k), _ptr(idx), _ptr(kth), _ptr(ws), wsn, _stream(q.device)))
+    return idx, kth
+
+
 def topk_indices(q, k_pool, page_table, seq_lens, k, max_seq_len=None, idx=None, kth=None,
                  ws=None):
     """Exact per-head top-k token indices (ascending) and k-th score.
     q [B,Hq,D] bf16, k_pool [pages,Hkv,16,D] bf16, page_table [B,max_pages] int32,
-    seq_lens [B] int32."""
-    lib = L.load()
-    shape = _decode_shape(q, k_pool, page_table, max_seq_len)
-    B, Hq, _ = q.shape
-    if idx is None:
-        idx = torch.empty((B, Hq, k), dtype=torch.int32, device=q.device)
-    if kth is None:
-        kth = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    wsb = workspace_size("topk", shape, int(k))
-    ws, wsn = _ws(wsb, q.device, ws)
-    L.check("topk_indices", lib.topk_indices(
-        _dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(page_table), _ptr(seq_lens),
-        ctypes.byref(shape), int(k), _ptr(idx), _ptr(kth), _ptr(ws), wsn, _stream(q.device)))
-    return idx, kth
+    seq_lens [B] int32.  Returns idx [B,Hq,k], kth [B,Hq]."""
+    return _topk("topk_indices", q.shape[1], q, k_pool, page_table, seq_lens, k, max_seq_len,
+                 idx, kth, ws)
+
+
+def topk_indices_kv(q, k_pool, page_table, seq_lens, k, max_seq_len=None, idx=None, kth=None,
+                    ws=None):
+    """Exact top-k per KV head of the max over its query heads' scores.
+    Returns idx [B,Hkv,k] (ascending) and kth [B,Hkv]; feed idx to
+    sparse_decode_attn with mode=SEL_INDEX_KV."""
+    return _topk("topk_indices_kv", k_pool.shape[1], q, k_pool, page_table, seq_lens, k,
+                 max_seq_len, idx, kth, ws)
 
 
 def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, idx=None,
                        segments=None, n_seg=None, scale=None, n_split=0, max_seq_len=None,
                        want_lse=True, out=None, lse=None, ws=None):
     """Split-KV paged decode attention.  mode SEL_ALL / SEL_INDEX (idx [B,Hq,k]) /
-    SEL_SEGMENT (segments [B,max_seg,2], n_seg [B]).  Returns (out bf16 [B,Hq,D],
-    lse fp32 [B,Hq] or None)."""
+    SEL_INDEX_KV (idx [B,Hkv,k]) / SEL_SEGMENT (segments [B,max_seg,2], n_seg [B]).
+    Returns (out bf16 [B,Hq,D], lse fp32 [B,Hq] or None)."""
     lib = L.load()
     shape = _decode_shape(q, k_pool, page_table, max_seq_len)
     B, Hq, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     sel = L.KvSelect(int(mode), None, 0, None, None, 0, int(n_split))
-    if mode == SEL_INDEX:
+    if mode in (SEL_INDEX, SEL_INDEX_KV):
         sel.idx = _ptr(idx).value
         sel.k = idx.shape[2]
     elif mode == SEL_SEGMENT:

@@ -2,7 +2,8 @@
 // plus the log-sum-exp combine.
 //
 // Kascade post, "What Kascade got right": reuse layers attend only at the
-// anchor layer's per-head top-k indices (index mode).  Declarative Attention
+// anchor layer's per-head top-k indices (index mode; the per-KV-head variant
+// shares one index set, and every K/V read, among a KV head's query heads).  Declarative Attention
 // post, "Declarative attention protocol": global / focus / local modes become
 // block-aligned token ranges that an unmodified attention kernel reads
 // (segment mode).  LoZA post, "4. From food delivery to AI":
@@ -57,6 +58,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int hh = item % per_b, b = item / per_b;
   const int g = (MODE == FSA_SEL_INDEX) ? hh / G : hh;
   const int h0 = (MODE == FSA_SEL_INDEX) ? hh : hh * G;  // first query head of the item
+  constexpr bool LISTED = MODE == FSA_SEL_INDEX || MODE == FSA_SEL_INDEX_KV;
   const int n = min(max(sl[b], 0), max_seq_len);
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     }
     __syncthreads();
     total = seg_pre[s_nseg];
-  } else if constexpr (MODE == FSA_SEL_INDEX) {
+  } else if constexpr (LISTED) {
     total = k;
   } else {
     total = n;
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     for (int e = 0; e < 8; ++e) o[x][e] = 0.f;
   }
   const int32_t* ptb = pt + (size_t)b * max_pages;
-  const int32_t* idxr = (MODE == FSA_SEL_INDEX) ? idx + ((size_t)b * Hq + hh) * k : nullptr;
+  // index list of the item: per query head, or per KV head shared by its G heads
+  const int32_t* idxr = LISTED ? idx + ((size_t)b * per_b + hh) * k : nullptr;
 
   for (int base = p0; base < p1; base += NSLOT * RB) {
     uint4 kr[RB], vr[RB];
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       const int pos = base + slot * RB + r;
       int tok = -1;
       if (pos < p1) {
-        if constexpr (MODE == FSA_SEL_INDEX) {
+        if constexpr (LISTED) {
           tok = idxr[pos];
           if (tok >= n) tok = -1;
         } else if constexpr (MODE == FSA_SEL_SEGMENT) {
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
 int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split) {
   if (n_split > 0) return n_split;
   const int items = mode == FSA_SEL_INDEX ? d.B * d.Hq : d.B * d.Hkv;
-  const int len = mode == FSA_SEL_INDEX ? k : d.max_seq_len;
+  const int len = (mode == FSA_SEL_INDEX || mode == FSA_SEL_INDEX_KV) ? k : d.max_seq_len;
   // aim for >= 2048 workgroups and >= 256 positions per split
   int ns = (2048 + items - 1) / items;
   const int cap = (len + 255) / 256;
@@ -291,6 +294,8 @@ static hipError_t launch_dec_d(const void* q, const void* kp, const void* vp, co
   if (G == GG) {                              \
     if (mode == FSA_SEL_SEGMENT)              \
       FSA_DEC(GG, FSA_SEL_SEGMENT);           \
+    else if (mode == FSA_SEL_INDEX_KV)        \
+      FSA_DEC(GG, FSA_SEL_INDEX_KV);          \
     else                                      \
       FSA_DEC(GG, FSA_SEL_ALL);               \
   } else

@@ -77,6 +77,7 @@ int check_kv_select(const fsa_kv_select* sel, const DecodeDims& d) {
     case FSA_SEL_ALL:
       return FSA_OK;
     case FSA_SEL_INDEX:
+    case FSA_SEL_INDEX_KV:
       if (sel->idx == nullptr) return FSA_ERR_NULL;
       if (sel->k < 1) return FSA_ERR_ARG;
       return FSA_OK;
@@ -127,9 +128,10 @@ size_t fsa_workspace_size(int op, const void* shape, const void* params) {
     // sizing depends on mode, k and n_split only; pointers are not needed yet
     const fsa_kv_select* sel = static_cast<const fsa_kv_select*>(params);
     if (sel == nullptr || sel->n_split < 0 || sel->n_split > kMaxSplit) return 0;
-    if (sel->mode != FSA_SEL_ALL && sel->mode != FSA_SEL_INDEX && sel->mode != FSA_SEL_SEGMENT)
+    if (sel->mode != FSA_SEL_ALL && sel->mode != FSA_SEL_INDEX && sel->mode != FSA_SEL_SEGMENT &&
+        sel->mode != FSA_SEL_INDEX_KV)
       return 0;
-    if (sel->mode == FSA_SEL_INDEX && sel->k < 1) return 0;
+    if ((sel->mode == FSA_SEL_INDEX || sel->mode == FSA_SEL_INDEX_KV) && sel->k < 1) return 0;
     return fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split);
   }
   return 0;
@@ -184,9 +186,10 @@ int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* 
                                                 scale, out, lse, st));
 }
 
-int topk_indices(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
-                 const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
-                 float* kth, void* ws, size_t ws_bytes, hipStream_t st) {
+static int topk_common(fsa_dtype dt, const void* q, const void* k_pool,
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       const fsa_decode_shape* s, int k, bool pooled, int32_t* idx, float* kth,
+                       void* ws, size_t ws_bytes, hipStream_t st) {
   DecodeDims d;
   int rc = check_decode_shape(s, &d);
   if (rc) return rc;
@@ -196,7 +199,20 @@ int topk_indices(fsa_dtype dt, const void* q, const void* k_pool, const int32_t*
   if (!ws) return FSA_ERR_NULL;
   if (ws_bytes < fsa::topk_ws_bytes(d, k)) return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;
-  return launch_status(fsa::launch_topk(q, k_pool, page_table, seq_lens, d, k, idx, kth, ws, st));
+  return launch_status(
+      fsa::launch_topk(q, k_pool, page_table, seq_lens, d, k, pooled, idx, kth, ws, st));
+}
+
+int topk_indices(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
+                 const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
+                 float* kth, void* ws, size_t ws_bytes, hipStream_t st) {
+  return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, false, idx, kth, ws, ws_bytes, st);
+}
+
+int topk_indices_kv(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
+                    const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
+                    float* kth, void* ws, size_t ws_bytes, hipStream_t st) {
+  return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, true, idx, kth, ws, ws_bytes, st);
 }
 
 int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const void* v_pool,

@@ -42,8 +42,9 @@ hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
 
 // topk.hip
 size_t topk_ws_bytes(const DecodeDims& d, int k);
+// pooled: one index set per KV head from the max over its query heads' scores
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
-                       const DecodeDims& d, int k, int32_t* idx, float* kth, void* ws,
+                       const DecodeDims& d, int k, bool pooled, int32_t* idx, float* kth, void* ws,
                        hipStream_t st);
 
 // decode_attn.hip

@@ -42,7 +42,10 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 
 static inline int seq_stride(int max_seq_len) { return (max_seq_len + 15) & ~15; }
 
-template <int D, int G>
+// POOL: one score row per KV head, the maximum of its G query heads' raw
+// scores (a key counts if any head of the group rates it), instead of one
+// row per query head.
+template <int D, int G, bool POOL>
 __global__ __launch_bounds__(256) void topk_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ sl, int Hq, int Hkv,
@@ -52,7 +55,8 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   constexpr int RB = 8;                  // rows per lane group per step
   constexpr int STEP = NSLOT * RB;       // tokens per step
   constexpr int TPAGES = kTopkTile / 16;
-  __shared__ uint32_t lh[G][kBins1];
+  constexpr int GR = POOL ? 1 : G;  // score rows per KV head
+  __shared__ uint32_t lh[GR][kBins1];
   __shared__ int pg[TPAGES];
   const int tile = blockIdx.x % tiles;
   const int bg = blockIdx.x / tiles;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   const int t1 = min(n, t0 + kTopkTile);
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int slot = wave * RG + l / LPR, dl = l % LPR;
-  for (int x = tid; x < G * kBins1; x += 256) (&lh[0][0])[x] = 0u;
+  for (int x = tid; x < GR * kBins1; x += 256) (&lh[0][0])[x] = 0u;
   // the tile's page ids, read once and coalesced: row loads then depend on an
   // LDS read instead of a second global load (bad ids become -1: skipped)
   const int32_t* ptb = pt + (size_t)b * max_pages;
@@ -98,23 +102,33 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   // dl of group s first picks token s*RB + dl % RB for heads dl / RB + k*HS,
   // which is exactly what lane ((t / RB)*LPR + hs*RB + t % RB) must hand to the
   // lane of token t and head slot hs.
-  constexpr int W = RG * RB, HS = 64 / W, NV = (G + HS - 1) / HS;
+  constexpr int W = RG * RB, HS = 64 / W, NV = (GR + HS - 1) / HS;
   static_assert(LPR == HS * RB, "row group covers the head slots");
   const int tw = l % W, hs = l / W;
   const int src = (tw / RB) * LPR + hs * RB + tw % RB;
   const int pick_r = dl % RB, pick_h = dl / RB;
+  // score row of head slot x: query head g*G + x, or the KV head's pooled row
+  const size_t row0 = POOL ? (size_t)b * Hkv + g : (size_t)b * Hq + (size_t)g * G;
   auto score_rows = [&](int base, const uint4 (&kr)[RB]) {
-    float sc[G][RB];
+    float sc[GR][RB];
 #pragma unroll
-    for (int x = 0; x < G; ++x)
+    for (int r = 0; r < RB; ++r) {
+      if constexpr (POOL) {
+        float m = group_sum<LPR>(dot8_bf16(qv[0], kr[r], 0.f));
 #pragma unroll
-      for (int r = 0; r < RB; ++r) sc[x][r] = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
+        for (int x = 1; x < G; ++x) m = fmaxf(m, group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f)));
+        sc[0][r] = m;
+      } else {
+#pragma unroll
+        for (int x = 0; x < G; ++x) sc[x][r] = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
+      }
+    }
     const int tok = base + wave * W + tw;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       float v = 0.f;
 #pragma unroll
-      for (int x = k * HS; x < G && x < (k + 1) * HS; ++x) {
+      for (int x = k * HS; x < GR && x < (k + 1) * HS; ++x) {
         float vx = sc[x][0];
 #pragma unroll
         for (int r = 1; r < RB; ++r) vx = pick_r == r ? sc[x][r] : vx;
@@ -122,8 +136,8 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
       }
       v = __shfl(v, src, 64) + 0.0f;  // + 0 folds -0 onto +0
       const int x = hs + k * HS;
-      if (x < G && tok < t1) {
-        scores[((size_t)b * Hq + g * G + x) * stride + tok] = v;
+      if (x < GR && tok < t1) {
+        scores[(row0 + x) * stride + tok] = v;
         atomicAdd(&lh[x][order_key(v) >> 21], 1u);
       }
     }
@@ -140,9 +154,9 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   }
   if (base < t1) score_rows(base, ka);
   __syncthreads();
-  for (int x = tid; x < G * kBins1; x += 256) {
+  for (int x = tid; x < GR * kBins1; x += 256) {
     const uint32_t c = (&lh[0][0])[x];
-    if (c) atomicAdd(&hist[((size_t)b * Hq + g * G + x / kBins1) * kBins1 + x % kBins1], c);
+    if (c) atomicAdd(&hist[(row0 + x / kBins1) * kBins1 + x % kBins1], c);
   }
 }
 
@@ -268,12 +282,14 @@ __device__ void select_from_candidates(const float* __restrict__ sr, int n, int 
   if (kth != nullptr && t == 0) *kth = key_to_float(ks);
 }
 
+// One workgroup per score row; rows_per_b rows (query heads, or KV heads when
+// pooled) per sequence.
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist,
-    const int32_t* __restrict__ sl, int Hq, int max_seq_len, int stride, int k,
+    const int32_t* __restrict__ sl, int rows_per_b, int max_seq_len, int stride, int k,
     int32_t* __restrict__ idx, float* __restrict__ kth) {
   __shared__ TopkShared sh;
-  const int row = blockIdx.x, b = row / Hq;
+  const int row = blockIdx.x, b = row / rows_per_b;
   const int n = min(max(sl[b], 0), max_seq_len);
   const int t = threadIdx.x;
   int32_t* out = idx + (size_t)row * k;
@@ -383,13 +399,14 @@ size_t topk_ws_bytes(const DecodeDims& d, int k) {
 }
 
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
-                       const DecodeDims& d, int k, int32_t* idx, float* kth, void* ws,
+                       const DecodeDims& d, int k, bool pooled, int32_t* idx, float* kth, void* ws,
                        hipStream_t st) {
   const int stride = seq_stride(d.max_seq_len);
+  const int rows_per_b = pooled ? d.Hkv : d.Hq;  // score rows (and index sets) per sequence
   float* scores = static_cast<float*>(ws);
   const size_t sc = (size_t)d.B * d.Hq * stride * sizeof(float);
   uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + ((sc + 255) / 256) * 256);
-  const size_t nh = (size_t)d.B * d.Hq * kBins1;
+  const size_t nh = (size_t)d.B * rows_per_b * kBins1;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + 255) / 256 < 4096 ? (nh + 255) / 256 : 4096)),
                      dim3(256), 0, st, hist, nh, 0u);
   hipError_t e = hipGetLastError();
@@ -399,19 +416,25 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
   const uint16_t* Q = static_cast<const uint16_t*>(q);
   const uint16_t* Kp = static_cast<const uint16_t*>(kpool);
   const dim3 grid(d.B * d.Hkv * tiles);
-#define FSA_TS(DD, GG)                                                                      \
-  if (d.D == DD && G == GG) {                                                               \
-    hipLaunchKernelGGL((topk_score_kernel<DD, GG>), grid, dim3(256), 0, st, Q, Kp, pt, sl, d.Hq, \
-                       d.Hkv, d.max_pages, d.num_pages, d.max_seq_len, stride, tiles, scores, \
-                       hist);                                                               \
+#define FSA_TS(DD, GG, PP)                                                                   \
+  hipLaunchKernelGGL((topk_score_kernel<DD, GG, PP>), grid, dim3(256), 0, st, Q, Kp, pt, sl,  \
+                     d.Hq, d.Hkv, d.max_pages, d.num_pages, d.max_seq_len, stride, tiles,      \
+                     scores, hist)
+#define FSA_TS_G(DD, GG)                  \
+  if (d.D == DD && G == GG) {             \
+    if (pooled)                           \
+      FSA_TS(DD, GG, true);               \
+    else                                  \
+      FSA_TS(DD, GG, false);              \
   } else
-  FSA_TS(128, 1) FSA_TS(128, 2) FSA_TS(128, 4) FSA_TS(128, 8) FSA_TS(64, 1) FSA_TS(64, 2)
-  FSA_TS(64, 4) FSA_TS(64, 8) { return hipErrorInvalidValue; }
+  FSA_TS_G(128, 1) FSA_TS_G(128, 2) FSA_TS_G(128, 4) FSA_TS_G(128, 8) FSA_TS_G(64, 1)
+  FSA_TS_G(64, 2) FSA_TS_G(64, 4) FSA_TS_G(64, 8) { return hipErrorInvalidValue; }
+#undef FSA_TS_G
 #undef FSA_TS
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * d.Hq), dim3(kSelThreads), 0, st, scores, hist,
-                     sl, d.Hq, d.max_seq_len, stride, k, idx, kth);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * rows_per_b), dim3(kSelThreads), 0, st, scores,
+                     hist, sl, rows_per_b, d.max_seq_len, stride, k, idx, kth);
   return hipGetLastError();
 }
 

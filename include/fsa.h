@@ -77,12 +77,16 @@ typedef struct {
   int32_t max_seq_len; /* upper bound of seq_lens[b], <= 16*max_pages   */
 } fsa_decode_shape;
 
-enum { FSA_SEL_ALL = 0, FSA_SEL_INDEX = 1, FSA_SEL_SEGMENT = 2 };
+enum { FSA_SEL_ALL = 0, FSA_SEL_INDEX = 1, FSA_SEL_SEGMENT = 2, FSA_SEL_INDEX_KV = 3 };
 
 /* Which cached tokens a decode query reads (host struct).
  *   FSA_SEL_ALL:     tokens [0, seq_lens[b]).
  *   FSA_SEL_INDEX:   idx (device) int32 [B, Hq, k], per query head; entries
  *                    outside [0, seq_lens[b]) are skipped.
+ *   FSA_SEL_INDEX_KV: idx (device) int32 [B, Hkv, k], one list per KV head
+ *                    shared by its G query heads (each K/V row is read once
+ *                    for the group); entries outside [0, seq_lens[b]) are
+ *                    skipped.
  *   FSA_SEL_SEGMENT: segments (device) int32 [B, max_seg, 2] token ranges
  *                    [start, end), n_seg (device) int32 [B]; ranges of one
  *                    sequence must be sorted and disjoint, and are clipped
@@ -166,6 +170,20 @@ int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* 
 int topk_indices(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
                  const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
                  float* kth, void* ws, size_t ws_bytes, hipStream_t st);
+
+/* topk_indices_kv -- exact top-k per KV head over a pooled score, the
+ * GQA-shared counterpart of topk_indices.  Kascade post, "Head-aware is the
+ * key to accuracy", favours one set per query head; one set per KV head lets
+ * the G query heads share every index and K/V read (FSA_SEL_INDEX_KV), at the
+ * accuracy cost that post describes.  The pooled score of a token is the
+ * maximum over the KV head's G query heads of the raw q . k (fp32); the k
+ * largest are kept, ties to the lower token index, written ascending; if
+ * seq_lens[b] < k the missing entries are -1 and kth is -inf.
+ *   q, k_pool, page_table, seq_lens, ws: as topk_indices
+ *   idx (device) int32 [B, Hkv, k]; kth (device, nullable) fp32 [B, Hkv] */
+int topk_indices_kv(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
+                    const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
+                    float* kth, void* ws, size_t ws_bytes, hipStream_t st);
 
 /* sparse_decode_attn -- split-KV decode attention over a paged cache.
  * Kascade post, "What Kascade got right" (reuse layers attend only at the

@@ -28,7 +28,7 @@ status per function:
   dense_attention, masked_attention, masked_attention_rows,
   index_attention, segment_attention, lse_combine  -- pinned
   block_stats, pool_queries, select_blocks           -- pinned
-  topk                                                -- pinned
+  topk, topk_pooled                                   -- pinned
   gather_pages, build_segments                        -- pinned
 """
 
@@ -36,13 +36,13 @@ from .attention import (dense_attention, masked_attention, masked_attention_rows
                         index_attention, segment_attention, lse_combine,
                         attention_partial)
 from .blocks import block_stats, pool_queries, select_blocks, visible_count, k_of
-from .topk import topk, near_kth_mask
+from .topk import topk, topk_pooled, near_kth_mask
 from .paged import gather_pages
 from .segments import build_segments, SEG_GLOBAL, SEG_FOCUS, SEG_LOCAL, SEG_STREAMING
 
 __all__ = [
     "dense_attention", "masked_attention", "masked_attention_rows", "index_attention",
     "segment_attention", "lse_combine", "attention_partial", "block_stats", "pool_queries",
-    "select_blocks", "visible_count", "k_of", "topk", "near_kth_mask", "gather_pages",
+    "select_blocks", "visible_count", "k_of", "topk", "topk_pooled", "near_kth_mask", "gather_pages",
     "build_segments", "SEG_GLOBAL", "SEG_FOCUS", "SEG_LOCAL", "SEG_STREAMING",
 ]

@@ -6,6 +6,12 @@ accuracy": this is done per attention head.  Reading taken: the score is the
 raw dot product q.k over every cached key, ties go to the lower key index, and
 the index set is returned sorted ascending (so that any consumer reads keys in
 cache order).
+
+topk_pooled is the GQA-shared counterpart: one index set per KV head, the
+head-aware choice above traded for G query heads sharing every index (the
+post argues for per-head sets; the shared one cuts reads by G).  Reading
+taken: a key's pooled score is the maximum of its G query heads' raw scores
+(kept if any head of the group rates it).
 """
 
 import numpy as np
@@ -31,3 +37,10 @@ def near_kth_mask(scores, kth, band):
     correct top-k sets computed at different precisions."""
     s = np.asarray(scores, dtype=np.float64)
     return np.abs(s - kth) <= band
+
+
+def topk_pooled(scores, k):
+    """Exact top-k of the per-key maximum over the rows of `scores` [G, N]
+    (the G query heads of one KV head).  Returns (idx, kth) as topk."""
+    s = np.asarray(scores, dtype=np.float64)
+    return topk(s.max(axis=0), k)

@@ -142,6 +142,18 @@ def test_topk_and_decode_argument_validation():
         dt, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(sl), 0.1, FAKE, None,
         FAKE, wsb, None)
     assert dcall(sel) == L.FSA_ERR_NULL                      # index mode without idx
+    sel = L.KvSelect(L.FSA_SEL_INDEX_KV, None, 16, None, None, 0, 0)
+    assert dcall(sel) == L.FSA_ERR_NULL                      # per-KV-head mode without idx
+    sel = L.KvSelect(L.FSA_SEL_INDEX_KV, FAKE.value, 0, None, None, 0, 0)
+    assert dcall(sel) == L.FSA_ERR_ARG                       # k = 0
+    sel = L.KvSelect(L.FSA_SEL_INDEX_KV, FAKE.value, 16, None, None, 0, 2)
+    assert lib.fsa_workspace_size(L.FSA_OP_DECODE_ATTN, ctypes.byref(s),
+                                  ctypes.byref(sel)) == 2 * 8 * 2 * (128 + 2) * 4
+    kcall = lambda dt, kk, wsb: lib.topk_indices_kv(dt, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s),
+                                                    kk, FAKE, None, FAKE, wsb, None)
+    assert kcall(L.FSA_F32, 16, ws) == L.FSA_ERR_DTYPE
+    assert kcall(L.FSA_BF16, 0, ws) == L.FSA_ERR_ARG
+    assert kcall(L.FSA_BF16, 16, ws - 1) == L.FSA_ERR_WORKSPACE
     sel = L.KvSelect(L.FSA_SEL_SEGMENT, None, 0, FAKE.value, FAKE.value, 0, 0)
     assert dcall(sel) == L.FSA_ERR_ARG                       # max_seg 0
     sel = L.KvSelect(9, None, 0, None, None, 0, 0)

@@ -1,5 +1,6 @@
-"""GPU parity of the decode path (topk_indices, sparse_decode_attn in index,
-segment and all modes) against the fp64 oracle, through the C ABI.
+"""GPU parity of the decode path (topk_indices, topk_indices_kv, sparse_decode_attn
+in index, per-KV-head index, segment and all modes) against the fp64 oracle,
+through the C ABI.
 
 The paged pools are shuffled, sequences are ragged (one shorter than k, one
 not a multiple of the page size), split counts vary (1, odd, automatic) and a
@@ -165,6 +166,66 @@ def test_index_decode_parity(name, n_split):
         for h in range(Hq):
             K, V = seq_kv(d, 1, b, h // G)
             o, l = oracle.index_attention(q1[b, h], K, V, idx[b, h], scale)
+            assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
+            assert abs(lse[b, h].item() - l) <= 1e-2
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_topk_kv_parity(name):
+    """One index set per KV head from the max over its query heads' scores."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L0 = gpu["layers"][0]
+    idx, kth = fsa.topk_indices_kv(L0["q"], L0["k"], gpu["page_table"], gpu["seq_lens"], k,
+                                   max_seq_len=N)
+    assert idx.shape == (B, Hkv, k) and kth.shape == (B, Hkv)
+    idx, kth = idx.cpu().numpy(), kth.cpu().numpy()
+    q = workloads.to_f64(d["layers"][0]["q"])
+    G = Hq // Hkv
+    n_diff = n_exc = 0
+    for b in range(B):
+        n = sl[b]
+        for g in range(Hkv):
+            row = idx[b, g]
+            if n < k:
+                assert (row[:n] == np.arange(n)).all() and (row[n:] == -1).all()
+                assert np.isneginf(kth[b, g])
+                continue
+            assert (np.diff(row) > 0).all() and row.min() >= 0 and row.max() < n
+            K, _ = seq_kv(d, 0, b, g)
+            scores = K @ q[b, g * G:(g + 1) * G].T        # [n, G]
+            ref_idx, ref_kth = oracle.topk_pooled(scores.T, k)
+            dd, ee = topk_diff_excused(row, ref_idx, scores.max(axis=1), ref_kth)
+            n_diff += dd
+            n_exc += ee
+            assert abs(kth[b, g] - ref_kth) <= 1e-3
+    print(f"[{name}] pooled top-k entries differing {n_diff}, excused near k-th value {n_exc}")
+    assert n_diff == n_exc
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("n_split", [1, 3, 0])
+def test_index_kv_decode_parity(name, n_split):
+    """Reuse layer with one shared index set per KV head: every query head of
+    the group attends at its KV head's indices."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L0, L1 = gpu["layers"]
+    idx, _ = fsa.topk_indices_kv(L0["q"], L0["k"], gpu["page_table"], gpu["seq_lens"], k,
+                                 max_seq_len=N)
+    out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"], gpu["seq_lens"],
+                                      mode=fsa.SEL_INDEX_KV, idx=idx, n_split=n_split,
+                                      max_seq_len=N)
+    out, lse, idx = out.cpu(), lse.cpu(), idx.cpu().numpy()
+    q1 = workloads.to_f64(d["layers"][1]["q"])
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(D)
+    for b in range(B):
+        for h in range(Hq):
+            K, V = seq_kv(d, 1, b, h // G)
+            o, l = oracle.index_attention(q1[b, h], K, V, idx[b, h // G], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
             assert abs(lse[b, h].item() - l) <= 1e-2
 

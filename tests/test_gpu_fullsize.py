@@ -7,7 +7,8 @@ times, checked on sampled outputs that the fp64 oracle computes one by one.
   * 128K sparse prefill: B=1, S=131072, 32 / 4 heads, block 128, diagonal
     band of 8 blocks + sink block, densities 3 / 6 / 12%.
   * 128K Kascade decode group: B=32, N=131072, 32 / 8 heads, k=2048, 4 layers
-    (anchor top-k, indices reused by layers 1-3), shuffled 16-token pages.
+    (anchor top-k, indices reused by layers 1-3), shuffled 16-token pages; and
+    its per-KV-head variant (pooled top-k, shared indices).
   * 1M segment decode: B=4, N=2^20, global / focus / local / streaming masks.
 
 Sampled rows: block statistics and selector rows against the oracle
@@ -146,6 +147,44 @@ def test_kascade_decode_128k_group():
                                                   row, 1 / math.sqrt(D))
                 assert np.abs(outs[li][b, h].double().cpu().numpy() - o_ref).max() <= TOL_BF16
     print(f"[fullsize kascade] top-k entries differing {n_diff}, excused {n_exc}", flush=True)
+    assert n_diff == n_exc
+
+
+def test_kascade_kv_shared_decode_128k_group():
+    """The per-KV-head variant at the benchmark size: one pooled top-k per KV
+    head, four layers attending at it with the group's query heads sharing
+    every read."""
+    fsa = _fsa()
+    B, N, Hq, Hkv, D, k, L = 32, 131072, 32, 8, 128, 2048, 4
+    print(f"[fullsize kascade-kv] B={B} N={N} k={k} layers={L}", flush=True)
+    d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=L, seed=1003, device="cuda")
+    pt, sl = d["page_table"], d["seq_lens"]
+    idx, kth = fsa.topk_indices_kv(d["layers"][0]["q"], d["layers"][0]["k"], pt, sl, k)
+    outs = [fsa.sparse_decode_attn(d["layers"][li]["q"], d["layers"][li]["k"], d["layers"][li]["v"],
+                                   pt, sl, mode=fsa.SEL_INDEX_KV, idx=idx)[0] for li in range(L)]
+    torch.cuda.synchronize()
+    idx_h, kth_h = idx.cpu().numpy(), kth.cpu().numpy()
+    rng = np.random.default_rng(5)
+    G = Hq // Hkv
+    n_diff = n_exc = 0
+    for b in rng.choice(B, size=3, replace=False):
+        for g in rng.choice(Hkv, size=2, replace=False):
+            K0 = _seq_kv_gpu(d["layers"][0]["k"], pt[b], N, g)
+            s = K0 @ workloads.to_f64(d["layers"][0]["q"][b, g * G:(g + 1) * G]).T
+            ref_idx, ref_kth = oracle.topk_pooled(s.T, k)
+            row = idx_h[b, g]
+            assert (np.diff(row) > 0).all()
+            dd, ee = topk_diff_excused(row, ref_idx, s.max(axis=1), ref_kth)
+            n_diff, n_exc = n_diff + dd, n_exc + ee
+            assert abs(kth_h[b, g] - ref_kth) <= BAND
+            for li in range(L):
+                Kl = K0 if li == 0 else _seq_kv_gpu(d["layers"][li]["k"], pt[b], N, g)
+                Vl = _seq_kv_gpu(d["layers"][li]["v"], pt[b], N, g)
+                for h in (g * G, g * G + G - 1):
+                    o_ref, _ = oracle.index_attention(workloads.to_f64(d["layers"][li]["q"][b, h]),
+                                                      Kl, Vl, row, 1 / math.sqrt(D))
+                    assert np.abs(outs[li][b, h].double().cpu().numpy() - o_ref).max() <= TOL_BF16
+    print(f"[fullsize kascade-kv] pooled top-k entries differing {n_diff}, excused {n_exc}", flush=True)
     assert n_diff == n_exc
 
 

@@ -19,7 +19,7 @@ import torch
 import oracle
 from oracle import (block_stats, build_segments, dense_attention, gather_pages,
                     index_attention, lse_combine, masked_attention, pool_queries,
-                    segment_attention, select_blocks, topk)
+                    segment_attention, select_blocks, topk, topk_pooled)
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -453,3 +453,30 @@ def test_forced_only_mask_is_window_plus_sink(band, sink):
     ref = torch.nn.functional.scaled_dot_product_attention(
         t(q), t(k), t(v), attn_mask=torch.from_numpy(tok)[None, None], scale=0.25)[0, 0].numpy()
     assert np.abs(o - ref).max() <= 1e-12
+
+
+# --------------------------------------------------- pooled (per-KV-head) top-k
+def test_topk_pooled_closed_forms_and_brute_force():
+    """G = 1 is plain top-k; a key that is the single best for one head only is
+    kept; the result equals brute-force rank counting on the per-key max; ties
+    go to the lower index; k = N keeps every key."""
+    rng = _rng(31)
+    G, N = 4, 300
+    s = rng.standard_normal((G, N))
+    for k in (1, 7, 64, N):
+        idx, kth = topk_pooled(s[:1], k)
+        ref_idx, ref_kth = oracle.topk(s[0], k)
+        assert (idx == ref_idx).all() and kth == ref_kth
+    star = s.copy()
+    star[2, 123] = 50.0  # only head 2 rates key 123
+    idx, kth = topk_pooled(star, 1)
+    assert list(idx) == [123] and kth == 50.0
+    m = s.max(axis=0)
+    for k in (5, 40, 299):
+        idx, kth = topk_pooled(s, k)
+        rank = np.array([(m > m[j]).sum() + (m[:j] == m[j]).sum() for j in range(N)])
+        assert list(idx) == list(np.flatnonzero(rank < k)) and kth == np.sort(m)[::-1][k - 1]
+    tie = np.zeros((G, 10))
+    tie[1, [3, 7]] = 1.0
+    assert list(topk_pooled(tie, 3)[0]) == [0, 3, 7]
+    assert list(topk_pooled(s, N)[0]) == list(range(N))

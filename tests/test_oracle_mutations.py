@@ -65,6 +65,10 @@ def _neighbourhood_one_sided(mode, n, chunk_start=0, chunk_len=2048, local_len=1
     return oracle.build_segments(mode, n, chunk_start, chunk_len + min_nb, local_len, n_sink, page)
 
 
+def _pooled_by_mean(scores, k):
+    return oracle.topk(np.asarray(scores, dtype=np.float64).mean(axis=0), k)
+
+
 def _pool_uses_first_row(q, T):
     q = np.asarray(q, dtype=np.float64)
     return q[::T].copy()
@@ -85,6 +89,7 @@ CASES = [
     ("build_segments", _neighbourhood_one_sided,
      [lambda: pins.test_F8_focus_minimum_neighbourhood(5000, 100)]),
     ("pool_queries", _pool_uses_first_row, [pins.test_F5_pool_queries_block_means]),
+    ("topk_pooled", _pooled_by_mean, [pins.test_topk_pooled_closed_forms_and_brute_force]),
 ]
 
 
