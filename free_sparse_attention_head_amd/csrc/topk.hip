@@ -10,10 +10,11 @@
 //      safe under graph capture).
 //   2. topk_score_kernel: streams K once from HBM through the page table; the
 //      G query heads of a KV head share every 256-byte key row (16 lanes x
-//      16 bytes, v_dot2_f32_bf16 + DPP butterfly).  Writes the fp32 score row
-//      of every query head and accumulates, in LDS, a histogram of the top 11
-//      bits of the order-preserving score key, flushed with one global atomic
-//      per non-empty bin.
+//      16 bytes, v_dot2_f32_bf16 + DPP butterfly).  Each workgroup keeps its
+//      tile's fp32 scores and a histogram of the top 11 bits of the
+//      order-preserving score key in LDS, then writes the scores as whole
+//      lines and flushes the histogram with one global atomic per non-empty
+//      bin.
 //   3. topk_select_kernel: one 1024-thread workgroup per (sequence, head).
 //      Digit 1 comes from the fused histogram.  When few keys lie in or above
 //      the k-th key's bin, one pass copies them to LDS and the rest runs
@@ -30,9 +31,12 @@
 
 namespace fsa {
 
-constexpr int kTopkTile = 4096;   // tokens per score workgroup
 constexpr int kBins1 = 2048;      // digit 1: key bits 31..21
 constexpr int kSelThreads = 1024;
+constexpr int kTileScores = 8192;  // scores of a score workgroup's tile, staged in LDS (32 KB)
+
+// tokens per score workgroup: the tile's scores of all its rows fit in LDS
+constexpr int topk_tile(int rows) { return kTileScores / rows; }
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
@@ -45,6 +49,11 @@ static inline int seq_stride(int max_seq_len) { return (max_seq_len + 15) & ~15;
 // POOL: one score row per KV head, the maximum of its G query heads' raw
 // scores (a key counts if any head of the group rates it), instead of one
 // row per query head.
+//
+// A workgroup scores one tile of TT tokens of one (sequence, KV head).  Its
+// scores and digit-1 histograms stay in LDS until the tile is done and are
+// then written out in one pass: a wave never issues a global store between
+// its K row loads, so a load never waits behind a store's acknowledgement.
 template <int D, int G, bool POOL>
 __global__ __launch_bounds__(256) void topk_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
@@ -54,20 +63,27 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   constexpr int LPR = D / 8, RG = 64 / LPR, NSLOT = 4 * RG;
   constexpr int RB = 8;                  // rows per lane group per step
   constexpr int STEP = NSLOT * RB;       // tokens per step
-  constexpr int TPAGES = kTopkTile / 16;
-  constexpr int GR = POOL ? 1 : G;  // score rows per KV head
-  __shared__ uint32_t lh[GR][kBins1];
+  constexpr int GR = POOL ? 1 : G;       // score rows per KV head
+  constexpr int TT = topk_tile(GR);      // tokens per tile
+  static_assert(TT % STEP == 0, "tile of whole steps");
+  // page ids of the tile plus the two steps that the last loads run past it
+  constexpr int TPAGES = (TT + 2 * STEP) / 16;
+  // digit-1 counts of bins 2w and 2w+1 share word w (a tile holds < 65536
+  // keys); the last word takes the adds of lanes with nothing to count
+  constexpr int HW = GR * kBins1 / 2, TRASH = HW;
+  __shared__ uint32_t lh[HW + 1];
+  __shared__ __align__(16) float ssc[GR * TT + 4];  // + a spare quad for idle lanes
   __shared__ int pg[TPAGES];
   const int tile = blockIdx.x % tiles;
   const int bg = blockIdx.x / tiles;
   const int g = bg % Hkv, b = bg / Hkv;
   const int n = min(max(sl[b], 0), max_seq_len);
-  const int t0 = tile * kTopkTile;
+  const int t0 = tile * TT;
   if (t0 >= n) return;
-  const int t1 = min(n, t0 + kTopkTile);
+  const int t1 = min(n, t0 + TT);
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int slot = wave * RG + l / LPR, dl = l % LPR;
-  for (int x = tid; x < GR * kBins1; x += 256) (&lh[0][0])[x] = 0u;
+  for (int x = tid; x <= TRASH; x += 256) lh[x] = 0u;
   // the tile's page ids, read once and coalesced: row loads then depend on an
   // LDS read instead of a second global load (bad ids become -1: skipped)
   const int32_t* ptb = pt + (size_t)b * max_pages;
@@ -82,33 +98,27 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
     qv[x] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * G + x) * D + dl * 8);
   __syncthreads();
 
-  // a lane group's RB rows are consecutive tokens inside one 16-token page
+  // A lane group's RB rows are consecutive tokens inside one 16-token page.
+  // Every wave issues all of its row loads on every step, with no branch
+  // around them (rows of a missing page, or past the tile, are read from page
+  // 0; their scores are replaced by 0 or never kept): the compiler then knows
+  // how many loads are younger than each row buffer and waits for that
+  // buffer alone.
+  auto page_of = [&](int base) { return pg[(base + slot * RB - t0) >> 4]; };
   auto load_rows = [&](int base, uint4 (&kr)[RB]) {
     const int tok0 = base + slot * RB;
-    const int page = tok0 < t1 ? pg[(tok0 - t0) >> 4] : -1;
-    const size_t row0 = ((size_t)(page < 0 ? 0 : page) * Hkv + g) * 16 + (tok0 & 15);
+    const int page = max(page_of(base), 0);
+    const size_t row0 = ((size_t)page * Hkv + g) * 16 + (tok0 & 15);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      if (page >= 0 && tok0 + r < t1)
-        kr[r] = *reinterpret_cast<const uint4*>(kpool + (row0 + r) * D + dl * 8);
-      else
-        kr[r] = make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < RB; ++r)
+      kr[r] = *reinterpret_cast<const uint4*>(kpool + (row0 + r) * D + dl * 8);
   };
-  // Scores leave in a coalesced layout: a wave's RG*RB rows of a step are W
-  // consecutive tokens, so lane l takes token l % W for the head slot l / W
-  // and the heads l / W + k*HS, writing whole lines per head.  After the group
-  // sums every lane of a row group holds all G*RB sums of its RB tokens; lane
-  // dl of group s first picks token s*RB + dl % RB for heads dl / RB + k*HS,
-  // which is exactly what lane ((t / RB)*LPR + hs*RB + t % RB) must hand to the
-  // lane of token t and head slot hs.
-  constexpr int W = RG * RB, HS = 64 / W, NV = (GR + HS - 1) / HS;
-  static_assert(LPR == HS * RB, "row group covers the head slots");
-  const int tw = l % W, hs = l / W;
-  const int src = (tw / RB) * LPR + hs * RB + tw % RB;
-  const int pick_r = dl % RB, pick_h = dl / RB;
-  // score row of head slot x: query head g*G + x, or the KV head's pooled row
-  const size_t row0 = POOL ? (size_t)b * Hkv + g : (size_t)b * Hq + (size_t)g * G;
+  // After the group sums every lane of a row group holds all GR*RB scores of
+  // its RB consecutive tokens, as GR*NQ quads of four consecutive tokens of
+  // one score row.  Quad c = j*LPR + dl is kept by lane dl of the group with
+  // its j-th 16-byte LDS store: row c / NQ, tokens 4*(c % NQ) .. +3.
+  constexpr int NQ = RB / 4, NJ = (GR * NQ + LPR - 1) / LPR;
+  static_assert(RB % 4 == 0, "quads of tokens");
   auto score_rows = [&](int base, const uint4 (&kr)[RB]) {
     float sc[GR][RB];
 #pragma unroll
@@ -123,22 +133,28 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
         for (int x = 0; x < G; ++x) sc[x][r] = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
       }
     }
-    const int tok = base + wave * W + tw;
+    const bool page_ok = page_of(base) >= 0;  // a missing page scores 0
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      float v = 0.f;
+    for (int j = 0; j < NJ; ++j) {
+      const int c = j * LPR + dl;
+      const int sx = c / NQ, sq = c % NQ;        // the quad's score row and place
+      const int tq = base + slot * RB + 4 * sq;  // its first token
+      floatx4 v;
 #pragma unroll
-      for (int x = k * HS; x < GR && x < (k + 1) * HS; ++x) {
-        float vx = sc[x][0];
+      for (int e = 0; e < 4; ++e) {
+        float w = 0.f;
 #pragma unroll
-        for (int r = 1; r < RB; ++r) vx = pick_r == r ? sc[x][r] : vx;
-        v = pick_h == x - k * HS ? vx : v;
+        for (int cc = j * LPR; cc < GR * NQ && cc < (j + 1) * LPR; ++cc)
+          w = c == cc ? sc[cc / NQ][4 * (cc % NQ) + e] : w;
+        v[e] = page_ok ? w + 0.0f : 0.f;  // + 0 folds -0 onto +0
       }
-      v = __shfl(v, src, 64) + 0.0f;  // + 0 folds -0 onto +0
-      const int x = hs + k * HS;
-      if (x < GR && tok < t1) {
-        scores[(row0 + x) * stride + tok] = v;
-        atomicAdd(&lh[x][order_key(v) >> 21], 1u);
+      const bool ok = (c < GR * NQ) & (tq < t1);
+      *reinterpret_cast<floatx4*>(&ssc[ok ? sx * TT + (tq - t0) : GR * TT]) = v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t bin = (uint32_t)sx * kBins1 + (order_key(v[e]) >> 21);
+        const bool oke = ok & (tq + e < t1);
+        atomicAdd(&lh[oke ? bin >> 1 : TRASH], (bin & 1) ? 0x10000u : 1u);
       }
     }
   };
@@ -147,16 +163,35 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   load_rows(t0, ka);
   int base = t0;
   for (; base + STEP < t1; base += 2 * STEP) {
+    // scheduling barriers keep each step's scoring after the loads of the
+    // next step and before the loads after it, so no score instruction waits
+    // for rows that were only just requested
     load_rows(base + STEP, kb);
+    __builtin_amdgcn_sched_barrier(0);
     score_rows(base, ka);
-    if (base + 2 * STEP < t1) load_rows(base + 2 * STEP, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    load_rows(base + 2 * STEP, ka);  // past the tile: rows of page 0, never kept
+    __builtin_amdgcn_sched_barrier(0);
     score_rows(base + STEP, kb);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (base < t1) score_rows(base, ka);
   __syncthreads();
-  for (int x = tid; x < GR * kBins1; x += 256) {
-    const uint32_t c = (&lh[0][0])[x];
-    if (c) atomicAdd(&hist[(row0 + x / kBins1) * kBins1 + x % kBins1], c);
+  // the tile's scores, whole lines per score row (a quad that straddles the
+  // sequence end also writes the row's padding, which nothing reads)
+  const size_t row0 = POOL ? (size_t)b * Hkv + g : (size_t)b * Hq + (size_t)g * G;
+  const int nq = (t1 - t0 + 3) >> 2;
+  for (int x = tid; x < GR * (TT / 4); x += 256) {
+    const int r = x / (TT / 4), qd = x % (TT / 4);
+    if (qd < nq)
+      *reinterpret_cast<floatx4*>(scores + (row0 + r) * stride + t0 + 4 * qd) =
+          *reinterpret_cast<const floatx4*>(&ssc[r * TT + 4 * qd]);
+  }
+  for (int x = tid; x < HW; x += 256) {
+    const uint32_t c = lh[x];
+    uint32_t* hr = hist + row0 * kBins1 + 2 * x;  // bins 2x, 2x+1 (rows are adjacent)
+    if (c & 0xffffu) atomicAdd(hr, c & 0xffffu);
+    if (c >> 16) atomicAdd(hr + 1, c >> 16);
   }
 }
 
@@ -411,8 +446,9 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
                      dim3(256), 0, st, hist, nh, 0u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int tiles = (d.max_seq_len + kTopkTile - 1) / kTopkTile;
   const int G = d.Hq / d.Hkv;
+  const int tt = topk_tile(pooled ? 1 : G);
+  const int tiles = (d.max_seq_len + tt - 1) / tt;
   const uint16_t* Q = static_cast<const uint16_t*>(q);
   const uint16_t* Kp = static_cast<const uint16_t*>(kpool);
   const dim3 grid(d.B * d.Hkv * tiles);
