@@ -196,6 +196,7 @@ static int topk_common(fsa_dtype dt, const void* q, const void* k_pool,
   if (dt != FSA_BF16) return FSA_ERR_DTYPE;
   if (!q || !k_pool || !page_table || !seq_lens || !idx) return FSA_ERR_NULL;
   if (k < 1 || k > d.max_seq_len) return FSA_ERR_ARG;
+  if (d.max_seq_len > fsa::kTopkMaxSeqLen) return FSA_ERR_SHAPE;
   if (!ws) return FSA_ERR_NULL;
   if (ws_bytes < fsa::topk_ws_bytes(d, k)) return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;

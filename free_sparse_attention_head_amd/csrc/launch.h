@@ -41,6 +41,7 @@ hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
                                     hipStream_t st);
 
 // topk.hip
+constexpr int kTopkMaxSeqLen = 1 << 23;  // tokens per sequence that top-k supports
 size_t topk_ws_bytes(const DecodeDims& d, int k);
 // pooled: one index set per KV head from the max over its query heads' scores
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,

@@ -10,20 +10,29 @@
 //      safe under graph capture).
 //   2. topk_score_kernel: streams K once from HBM through the page table; the
 //      G query heads of a KV head share every 256-byte key row (16 lanes x
-//      16 bytes, v_dot2_f32_bf16 + DPP butterfly).  Each workgroup keeps its
-//      tile's fp32 scores and a histogram of the top 11 bits of the
-//      order-preserving score key in LDS, then writes the scores as whole
-//      lines and flushes the histogram with one global atomic per non-empty
-//      bin.
-//   3. topk_select_kernel: one 1024-thread workgroup per (sequence, head).
-//      Digit 1 comes from the fused histogram.  When few keys lie in or above
-//      the k-th key's bin, one pass copies them to LDS and the rest runs
-//      there; otherwise digits 2 (11 bits) and 3 (10 bits) are histogrammed
-//      over the candidates sharing the prefix by re-reading the row.
-//      This yields the exact k-th key K* and how many keys equal to K* are
-//      taken.  A final pass in index order keeps key > K*, plus the first keys
-//      equal to K*, compacting positions with workgroup scans so that the
-//      output is ascending.
+//      16 bytes, v_dot2_f32_bf16 + DPP butterfly).  A workgroup scores one
+//      tile of a row and keeps the tile's fp32 scores, and a histogram of the
+//      top 11 bits of their order-preserving keys, in LDS.  At the end it
+//      reads the row's histogram as it stands and takes as bound the bin of
+//      the k-th largest key counted there (0 while fewer than k are counted).
+//      Counts only grow, so any reading counts a subset of the row: its k-th
+//      largest key is never above the row's, and the bound never exceeds the
+//      bin b1 of the row's k-th largest key.  The tile then keeps only its
+//      candidates, keys in bins >= bound, written (order key, index) in index
+//      order as one list per tile, and adds its counts of bins >= bound to
+//      the row's histogram, which is therefore exact from b1 up, the only
+//      part the select reads.  Tiles run in order along the row, so later
+//      tiles see tighter bounds and write few candidates.
+//   3. topk_select_kernel: one 1024-thread workgroup per score row, reading
+//      the row's candidate lists as one stream in index order.  Digit 1 comes
+//      from the row histogram.  When few keys lie in or above the k-th key's
+//      bin, one pass copies them to LDS and the rest runs there; otherwise
+//      digits 2 (11 bits) and 3 (10 bits) are histogrammed over the
+//      candidates sharing the prefix by re-reading the stream.  This yields
+//      the exact k-th key K* and how many keys equal to K* are taken.  A
+//      final pass in index order keeps key > K*, plus the first keys equal to
+//      K*, compacting positions with workgroup scans so that the output is
+//      ascending.
 #include <math.h>
 
 #include "common.h"
@@ -34,6 +43,7 @@ namespace fsa {
 constexpr int kBins1 = 2048;      // digit 1: key bits 31..21
 constexpr int kSelThreads = 1024;
 constexpr int kTileScores = 8192;  // scores of a score workgroup's tile, staged in LDS (32 KB)
+constexpr int kMaxSelTiles = kTopkMaxSeqLen / (kTileScores / 8);  // tiles of a row, at most
 
 // tokens per score workgroup: the tile's scores of all its rows fit in LDS
 constexpr int topk_tile(int rows) { return kTileScores / rows; }
@@ -44,22 +54,21 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
     p[x] = v;
 }
 
-static inline int seq_stride(int max_seq_len) { return (max_seq_len + 15) & ~15; }
-
 // POOL: one score row per KV head, the maximum of its G query heads' raw
 // scores (a key counts if any head of the group rates it), instead of one
 // row per query head.
 //
 // A workgroup scores one tile of TT tokens of one (sequence, KV head).  Its
-// scores and digit-1 histograms stay in LDS until the tile is done and are
-// then written out in one pass: a wave never issues a global store between
-// its K row loads, so a load never waits behind a store's acknowledgement.
+// scores and digit-1 histograms stay in LDS until the tile is done: a wave
+// issues no global store between its K row loads, so a load never waits
+// behind a store's acknowledgement.
 template <int D, int G, bool POOL>
 __global__ __launch_bounds__(256) void topk_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
-    const int32_t* __restrict__ pt, const int32_t* __restrict__ sl, int Hq, int Hkv,
-    int max_pages, int num_pages, int max_seq_len, int stride, int tiles,
-    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ sl, int B, int Hq, int Hkv,
+    int max_pages, int num_pages, int max_seq_len, int k, int tiles, int cstride,
+    uint32_t* __restrict__ ckey, uint16_t* __restrict__ cidx, uint32_t* __restrict__ ccnt,
+    uint32_t* __restrict__ hist) {
   constexpr int LPR = D / 8, RG = 64 / LPR, NSLOT = 4 * RG;
   constexpr int RB = 8;                  // rows per lane group per step
   constexpr int STEP = NSLOT * RB;       // tokens per step
@@ -74,8 +83,12 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   __shared__ uint32_t lh[HW + 1];
   __shared__ __align__(16) float ssc[GR * TT + 4];  // + a spare quad for idle lanes
   __shared__ int pg[TPAGES];
-  const int tile = blockIdx.x % tiles;
-  const int bg = blockIdx.x / tiles;
+  __shared__ int scan_tmp[17];
+  // tile-major order: the first tiles of every row are scored first, so the
+  // rows' histograms already hold several tiles when later tiles bound
+  // their candidates
+  const int tile = blockIdx.x / (B * Hkv);
+  const int bg = blockIdx.x % (B * Hkv);
   const int g = bg % Hkv, b = bg / Hkv;
   const int n = min(max(sl[b], 0), max_seq_len);
   const int t0 = tile * TT;
@@ -177,21 +190,83 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   }
   if (base < t1) score_rows(base, ka);
   __syncthreads();
-  // the tile's scores, whole lines per score row (a quad that straddles the
-  // sequence end also writes the row's padding, which nothing reads)
   const size_t row0 = POOL ? (size_t)b * Hkv + g : (size_t)b * Hq + (size_t)g * G;
-  const int nq = (t1 - t0 + 3) >> 2;
-  for (int x = tid; x < GR * (TT / 4); x += 256) {
-    const int r = x / (TT / 4), qd = x % (TT / 4);
-    if (qd < nq)
-      *reinterpret_cast<floatx4*>(scores + (row0 + r) * stride + t0 + 4 * qd) =
-          *reinterpret_cast<const floatx4*>(&ssc[r * TT + 4 * qd]);
+  constexpr int BPT = kBins1 / 256;  // histogram bins per thread
+  constexpr int PER = TT / 256;      // tile tokens per thread
+  __shared__ uint32_t sbound[GR];
+  const int nt = t1 - t0;
+  // Candidate bounds: per row, the bin of the k-th largest key counted in
+  // the row's histogram as it stands (0 while fewer than k keys are
+  // counted).  Thread t reads bins [top, top + BPT), the threads in
+  // descending bin order; all rows' reads are issued together.
+  const int top = kBins1 - BPT * (tid + 1);
+  uint32_t hc[GR][BPT];
+#pragma unroll
+  for (int x = 0; x < GR; ++x)
+#pragma unroll
+    for (int e = 0; e < BPT; ++e)
+      hc[x][e] = __hip_atomic_load(hist + (row0 + x) * kBins1 + top + e, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < GR) sbound[tid] = 0u;
+#pragma unroll
+  for (int x = 0; x < GR; ++x) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) c += (int)hc[x][e];
+    int tot;
+    const int above = block_excl_scan(c, scan_tmp, &tot);  // keys in higher bins
+    if (above < k && k <= above + c) {
+      int acc = above;
+#pragma unroll
+      for (int e = BPT - 1; e >= 0; --e) {
+        acc += (int)hc[x][e];
+        if (acc >= k) {
+          sbound[x] = (uint32_t)(top + e);
+          break;
+        }
+      }
+    }
   }
-  for (int x = tid; x < HW; x += 256) {
-    const uint32_t c = lh[x];
-    uint32_t* hr = hist + row0 * kBins1 + 2 * x;  // bins 2x, 2x+1 (rows are adjacent)
-    if (c & 0xffffu) atomicAdd(hr, c & 0xffffu);
-    if (c >> 16) atomicAdd(hr + 1, c >> 16);
+  __syncthreads();
+  // The tile's counts into the rows' histograms, from each row's bound up:
+  // the select reads exact counts only from the k-th key's bin up, and that
+  // bin is at or above every tile's bound.
+  for (int y = tid; y < HW; y += 256) {
+    const int x = y / (kBins1 / 2), bin = 2 * (y % (kBins1 / 2));
+    const uint32_t cc = lh[y], bound = sbound[x];
+    uint32_t* hr = hist + (row0 + x) * kBins1 + bin;
+    if ((cc & 0xffffu) && (uint32_t)bin >= bound) atomicAdd(hr, cc & 0xffffu);
+    if ((cc >> 16) && (uint32_t)(bin + 1) >= bound) atomicAdd(hr + 1, cc >> 16);
+  }
+  // Each row's candidates of this tile, compacted in index order: thread t
+  // takes tokens [t*PER, t*PER + PER), a workgroup scan places them.
+  const int j0 = tid * PER;
+#pragma unroll 1
+  for (int x = 0; x < GR; ++x) {
+    const uint32_t bound = sbound[x];
+    uint32_t key[PER];
+    int nc = 0;
+#pragma unroll
+    for (int e = 0; e < PER; e += 4) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(&ssc[x * TT + j0 + e]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        key[e + u] = order_key(v[u]);
+        nc += (j0 + e + u < nt && (key[e + u] >> 21) >= bound) ? 1 : 0;
+      }
+    }
+    int ntot;
+    int pos = block_excl_scan(nc, scan_tmp, &ntot);
+    const size_t cbase = (row0 + x) * (size_t)cstride + t0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (j0 + e < nt && (key[e] >> 21) >= bound) {
+        ckey[cbase + pos] = key[e];
+        cidx[cbase + pos] = (uint16_t)(j0 + e);
+        ++pos;
+      }
+    }
+    if (tid == 0) ccnt[(row0 + x) * tiles + tile] = (uint32_t)ntot;
   }
 }
 
@@ -226,34 +301,61 @@ __device__ void find_digit(TopkShared& sh, int nbins, int kk, int& digit, int& a
   __syncthreads();
 }
 
+// A row's candidates as one stream in index order: the lists of its tiles
+// one after another.  seg[i] = candidates in tiles before i (seg[nt] = all).
+struct CandStream {
+  const uint32_t* key;  // the row's candidate keys, tile i's list at i * tt
+  const uint16_t* idx;  // their indices inside the tile
+  const int* seg;       // LDS
+  int nt, tt, m;
+  // element p < m: the tile holding it is the last i with seg[i] <= p;
+  // hint = a tile at or before it
+  __device__ void at(int p, int& hint, uint32_t& k, int& tok) const {
+    int lo = hint, hi = nt - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    hint = lo;
+    const int o = lo * tt + (p - seg[lo]);
+    k = key[o];
+    tok = lo * tt + (int)idx[o];
+  }
+  // this thread's four consecutive elements from p0 (invalid past the end)
+  __device__ void quad(int p0, uint32_t (&k)[4], int (&tok)[4], bool (&valid)[4]) const {
+    int hint = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      valid[e] = p0 + e < m;
+      k[e] = 0u;
+      tok[e] = -1;
+      if (valid[e]) at(p0 + e, hint, k[e], tok[e]);
+    }
+  }
+};
+
 // Fast path, used when the keys in or above the k-th key's top-11-bit bin
-// number at most kCandCap: one pass over the score row copies them (key,
-// index) into LDS in index order; digits 2-3 and the ordered output then run
-// on LDS only.  `need` = how many keys of bin b1 still have to be taken.
+// number at most kCandCap: one pass over the candidate stream copies them
+// (key, index) into LDS in index order; digits 2-3 and the ordered output
+// then run on LDS only.  `need` = how many keys of bin b1 still have to be
+// taken.
 constexpr int kCandCap = 6144;
-__device__ void select_from_candidates(const float* __restrict__ sr, int n, int k, uint32_t b1,
-                                       int need, TopkShared& sh, int32_t* __restrict__ out,
+__device__ void select_from_candidates(const CandStream& cs, int k, uint32_t b1, int need,
+                                       TopkShared& sh, int32_t* __restrict__ out,
                                        float* __restrict__ kth) {
   __shared__ uint32_t ck[kCandCap];
   __shared__ int ci[kCandCap];
   const int t = threadIdx.x;
   int ncand = 0;
-  for (int base = 0; base < n; base += 4 * kSelThreads) {
-    const int j0 = base + 4 * t;
+  for (int base = 0; base < cs.m; base += 4 * kSelThreads) {
     uint32_t key[4];
+    int tok[4];
     bool f[4];
-    if (j0 + 3 < n) {
-      const float4 v = *reinterpret_cast<const float4*>(sr + j0);
-      key[0] = order_key(v.x); key[1] = order_key(v.y);
-      key[2] = order_key(v.z); key[3] = order_key(v.w);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) key[e] = j0 + e < n ? order_key(sr[j0 + e]) : 0u;
-    }
+    cs.quad(base + 4 * t, key, tok, f);
     int c = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      f[e] = j0 + e < n && (key[e] >> 21) >= b1;
+      f[e] = f[e] && (key[e] >> 21) >= b1;
       c += f[e] ? 1 : 0;
     }
     int tot;
@@ -262,7 +364,7 @@ __device__ void select_from_candidates(const float* __restrict__ sr, int n, int 
     for (int e = 0; e < 4; ++e)
       if (f[e]) {
         ck[pos] = key[e];
-        ci[pos] = j0 + e;
+        ci[pos] = tok[e];
         ++pos;
       }
     ncand += tot;
@@ -320,21 +422,46 @@ __device__ void select_from_candidates(const float* __restrict__ sr, int n, int 
 // One workgroup per score row; rows_per_b rows (query heads, or KV heads when
 // pooled) per sequence.
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ hist,
-    const int32_t* __restrict__ sl, int rows_per_b, int max_seq_len, int stride, int k,
-    int32_t* __restrict__ idx, float* __restrict__ kth) {
+    const uint32_t* __restrict__ ckey, const uint16_t* __restrict__ cidx,
+    const uint32_t* __restrict__ ccnt, const uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ sl, int rows_per_b, int max_seq_len, int tt, int tiles,
+    int cstride, int k, int32_t* __restrict__ idx, float* __restrict__ kth) {
   __shared__ TopkShared sh;
+  __shared__ int seg[kMaxSelTiles + 1];
   const int row = blockIdx.x, b = row / rows_per_b;
   const int n = min(max(sl[b], 0), max_seq_len);
   const int t = threadIdx.x;
   int32_t* out = idx + (size_t)row * k;
-  const float* sr = scores + (size_t)row * stride;
   if (n < k) {
     for (int x = t; x < k; x += kSelThreads) out[x] = x < n ? x : -1;
     if (kth != nullptr && t == 0) kth[row] = -INFINITY;
     return;
   }
-  // digit 1 from the fused histogram
+  // the candidate stream: exclusive prefix of the tiles' list lengths
+  const int nt = (n + tt - 1) / tt;
+  {
+    constexpr int TPT = kMaxSelTiles / kSelThreads;  // tiles per thread, consecutive
+    int c[TPT], sum = 0;
+#pragma unroll
+    for (int e = 0; e < TPT; ++e) {
+      const int i = t * TPT + e;
+      c[e] = i < nt ? (int)ccnt[(size_t)row * tiles + i] : 0;
+      sum += c[e];
+    }
+    int tot;
+    int run = block_excl_scan(sum, sh.scan, &tot);
+#pragma unroll
+    for (int e = 0; e < TPT; ++e) {
+      const int i = t * TPT + e;
+      if (i <= nt) seg[i] = run;
+      run += c[e];
+    }
+    if (t == 0) seg[nt] = tot;
+  }
+  __syncthreads();
+  const CandStream cs{ckey + (size_t)row * cstride, cidx + (size_t)row * cstride, seg, nt, tt,
+                      seg[nt]};
+  // digit 1 from the row histogram (exact from the k-th key's bin up)
   for (int x = t; x < kBins1; x += kSelThreads) sh.hist[x] = hist[(size_t)row * kBins1 + x];
   __syncthreads();
   int kk = k, d, above;
@@ -343,33 +470,26 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int cand = above + (int)sh.hist[d];
   __syncthreads();
   if (cand <= kCandCap) {
-    select_from_candidates(sr, n, k, (uint32_t)d, kk, sh, out, kth ? kth + row : nullptr);
+    select_from_candidates(cs, k, (uint32_t)d, kk, sh, out, kth ? kth + row : nullptr);
     return;
   }
-  // general path: refine digits 2 and 3 by re-reading the score row
+  // general path: refine digits 2 and 3 by re-reading the candidate stream
   uint32_t prefix = (uint32_t)d << 21, pmask = 0xffe00000u;
-  // digits 2 and 3 over the candidates sharing the prefix
   const int shifts[2] = {10, 0};
   const int nbins[2] = {2048, 1024};
   for (int pass = 0; pass < 2; ++pass) {
     for (int x = t; x < nbins[pass]; x += kSelThreads) sh.hist[x] = 0u;
     __syncthreads();
     const uint32_t dmask = (uint32_t)nbins[pass] - 1u;
-    for (int j0 = 4 * t; j0 < n; j0 += 4 * kSelThreads) {
-      float v[4];
-      if (j0 + 3 < n) {
-        const float4 f = *reinterpret_cast<const float4*>(sr + j0);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-      } else {
+    for (int p0 = 4 * t; p0 < cs.m; p0 += 4 * kSelThreads) {
+      uint32_t key[4];
+      int tok[4];
+      bool valid[4];
+      cs.quad(p0, key, tok, valid);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = j0 + e < n ? sr[j0 + e] : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = order_key(v[e]);
-        if (j0 + e < n && (key & pmask) == prefix)
-          atomicAdd(&sh.hist[(key >> shifts[pass]) & dmask], 1u);
-      }
+      for (int e = 0; e < 4; ++e)
+        if (valid[e] && (key[e] & pmask) == prefix)
+          atomicAdd(&sh.hist[(key[e] >> shifts[pass]) & dmask], 1u);
     }
     __syncthreads();
     find_digit(sh, nbins[pass], kk, d, above);
@@ -381,15 +501,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int need_eq = kk;
   // output pass in index order: keep key > K*, and the first need_eq keys == K*
   int eq_before = 0, out_before = 0;
-  for (int base = 0; base < n; base += 4 * kSelThreads) {
-    const int j0 = base + 4 * t;
+  for (int base = 0; base < cs.m; base += 4 * kSelThreads) {
     uint32_t key[4];
+    int tok[4];
     bool valid[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      valid[e] = j0 + e < n;
-      key[e] = valid[e] ? order_key(sr[j0 + e]) : 0u;
-    }
+    cs.quad(base + 4 * t, key, tok, valid);
     int neq = 0, ngt = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -409,11 +525,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     for (int e = 0; e < 4; ++e) {
       if (!valid[e]) continue;
       if (key[e] > kstar) {
-        if (pos < k) out[pos] = j0 + e;
+        if (pos < k) out[pos] = tok[e];
         ++pos;
       } else if (key[e] == kstar) {
         if (eq_rank < need_eq) {
-          if (pos < k) out[pos] = j0 + e;
+          if (pos < k) out[pos] = tok[e];
           ++pos;
         }
         ++eq_rank;
@@ -426,36 +542,56 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   if (kth != nullptr && t == 0) kth[row] = key_to_float(kstar);
 }
 
+// Workspace: candidate keys and tile indices (one TT-entry list per tile of
+// every score row), list lengths, and the rows' digit-1 histograms.
+struct TopkLayout {
+  int rows, tt, tiles, cstride;
+  size_t idx_off, cnt_off, hist_off, bytes;
+};
+
+static TopkLayout topk_layout(const DecodeDims& d, bool pooled) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  TopkLayout L;
+  L.rows = d.B * (pooled ? d.Hkv : d.Hq);
+  L.tt = topk_tile(pooled ? 1 : d.Hq / d.Hkv);
+  L.tiles = (d.max_seq_len + L.tt - 1) / L.tt;
+  L.cstride = L.tiles * L.tt;
+  L.idx_off = up((size_t)L.rows * L.cstride * sizeof(uint32_t));
+  L.cnt_off = L.idx_off + up((size_t)L.rows * L.cstride * sizeof(uint16_t));
+  L.hist_off = L.cnt_off + up((size_t)L.rows * L.tiles * sizeof(uint32_t));
+  L.bytes = L.hist_off + (size_t)L.rows * kBins1 * sizeof(uint32_t);
+  return L;
+}
+
 size_t topk_ws_bytes(const DecodeDims& d, int k) {
   (void)k;
-  const size_t sc = (size_t)d.B * d.Hq * seq_stride(d.max_seq_len) * sizeof(float);
-  const size_t hs = (size_t)d.B * d.Hq * kBins1 * sizeof(uint32_t);
-  return ((sc + 255) / 256) * 256 + hs;
+  const size_t a = topk_layout(d, false).bytes, b = topk_layout(d, true).bytes;
+  return a > b ? a : b;
 }
 
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
                        const DecodeDims& d, int k, bool pooled, int32_t* idx, float* kth, void* ws,
                        hipStream_t st) {
-  const int stride = seq_stride(d.max_seq_len);
   const int rows_per_b = pooled ? d.Hkv : d.Hq;  // score rows (and index sets) per sequence
-  float* scores = static_cast<float*>(ws);
-  const size_t sc = (size_t)d.B * d.Hq * stride * sizeof(float);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + ((sc + 255) / 256) * 256);
-  const size_t nh = (size_t)d.B * rows_per_b * kBins1;
+  const TopkLayout L = topk_layout(d, pooled);
+  char* w = static_cast<char*>(ws);
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(w);
+  uint16_t* cidx = reinterpret_cast<uint16_t*>(w + L.idx_off);
+  uint32_t* ccnt = reinterpret_cast<uint32_t*>(w + L.cnt_off);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(w + L.hist_off);
+  const size_t nh = (size_t)L.rows * kBins1;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + 255) / 256 < 4096 ? (nh + 255) / 256 : 4096)),
                      dim3(256), 0, st, hist, nh, 0u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = d.Hq / d.Hkv;
-  const int tt = topk_tile(pooled ? 1 : G);
-  const int tiles = (d.max_seq_len + tt - 1) / tt;
   const uint16_t* Q = static_cast<const uint16_t*>(q);
   const uint16_t* Kp = static_cast<const uint16_t*>(kpool);
-  const dim3 grid(d.B * d.Hkv * tiles);
+  const dim3 grid(d.B * d.Hkv * L.tiles);
 #define FSA_TS(DD, GG, PP)                                                                   \
   hipLaunchKernelGGL((topk_score_kernel<DD, GG, PP>), grid, dim3(256), 0, st, Q, Kp, pt, sl,  \
-                     d.Hq, d.Hkv, d.max_pages, d.num_pages, d.max_seq_len, stride, tiles,      \
-                     scores, hist)
+                     d.B, d.Hq, d.Hkv, d.max_pages, d.num_pages, d.max_seq_len, k, L.tiles,    \
+                     L.cstride, ckey, cidx, ccnt, hist)
 #define FSA_TS_G(DD, GG)                  \
   if (d.D == DD && G == GG) {             \
     if (pooled)                           \
@@ -469,8 +605,9 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
 #undef FSA_TS
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * rows_per_b), dim3(kSelThreads), 0, st, scores,
-                     hist, sl, rows_per_b, d.max_seq_len, stride, k, idx, kth);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * rows_per_b), dim3(kSelThreads), 0, st, ckey,
+                     cidx, ccnt, hist, sl, rows_per_b, d.max_seq_len, L.tt, L.tiles, L.cstride, k,
+                     idx, kth);
   return hipGetLastError();
 }
 

@@ -162,7 +162,8 @@ int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* 
  * accuracy": one index set per attention (query) head.  Scores are raw
  * q . k in fp32 over tokens [0, seq_lens[b]); the k largest are kept, ties
  * to the lower token index, written ascending.  If seq_lens[b] < k the
- * missing entries are -1 and kth is -inf.
+ * missing entries are -1 and kth is -inf.  max_seq_len <= 2^23 (else
+ * FSA_ERR_SHAPE).
  *   q (device) bf16 [B, Hq, D]; k_pool (device) bf16 [num_pages, Hkv, 16, D]
  *   page_table (device) int32 [B, max_pages]; seq_lens (device) int32 [B]
  *   idx (device) int32 [B, Hq, k]; kth (device, nullable) fp32 [B, Hq]

@@ -147,6 +147,35 @@ def test_topk_many_ties_uses_general_path_exactly():
         assert (idx[1, h] == ref).all()
 
 
+def test_topk_ties_across_pruned_tiles():
+    """Candidate pruning across tiles: the best key is planted in three tiles
+    of a 20000-token row (50 copies each, in tiles 0, 5 and 9 of 2048
+    tokens), so the k-th key (k = 120) is tied 150 times and its ties
+    straddle tiles scored before and after the row's histogram fills up.  The
+    index set must be exactly the oracle's (the 120 lowest tied positions),
+    per query head and pooled per KV head."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, k = 1, 20000, 4, 1, 128, 120
+    d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=1, seed=5, device="cpu")
+    kp = d["layers"][0]["k"].clone()
+    pt = d["page_table"]
+    q = d["layers"][0]["q"].clone()
+    q[0, 1:] = q[0, 0]                      # one query for every head: one best key
+    best = q[0, 0].clone()
+    planted = [j for t in (0, 5, 9) for j in range(t * 2048 + 100, t * 2048 + 150)]
+    for j in planted:
+        kp[pt[0, j // 16], 0, j % 16] = best
+    idx, kth = fsa.topk_indices(q.cuda(), kp.cuda(), pt.cuda(), d["seq_lens"].cuda(), k)
+    idxp, _ = fsa.topk_indices_kv(q.cuda(), kp.cuda(), pt.cuda(), d["seq_lens"].cuda(), k)
+    K = oracle.gather_pages(workloads.to_f64(kp), pt[0].numpy(), N, 0)
+    qq = workloads.to_f64(q)
+    ref, _ = oracle.topk(K @ qq[0, 0], k)
+    assert list(ref) == planted[:k]
+    for h in range(Hq):
+        assert (idx[0, h].cpu().numpy() == ref).all()
+    assert (idxp[0, 0].cpu().numpy() == ref).all()
+
+
 @pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("n_split", [0, 1, 3])
 def test_index_decode_parity(name, n_split):
