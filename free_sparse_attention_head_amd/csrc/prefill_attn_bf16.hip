@@ -347,7 +347,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     if (c + 1 < n) issue_v(c + 1, vI);
     const float mc = prelude(c, sc);
     uint32_t pp[NP];
+    // Two waves share each SIMD.  While one is in its S + softmax phase
+    // (MFMAs interleaved with exp and convert work) it takes issue priority;
+    // the other's PV phase, back-to-back MFMAs, keeps the matrix core busy
+    // meanwhile.
+    __builtin_amdgcn_s_setprio(1);
     s_and_p(has_next, std::true_type{}, kS, sn, sc, mc, pp);
+    __builtin_amdgcn_s_setprio(0);
     pv(pp, vP);
   };
 
