@@ -31,7 +31,8 @@
 namespace fsa {
 
 constexpr int kDecThreads = 256;
-constexpr int kMaxSeg = 64;  // segments per sequence kept in LDS
+constexpr int kMaxSeg = 64;     // segments per sequence kept in LDS
+constexpr int kRowBatch = 1024;  // listed positions resolved to pool rows at a time
 
 template <int D, int NH, int MODE>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ float sm_o[4][NH][D];
   __shared__ int seg_lo[kMaxSeg], seg_pre[kMaxSeg + 1];
   __shared__ int s_nseg;
+  __shared__ uint32_t rows_lds[kRowBatch];  // listed modes: pool row of each position
 
   const int G = Hq / Hkv;
   const int s = blockIdx.x % n_split;
@@ -116,66 +118,84 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   // index list of the item: per query head, or per KV head shared by its G heads
   const int32_t* idxr = LISTED ? idx + ((size_t)b * per_b + hh) * k : nullptr;
 
-  for (int base = p0; base < p1; base += NSLOT * RB) {
-    uint4 kr[RB], vr[RB];
-    bool ok[RB];
+  // pool row of token tok, or kNoRow (out of range, or a bad page id: such
+  // tokens are skipped, never read)
+  constexpr uint32_t kNoRow = 0xffffffffu;
+  auto row_of = [&](int tok) -> uint32_t {
+    if (tok < 0 || tok >= n) return kNoRow;
+    const int page = ptb[tok >> 4];
+    if (page < 0 || page >= num_pages) return kNoRow;
+    return ((uint32_t)page * (uint32_t)Hkv + (uint32_t)g) * 16u + (uint32_t)(tok & 15);
+  };
+  // Listed modes resolve up to kRowBatch positions (index, then page id) to
+  // pool rows in LDS before streaming them, so the K/V loads of a step depend
+  // on no other global load.
+  for (int b0 = p0; b0 < p1; b0 += kRowBatch) {
+    const int b1 = LISTED ? min(p1, b0 + kRowBatch) : p1;
+    if constexpr (LISTED) {
+      __syncthreads();  // the previous batch's rows have been read
+      for (int x = tid; x < b1 - b0; x += kDecThreads) rows_lds[x] = row_of(idxr[b0 + x]);
+      __syncthreads();
+    }
+    for (int base = b0; base < b1; base += NSLOT * RB) {
+      uint4 kr[RB], vr[RB];
+      bool ok[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int pos = base + slot * RB + r;
-      int tok = -1;
-      if (pos < p1) {
-        if constexpr (LISTED) {
-          tok = idxr[pos];
-          if (tok >= n) tok = -1;
-        } else if constexpr (MODE == FSA_SEL_SEGMENT) {
-          int x = 0;
-          while (x + 1 < s_nseg && seg_pre[x + 1] <= pos) ++x;
-          tok = seg_lo[x] + (pos - seg_pre[x]);
+      for (int r = 0; r < RB; ++r) {
+        const int pos = base + slot * RB + r;
+        uint32_t row = kNoRow;
+        if (pos < b1) {
+          if constexpr (LISTED) {
+            row = rows_lds[pos - b0];
+          } else if constexpr (MODE == FSA_SEL_SEGMENT) {
+            int x = 0;
+            while (x + 1 < s_nseg && seg_pre[x + 1] <= pos) ++x;
+            row = row_of(seg_lo[x] + (pos - seg_pre[x]));
+          } else {
+            row = row_of(pos);
+          }
+        }
+        ok[r] = row != kNoRow;
+        if (ok[r]) {
+          kr[r] = *reinterpret_cast<const uint4*>(kpool + (size_t)row * D + dl * 8);
+          vr[r] = *reinterpret_cast<const uint4*>(vpool + (size_t)row * D + dl * 8);
         } else {
-          tok = pos;
+          kr[r] = make_uint4(0, 0, 0, 0);
+          vr[r] = make_uint4(0, 0, 0, 0);
         }
       }
-      const int page = tok >= 0 ? ptb[tok >> 4] : -1;
-      ok[r] = page >= 0 && page < num_pages;  // bad page ids are skipped, never read
-      if (ok[r]) {
-        const size_t row = ((size_t)page * Hkv + g) * 16 + (tok & 15);
-        kr[r] = *reinterpret_cast<const uint4*>(kpool + row * D + dl * 8);
-        vr[r] = *reinterpret_cast<const uint4*>(vpool + row * D + dl * 8);
-      } else {
-        kr[r] = make_uint4(0, 0, 0, 0);
-        vr[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
 #pragma unroll
-    for (int x = 0; x < NHEAD_ITEM; ++x) {
-      float sc[RB];
-      float mx = -INFINITY;
+      for (int x = 0; x < NHEAD_ITEM; ++x) {
+        float sc[RB];
+        float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        float d = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
-        sc[r] = ok[r] ? d * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sc[r]);
-      }
-      const float m_new = fmaxf(m_run[x], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[x] - m_use);
-      m_run[x] = m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[x][e] *= alpha;
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[r] - m_use);
-        ls += p;
-        const uint32_t w[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[x][2 * e] = fmaf(p, bf16_lo(w[e]), o[x][2 * e]);
-          o[x][2 * e + 1] = fmaf(p, bf16_hi(w[e]), o[x][2 * e + 1]);
+        for (int r = 0; r < RB; ++r) {
+          float d = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
+          sc[r] = ok[r] ? d * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sc[r]);
         }
+        const float m_new = fmaxf(m_run[x], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[x] - m_use);
+        m_run[x] = m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[x][e] *= alpha;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sc[r] - m_use);
+          ls += p;
+          const uint32_t w[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[x][2 * e] = fmaf(p, bf16_lo(w[e]), o[x][2 * e]);
+            o[x][2 * e + 1] = fmaf(p, bf16_hi(w[e]), o[x][2 * e + 1]);
+          }
+        }
+        l_run[x] = l_run[x] * alpha + ls;
       }
-      l_run[x] = l_run[x] * alpha + ls;
     }
+    if constexpr (!LISTED) break;  // one pass over [p0, p1)
   }
 
   // ---- merge the row groups of each wave (lanes LPR apart hold the same d
