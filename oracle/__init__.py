@@ -30,6 +30,7 @@ status per function:
   block_stats, pool_queries, select_blocks           -- pinned
   topk, topk_pooled                                   -- pinned
   gather_pages, build_segments                        -- pinned
+  token_block_mass, retention, ideal_rows             -- pinned
 """
 
 from .attention import (dense_attention, masked_attention, masked_attention_rows,
@@ -39,10 +40,12 @@ from .blocks import block_stats, pool_queries, select_blocks, visible_count, k_o
 from .topk import topk, topk_pooled, near_kth_mask
 from .paged import gather_pages
 from .segments import build_segments, SEG_GLOBAL, SEG_FOCUS, SEG_LOCAL, SEG_STREAMING
+from .quality import token_block_mass, retention, ideal_rows
 
 __all__ = [
     "dense_attention", "masked_attention", "masked_attention_rows", "index_attention",
     "segment_attention", "lse_combine", "attention_partial", "block_stats", "pool_queries",
     "select_blocks", "visible_count", "k_of", "topk", "topk_pooled", "near_kth_mask", "gather_pages",
     "build_segments", "SEG_GLOBAL", "SEG_FOCUS", "SEG_LOCAL", "SEG_STREAMING",
+    "token_block_mass", "retention", "ideal_rows",
 ]

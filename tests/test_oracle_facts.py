@@ -17,9 +17,9 @@ import pytest
 import torch
 
 import oracle
-from oracle import (block_stats, build_segments, dense_attention, gather_pages,
-                    index_attention, lse_combine, masked_attention, pool_queries,
-                    segment_attention, select_blocks, topk, topk_pooled)
+from oracle import (block_stats, build_segments, dense_attention, gather_pages, ideal_rows,
+                    index_attention, lse_combine, masked_attention, pool_queries, retention,
+                    segment_attention, select_blocks, token_block_mass, topk, topk_pooled)
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -480,3 +480,82 @@ def test_topk_pooled_closed_forms_and_brute_force():
     tie[1, [3, 7]] = 1.0
     assert list(topk_pooled(tie, 3)[0]) == [0, 3, 7]
     assert list(topk_pooled(s, N)[0]) == list(range(N))
+
+
+# ---- selector quality (RBS-Attention post, "Experimental data": actual
+# retention, selectors compared at matched density)
+
+def _mass_brute_force(q, k, T, scale, i):
+    """Per-query softmax mass on each visible key block, with scalar loops
+    and math.exp (no vectorised softmax)."""
+    out = np.zeros((T, i + 1))
+    for a in range(T):
+        t = i * T + a
+        s = [scale * float(np.dot(q[t], k[u])) for u in range(t + 1)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        tot = sum(w)
+        for u in range(t + 1):
+            out[a, u // T] += w[u] / tot
+    return out
+
+
+def test_Q1_full_mask_retains_everything_and_complement_sums_to_one():
+    """Every visible block admitted -> retention 1 (the softmax sums to 1); a
+    mask and its complement within the visible blocks split the mass."""
+    rng = _rng(21)
+    S, D, T = 48, 8, 4
+    q, k = rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    nB = S // T
+    full = np.tril(np.ones((nB, nB), dtype=bool))
+    for i, r in retention(q, k, full, T, 0.5).items():
+        assert np.abs(r - 1.0).max() < 1e-12
+    half = full & (rng.random((nB, nB)) < 0.5)
+    r1 = retention(q, k, half, T, 0.5)
+    r2 = retention(q, k, full & ~half, T, 0.5)
+    for i in range(nB):
+        assert np.abs(r1[i] + r2[i] - 1.0).max() < 1e-12
+        assert (r1[i] >= 0).all() and (r1[i] <= 1 + 1e-12).all()
+
+
+def test_Q2_block_mass_brute_force_and_library_softmax():
+    """Block masses equal scalar-loop softmax sums, and torch's causal softmax
+    summed per block; a T = 1 diagonal-only mask keeps exactly each token's
+    weight on itself."""
+    rng = _rng(22)
+    S, D, T, scale = 24, 6, 3, 0.7
+    q, k = rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    mass = token_block_mass(q, k, T, scale)
+    sc = torch.from_numpy(scale * q @ k.T)
+    sc = sc.masked_fill(torch.triu(torch.ones(S, S, dtype=torch.bool), 1), -math.inf)
+    p = torch.softmax(sc, dim=1).numpy()
+    for i in range(S // T):
+        assert np.abs(mass[i] - _mass_brute_force(q, k, T, scale, i)).max() < 1e-12
+        lib = p[i * T:(i + 1) * T, :(i + 1) * T].reshape(T, i + 1, T).sum(axis=2)
+        assert np.abs(mass[i] - lib).max() < 1e-12
+    diag = np.eye(S, dtype=bool)
+    r = retention(q, k, diag, 1, scale)
+    assert np.abs(np.array([r[t][0] for t in range(S)]) - np.diag(p)).max() < 1e-12
+
+
+def test_Q3_ideal_rows_brute_force_over_block_subsets():
+    """The ideal set at count c is the c-subset of visible blocks with the
+    largest mean retention (checked against every subset)."""
+    import itertools
+    rng = _rng(23)
+    S, D, T = 28, 5, 4
+    q, k = 2 * rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    nB = S // T
+    counts = {i: 1 + (i * 3) % (i + 1) for i in range(nB)}
+    ideal = ideal_rows(q, k, T, 0.9, counts, range(nB))
+    for i in range(nB):
+        best, best_set = -1.0, None
+        for sub in itertools.combinations(range(i + 1), counts[i]):
+            m = np.zeros((nB, nB), dtype=bool)
+            m[i, list(sub)] = True
+            val = retention(q, k, m, T, 0.9, rows=[i])[i].mean()
+            if val > best + 1e-12:
+                best, best_set = val, sub
+        blocks, ret = ideal[i]
+        assert tuple(blocks) == best_set
+        assert abs(ret.mean() - best) < 1e-12

@@ -14,6 +14,7 @@ import pytest
 import oracle
 from oracle import attention as att
 from oracle import blocks as blk
+from oracle import quality as qual
 from tests import test_oracle_facts as pins
 
 
@@ -74,6 +75,33 @@ def _pool_uses_first_row(q, T):
     return q[::T].copy()
 
 
+def _mass_without_causality(q, k, T, scale, rows=None):
+    q, k = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
+    rows = range(q.shape[0] // T) if rows is None else rows
+    out = {}
+    for i in rows:
+        s = scale * (q[i * T:(i + 1) * T] @ k[:(i + 1) * T].T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out[i] = p.reshape(T, i + 1, T).sum(axis=2)
+    return out
+
+
+def _retention_of_complement(q, k, mask, T, scale, rows=None):
+    mass = qual.token_block_mass(q, k, T, scale, rows)
+    mask = np.asarray(mask, dtype=bool)
+    return {i: m[:, ~mask[i, :i + 1]].sum(axis=1) for i, m in mass.items()}
+
+
+def _ideal_keeps_least(q, k, T, scale, counts, rows):
+    mass = qual.token_block_mass(q, k, T, scale, rows)
+    out = {}
+    for i, m in mass.items():
+        keep = np.sort(np.argsort(m.mean(axis=0), kind="stable")[:counts[i]])
+        out[i] = (keep, m[:, keep].sum(axis=1))
+    return out
+
+
 CASES = [
     ("select_blocks", _rescue_sign_flipped,
      [pins.test_F4_planted_spike_dropped_by_centroid_recovered_by_rescue]),
@@ -90,6 +118,11 @@ CASES = [
      [lambda: pins.test_F8_focus_minimum_neighbourhood(5000, 100)]),
     ("pool_queries", _pool_uses_first_row, [pins.test_F5_pool_queries_block_means]),
     ("topk_pooled", _pooled_by_mean, [pins.test_topk_pooled_closed_forms_and_brute_force]),
+    ("token_block_mass", _mass_without_causality,
+     [pins.test_Q2_block_mass_brute_force_and_library_softmax]),
+    ("retention", _retention_of_complement,
+     [pins.test_Q1_full_mask_retains_everything_and_complement_sums_to_one]),
+    ("ideal_rows", _ideal_keeps_least, [pins.test_Q3_ideal_rows_brute_force_over_block_subsets]),
 ]
 
 

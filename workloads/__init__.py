@@ -21,6 +21,9 @@ for them):
     layer 0 keys/values/queries i.i.d. N(0,1); later layers of a Kascade group
     use fresh queries and values and keys 0.9 * K_0 + sqrt(0.19) * Z (cosine
     ~0.9 to the anchor layer's keys).
+  * prefill layer group (anchor selection reused by later layers): layer l > 0
+    has Q_l = 0.9 * Q_0 + sqrt(0.19) * Z_q and K_l = 0.9 * K_0 + sqrt(0.19) * Z_k
+    (the anchor layer's planted spikes carry over, scaled) and fresh V_l.
 Every tensor comes from its own generator stream seeded seed * 100 + id.
 """
 
@@ -100,6 +103,23 @@ def prefill_inputs(B, S, Hq, Hkv, D, T, dtype=torch.bfloat16, model="lowrank",
                 k[b, int(tok), g] = (spike_scale * u / u.norm()).float()
                 spikes.append((b, g, int(tok), h, i))
     return {"q": q.to(dtype), "k": k.to(dtype), "v": v.to(dtype), "spikes": spikes}
+
+
+def prefill_layer(base, layer, corr=0.9, seed=0):
+    """Layer `layer` >= 1 of a prefill group whose anchor layer is `base` (a
+    prefill_inputs dict): queries and keys corr * anchor + sqrt(1-corr^2) * Z,
+    values fresh N(0,1).  Returns dict(q, k, v) with the anchor's dtypes."""
+    assert layer >= 1
+    s = math.sqrt(1.0 - corr * corr)
+    out = {}
+    for name, sid in (("q", 40), ("k", 41)):
+        t = base[name]
+        z = _randn(t.shape, t.device, seed, sid + 3 * layer)
+        out[name] = (corr * t.float() + s * z).to(t.dtype)
+        del z
+    v = base["v"]
+    out["v"] = _randn(v.shape, v.device, seed, 42 + 3 * layer).to(v.dtype)
+    return out
 
 
 def page_table_for(B, max_pages, device, seed, sid=20):
