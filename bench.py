@@ -74,16 +74,19 @@ class Timer:
         self.ev = {}
 
 
-def tune_selector(fsa, q, c, r, P, density, out=None):
+def tune_selector(fsa, q, c, r, P, density, out=None, branches="both"):
     """Bisect p_c (p_r = 0.4 p_c) until the selector's density is within
-    0.25 points of the target; returns (p_c, density, selector outputs)."""
+    0.25 points of the target; returns (p_c, density, selector outputs).
+    branches "centroid" / "rescue" switch the other branch off and bisect the
+    one left (its p is returned)."""
     nB = P["S"] // P["T"]
     visible = P["Hq"] * nB * (nB + 1) // 2
     lo, hi = 0.0, 1.0
     pc = dens = None
     for _ in range(30):
         pc = 0.5 * (lo + hi)
-        out = fsa.select_blocks(q, c, r, P["T"], pc, 0.4 * pc, P["band"], P["sink"], out=out)
+        p_c, p_r = {"both": (pc, 0.4 * pc), "centroid": (pc, -1.0), "rescue": (-1.0, pc)}[branches]
+        out = fsa.select_blocks(q, c, r, P["T"], p_c, p_r, P["band"], P["sink"], out=out)
         dens = out["block_cnt"].sum().item() / visible
         if abs(dens - density) <= 0.0025:
             break
@@ -91,7 +94,7 @@ def tune_selector(fsa, q, c, r, P, density, out=None):
             lo = pc
         else:
             hi = pc
-    log(f"[bench] S={P['S']} T={P['T']} selector p_c={pc:.5f} p_r={0.4 * pc:.5f} density={dens:.4f}")
+    log(f"[bench] S={P['S']} T={P['T']} selector ({branches}) p={pc:.5f} density={dens:.4f}")
     return pc, dens, out
 
 
@@ -104,6 +107,7 @@ def make_prefill(fsa, workloads, density, seed=1002, P=None):
     c, r = fsa.block_stats(k, P["T"])
     pc, dens, out = tune_selector(fsa, q, c, r, P, density)
     return dict(q=q, k=k, v=v, p_c=pc, p_r=0.4 * pc, density=dens, sel=out, c=c, r=r,
+                spikes=inp["spikes"],
                 o=torch.empty_like(q), lse=torch.empty((1, P["Hq"], P["S"]), dtype=torch.float32,
                                                       device="cuda"))
 
@@ -170,7 +174,52 @@ def prefill_sweep(fsa, workloads, pf):
     del sel
     p32 = make_prefill(fsa, workloads, 0.10, seed=1001, P=PREFILL_32K)
     res["32k_block64_10pct"] = time_attention(fsa, p32, PREFILL_32K)
-    del p32
+    return res, p32
+
+
+def spike_recall(sel, spikes, device="cuda"):
+    """Share of planted spikes whose key block is in the mask row of the query
+    block and head the spike was aimed at."""
+    if not spikes:
+        return None
+    b, g, tok, h, i = (torch.tensor(x, device=device) for x in zip(*spikes))
+    T = sel["T"]
+    j = tok // T
+    words = sel["mask"][b, h, i, j // 32].to(torch.int64) & 0xffffffff
+    return round(((words >> (j % 32)) & 1).float().mean().item(), 4)
+
+
+def selector_quality(fsa, workloads, p32, density=0.10):
+    """Selectors compared at matched density on the 32K prompt with 64-token
+    blocks (RBS-Attention post, "Experimental data": actual retention, matched
+    density).  Retention of token t = the share of its causal softmax mass on
+    admitted keys = exp(lse_mask(t) - lse_dense(t)), both from the attention
+    kernel.  Spike recall: planted spikes whose block the selector keeps, on
+    this prompt (spikes of norm 6) and on one with spikes of norm 2 sqrt(D),
+    which then dominate the block radius."""
+    P = PREFILL_32K
+    T = P["T"]
+    q, k, v = p32["q"], p32["k"], p32["v"]
+    _, lse_d = fsa.sparse_prefill_attn(q, k, v, T)
+    res = {"density_target": density, "retention_mean": {}, "retention_p10": {},
+           "spike_recall_norm6": {}, "spike_recall_norm2sqrtD": {}, "density": {}}
+    alt = workloads.prefill_inputs(1, P["S"], P["Hq"], P["Hkv"], P["D"], T, model="lowrank",
+                                   spike_scale=2 * math.sqrt(P["D"]), seed=1011, device="cuda")
+    c2, r2 = fsa.block_stats(alt["k"], T)
+    for br in ("both", "centroid", "rescue"):
+        _, dens, sel = tune_selector(fsa, q, p32["c"], p32["r"], P, density, branches=br)
+        _, lse_m = fsa.sparse_prefill_attn(q, k, v, T, sel["block_idx"], sel["block_cnt"])
+        ret = torch.exp(lse_m - lse_d).flatten()
+        name = {"both": "merged", "centroid": "centroid_only", "rescue": "rescue_only"}[br]
+        res["density"][name] = round(dens, 4)
+        res["retention_mean"][name] = round(ret.mean().item(), 4)
+        res["retention_p10"][name] = round(torch.quantile(ret, 0.10).item(), 4)
+        res["spike_recall_norm6"][name] = spike_recall(dict(sel, T=T), p32["spikes"])
+        del sel, lse_m, ret
+        _, _, sel2 = tune_selector(fsa, alt["q"], c2, r2, P, density, branches=br)
+        res["spike_recall_norm2sqrtD"][name] = spike_recall(dict(sel2, T=T), alt["spikes"])
+        del sel2
+    del alt, c2, r2, lse_d
     torch.cuda.empty_cache()
     return res
 
@@ -402,6 +451,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the prefill density sweep")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the selector comparison at matched density")
     ap.add_argument("--only", choices=["prefill", "decode", "segment"], default=None,
                     help="profile one part of the step only (not a benchmark result)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -489,10 +540,15 @@ def main():
                                               (ddec * 1e-3) / 1e9, 1),
                  "decode_group_speedup": round(ddec / group_ms, 2)}
 
-    sweep, kv_shared = {}, {}
+    sweep, kv_shared, quality = {}, {}, {}
     if not args.no_sweep:
         log("[bench] prefill density sweep and 32K prompt")
-        sweep = prefill_sweep(fsa, workloads, pf)
+        sweep, p32 = prefill_sweep(fsa, workloads, pf)
+        if not args.no_quality:
+            log("[bench] selectors at matched density (32K prompt)")
+            quality = selector_quality(fsa, workloads, p32)
+        del p32
+        torch.cuda.empty_cache()
         log("[bench] per-KV-head Kascade variant")
         kv_shared = decode_kv_shared(fsa, dc)
 
@@ -549,6 +605,7 @@ def main():
         "dense": dense,
         "prefill_sweep": sweep,
         "decode_kv_shared": kv_shared,
+        "selector_quality": quality,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

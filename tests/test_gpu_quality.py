@@ -1,0 +1,120 @@
+"""Selector quality on the GPU against the fp64 oracle (RBS-Attention post,
+"Experimental data": actual retention, selectors at matched density).
+
+The retention of query token t under a block mask is the share of its causal
+softmax mass on the admitted keys; the library gives it without a new kernel,
+as exp(lse_mask(t) - lse_dense(t)) from two sparse_prefill_attn launches.
+Tolerance: both log-sum-exps sum bf16-rounded probabilities (relative error at
+most 2^-9 each), so the ratio of the two sums is off by at most about
+2 * 2^-9 < 4e-3 of its value.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._parity import lists_to_mask
+
+pytestmark = pytest.mark.gpu
+
+B, S, Hq, Hkv, D, T = 1, 4096, 4, 2, 128, 64
+TOL_RET = 4e-3
+
+
+def _case():
+    import free_sparse_attention_head_amd as fsa
+    print(f"[quality case] S={S} Hq={Hq} Hkv={Hkv} D={D} T={T} spikes of norm 2 sqrt(D)", flush=True)
+    inp = workloads.prefill_inputs(B, S, Hq, Hkv, D, T, model="lowrank", n_spikes=40,
+                                   spike_scale=2 * math.sqrt(D), seed=7, device="cpu")
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    c, r = fsa.block_stats(k, T)
+    sel = {name: fsa.select_blocks(q, c, r, T, pc, pr)
+           for name, pc, pr in (("merged", 0.10, 0.04), ("centroid", 0.14, -1.0),
+                                ("rescue", -1.0, 0.14))}
+    _, lse_d = fsa.sparse_prefill_attn(q, k, v, T)
+    ret = {}
+    for name, s in sel.items():
+        _, lse_m = fsa.sparse_prefill_attn(q, k, v, T, s["block_idx"], s["block_cnt"])
+        ret[name] = torch.exp(lse_m - lse_d)[0].cpu().double().numpy()   # [Hq, S]
+    return inp, {n: {x: y.cpu() for x, y in s.items() if y is not None} for n, s in sel.items()}, ret
+
+
+_cache = []
+
+
+def case():
+    if not _cache:
+        _cache.append(_case())
+    return _cache[0]
+
+
+def test_retention_from_lse_matches_oracle():
+    inp, sel, ret = case()
+    q, k = workloads.to_f64(inp["q"]), workloads.to_f64(inp["k"])
+    nB = S // T
+    scale = 1 / math.sqrt(D)
+    worst = 0.0
+    for name in sel:
+        for h in (0, Hq - 1):
+            m = lists_to_mask(sel[name]["block_idx"][0, h].numpy(), sel[name]["block_cnt"][0, h].numpy(), nB)
+            ref = oracle.retention(q[0, :, h], k[0, :, h // (Hq // Hkv)], m, T, scale)
+            for i in range(nB):
+                err = np.abs(ret[name][h, i * T:(i + 1) * T] - ref[i]).max()
+                worst = max(worst, err)
+                assert err <= TOL_RET, (name, h, i, err)
+    print(f"[quality] retention max-abs difference GPU vs oracle {worst:.2e}")
+
+
+def test_ideal_mask_bounds_every_selector_row():
+    """At each row's own block count, the oracle's ideal mask keeps at least
+    as much mass as any selector's mask (and the report shows how far each
+    selector is from it)."""
+    inp, sel, ret = case()
+    q, k = workloads.to_f64(inp["q"]), workloads.to_f64(inp["k"])
+    nB = S // T
+    scale = 1 / math.sqrt(D)
+    h = 1
+    rows = list(range(0, nB, 3))
+    for name in sel:
+        cnt = sel[name]["block_cnt"][0, h].numpy()
+        ideal = oracle.ideal_rows(q[0, :, h], k[0, :, h // (Hq // Hkv)], T, scale, cnt, rows)
+        got = [ret[name][h, i * T:(i + 1) * T].mean() for i in rows]
+        best = [ideal[i][1].mean() for i in rows]
+        for g_, b_ in zip(got, best):
+            assert g_ <= b_ + TOL_RET
+        print(f"[quality] {name}: mean retention {np.mean(got):.4f}, ideal at the same counts "
+              f"{np.mean(best):.4f}")
+
+
+def test_spike_recall_at_matched_density():
+    """Spikes of norm 2 sqrt(D) dominate their block's radius: the rescue
+    branch keeps every spike block and the merged selector more of them than
+    the centroid branch alone at about the same density.  The GPU masks'
+    recall equals the oracle selector's on the same inputs."""
+    inp, sel, ret = case()
+    q, k = workloads.to_f64(inp["q"]), workloads.to_f64(inp["k"])
+    nB = S // T
+    G = Hq // Hkv
+    params = {"merged": (0.10, 0.04), "centroid": (0.14, -1.0), "rescue": (-1.0, 0.14)}
+    recall = {}
+    for name, (pc, pr) in params.items():
+        hit_gpu = hit_ref = 0
+        masks = {}
+        for g in range(Hkv):
+            c, r = oracle.block_stats(k[0, :, g], T)
+            for h in range(g * G, (g + 1) * G):
+                masks[h] = oracle.select_blocks(oracle.pool_queries(q[0, :, h], T), c, r, pc, pr)["M"]
+        for (b, g, tok, h, i) in inp["spikes"]:
+            gm = lists_to_mask(sel[name]["block_idx"][0, h].numpy(), sel[name]["block_cnt"][0, h].numpy(), nB)
+            hit_gpu += bool(gm[i, tok // T])
+            hit_ref += bool(masks[h][i, tok // T])
+        n = len(inp["spikes"])
+        assert hit_gpu == hit_ref, (name, hit_gpu, hit_ref)
+        recall[name] = hit_gpu / n
+    print(f"[quality] spike recall {recall}")
+    assert recall["rescue"] == 1.0
+    assert recall["merged"] > recall["centroid"]
