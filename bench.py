@@ -224,6 +224,59 @@ def selector_quality(fsa, workloads, p32, density=0.10):
     return res
 
 
+def prefill_reuse(fsa, workloads, pf, anchor_path_ms, layers=4, reps=3):
+    """Kascade-style prefill on the 128K prompt (outside the timed steps): the
+    anchor layer's block lists (the steps' selection) drive the attention of
+    three later layers whose queries and keys sit at cosine ~0.9 to the
+    anchor's, against each layer running its own block_stats + select_blocks
+    at the anchor's thresholds.  Also reported per later layer: the share of
+    its own selection that the anchor's mask contains, and the retention
+    (causal softmax mass kept) of both masks, from the kernel's LSE."""
+    P = PREFILL
+    T = P["T"]
+    anchor = pf["sel"]
+    base = {"q": pf["q"], "k": pf["k"], "v": pf["v"]}
+    nwords = anchor["mask"].shape[-1]
+    shifts = torch.arange(32, device="cuda", dtype=torch.int64)
+
+    def nbits(m):
+        w = m.to(torch.int64) & 0xffffffff
+        return ((w.unsqueeze(-1) >> shifts) & 1).sum().item()
+
+    tm = Timer()
+    out = {"overlap_own_in_anchor": [], "retention_reused": [], "retention_own": []}
+    lse_r = torch.empty_like(pf["lse"])
+    lse_o = torch.empty_like(pf["lse"])
+    for li in range(1, layers):
+        L = workloads.prefill_layer(base, li, seed=1002)
+        own = None
+        for _ in range(2 + reps):
+            tm.run(f"reuse_attn{li}", lambda: fsa.sparse_prefill_attn(
+                L["q"], L["k"], L["v"], T, anchor["block_idx"], anchor["block_cnt"], out=pf["o"],
+                lse=lse_r))
+            cr = tm.run(f"own_stats{li}", lambda: fsa.block_stats(L["k"], T))
+            own = tm.run(f"own_select{li}", lambda: fsa.select_blocks(
+                L["q"], cr[0], cr[1], T, pf["p_c"], pf["p_r"], P["band"], P["sink"], out=own))
+            tm.run(f"own_attn{li}", lambda: fsa.sparse_prefill_attn(
+                L["q"], L["k"], L["v"], T, own["block_idx"], own["block_cnt"], out=pf["o"],
+                lse=lse_o))
+        _, lse_d = fsa.sparse_prefill_attn(L["q"], L["k"], L["v"], T)
+        assert own["mask"].shape[-1] == nwords
+        out["overlap_own_in_anchor"].append(round(nbits(own["mask"] & anchor["mask"]) / nbits(own["mask"]), 4))
+        out["retention_reused"].append(round(torch.exp(lse_r - lse_d).mean().item(), 4))
+        out["retention_own"].append(round(torch.exp(lse_o - lse_d).mean().item(), 4))
+        del L, own, lse_d
+        torch.cuda.empty_cache()
+    later = range(1, layers)
+    reuse = [tm.ms(f"reuse_attn{li}", skip=2)[0] for li in later]
+    own = [sum(tm.ms(f"{x}{li}", skip=2)[0] for x in ("own_stats", "own_select", "own_attn"))
+           for li in later]
+    return dict(out, layers=layers, anchor_path_ms=round(anchor_path_ms, 4),
+                reuse_attn_ms=[round(x, 4) for x in reuse], own_path_ms=[round(x, 4) for x in own],
+                group_reused_ms=round(anchor_path_ms + sum(reuse), 4),
+                group_own_ms=round(anchor_path_ms + sum(own), 4))
+
+
 def make_decode(fsa, workloads, seed=1003):
     D = DECODE
     log(f"[bench] generating Kascade decode group B={D['B']} N={D['N']} layers={D['layers']}")
@@ -540,8 +593,10 @@ def main():
                                               (ddec * 1e-3) / 1e9, 1),
                  "decode_group_speedup": round(ddec / group_ms, 2)}
 
-    sweep, kv_shared, quality = {}, {}, {}
+    sweep, kv_shared, quality, reuse = {}, {}, {}, {}
     if not args.no_sweep:
+        log("[bench] anchor selection reused by three later prefill layers")
+        reuse = prefill_reuse(fsa, workloads, pf, path_ms)
         log("[bench] prefill density sweep and 32K prompt")
         sweep, p32 = prefill_sweep(fsa, workloads, pf)
         if not args.no_quality:
@@ -606,6 +661,7 @@ def main():
         "prefill_sweep": sweep,
         "decode_kv_shared": kv_shared,
         "selector_quality": quality,
+        "prefill_reuse": reuse,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

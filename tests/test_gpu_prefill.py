@@ -182,3 +182,30 @@ def test_empty_and_invalid_list_entries():
     diag = np.eye(nB, dtype=bool)
     ref, _ = oracle.masked_attention(qq[0, :, 0], kk[0, :, 0], vv[0, :, 0], diag, T, 1 / math.sqrt(D))
     assert np.abs(o[0, :, 0].double().numpy() - ref).max() <= TOL_BF16
+
+
+def test_anchor_selection_reused_by_a_later_layer():
+    """Kascade-style prefill: the anchor layer's block lists drive a later
+    layer's attention (queries and keys at cosine ~0.9 to the anchor's).  The
+    result is exact masked attention of the later layer's Q, K, V under the
+    anchor's mask."""
+    import free_sparse_attention_head_amd as fsa
+    Bb, S, Hq, Hkv, D, T = 1, 2048, 4, 2, 128, 64
+    nB = S // T
+    print(f"[prefill reuse case] S={S} Hq={Hq} Hkv={Hkv} D={D} T={T}", flush=True)
+    base = workloads.prefill_inputs(Bb, S, Hq, Hkv, D, T, model="lowrank", n_spikes=20, seed=31,
+                                    device="cpu")
+    later = workloads.prefill_layer(base, 1, seed=31)
+    q0, k0 = base["q"].cuda(), base["k"].cuda()
+    c, r = fsa.block_stats(k0, T)
+    sel = fsa.select_blocks(q0, c, r, T, 0.15, 0.06, 2, 1)
+    q1, k1, v1 = (later[x].cuda() for x in ("q", "k", "v"))
+    o, lse = fsa.sparse_prefill_attn(q1, k1, v1, T, sel["block_idx"], sel["block_cnt"])
+    o, lse = o.cpu(), lse.cpu()
+    q, k, v = (workloads.to_f64(later[x]) for x in ("q", "k", "v"))
+    for h in range(Hq):
+        m = lists_to_mask(sel["block_idx"][0, h].cpu().numpy(), sel["block_cnt"][0, h].cpu().numpy(), nB)
+        ref, ref_lse = oracle.masked_attention(q[0, :, h], k[0, :, h // 2], v[0, :, h // 2], m, T,
+                                               1 / math.sqrt(D))
+        assert np.abs(o[0, :, h].double().numpy() - ref).max() <= TOL_BF16
+        assert np.abs(lse[0, h].double().numpy() - ref_lse).max() <= 10 * TOL_BF16
