@@ -193,6 +193,8 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   const size_t row0 = POOL ? (size_t)b * Hkv + g : (size_t)b * Hq + (size_t)g * G;
   constexpr int BPT = kBins1 / 256;  // histogram bins per thread
   constexpr int PER = TT / 256;      // tile tokens per thread
+  // the compaction below reads each thread's tokens as 16-byte quads
+  static_assert(PER >= 4 && PER % 4 == 0, "tile of whole 16-byte quads per thread");
   __shared__ uint32_t sbound[GR];
   const int nt = t1 - t0;
   // Candidate bounds: per row, the bin of the k-th largest key counted in
