@@ -77,6 +77,14 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, const void* l) {
   __builtin_amdgcn_global_load_lds(g, lds_ptr<void>(l), 16, 0, 0);
 }
 
+// max of x over lanes l and l ^ 32: v_permlane32_swap exchanges the two
+// halves of the wave in registers (no LDS round trip); of its two results,
+// lane l < 32 holds x[l] and x[l + 32], lane l >= 32 holds x[l - 32] and x[l]
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 }  // namespace
 
 template <int D, int BLK, int KCH, int LMAX>
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     for (int tl = 0; tl < NKT; ++tl)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tl][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor32(mx);
     // lazy rescale: the reference max moves only when a row grows by more
     // than kRescale (log2 units), so p <= 256 and O^T is rescaled rarely
     const bool grow = (mx - m_run) * scale_log2 > kRescale;
