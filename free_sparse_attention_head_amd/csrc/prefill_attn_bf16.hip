@@ -170,17 +170,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     kofs[m] = (uint32_t)((r * kv_stride + (sl ^ k_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
     vofs[m] = (uint32_t)((r * kv_stride + (sl ^ v_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
   }
-  auto issue_tile = [&](int c, const uint16_t* src0, const uint32_t (&ofs)[Tr::IPW],
+  // (j = key block of chunk c, read from the list one step ahead)
+  auto issue_tile = [&](int c, int j, const uint16_t* src0, const uint32_t (&ofs)[Tr::IPW],
                         unsigned char* tile) {
-    const int j = __builtin_amdgcn_readfirstlane(Ls[c / NCH]);
+    j = __builtin_amdgcn_readfirstlane(j);
     const size_t base = ((size_t)j * BLK + (c % NCH) * KC) * kv_stride * sizeof(uint16_t);
     const char* src = reinterpret_cast<const char*>(src0) + base;
 #pragma unroll
     for (int m = 0; m < Tr::IPW; ++m)
       copy16_to_lds(src + ofs[m], tile + (wave * Tr::IPW + m) * 1024);
   };
-  auto issue_k = [&](int c, unsigned char* kt) { issue_tile(c, Kb, kofs, kt); };
-  auto issue_v = [&](int c, unsigned char* vt) { issue_tile(c, Vb, vofs, vt); };
+  auto issue_k = [&](int c, int j, unsigned char* kt) { issue_tile(c, j, Kb, kofs, kt); };
+  auto issue_v = [&](int c, int j, unsigned char* vt) { issue_tile(c, j, Vb, vofs, vt); };
 
   // Pipeline barrier: this wave's tile copies have landed and its LDS reads
   // have retired; the s_barrier then publishes every wave's copies and frees
@@ -216,8 +217,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // rescale for chunk c; returns the exponent offset of P.  Register r of
   // tile tl holds key koff + tl*32 + (r/4)*8 + lg*4 + r%4.  Chunks wholly
   // after this wave's rows come out all masked (P = 0).
-  auto prelude = [&](int c, floatx16 (&s)[NKT]) -> float {
-    const int j = Ls[c / NCH];
+  auto prelude = [&](int c, int j, floatx16 (&s)[NKT]) -> float {
     const int koff = (c % NCH) * KC;
     if (j == i) {
       const int rel = koff + lg * 4 - qrow;
@@ -348,12 +348,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // landed; it then refills the K slot of chunk c (read by the previous step)
   // with chunk c+2 and the V slot of chunk c-1 with chunk c+1.
   const int n = nchunks;
+  // key blocks of chunks c, c+1 and c+2 at step c; the next one is read from
+  // the list during step c, so no list read sits between a step's barrier
+  // and its copies
+  auto block_of = [&](int c) { return (int)Ls[min(c, n - 1) / NCH]; };
+  int jq0 = 0, jq1 = 0, jq2 = 0;
   auto step = [&](auto has_next, int c, const unsigned char* kS, const unsigned char* vP,
                   unsigned char* kI, unsigned char* vI, floatx16 (&sc)[NKT], floatx16 (&sn)[NKT]) {
     tile_barrier();
-    if (c + 2 < n) issue_k(c + 2, kI);
-    if (c + 1 < n) issue_v(c + 1, vI);
-    const float mc = prelude(c, sc);
+    if (c + 2 < n) issue_k(c + 2, jq2, kI);
+    if (c + 1 < n) issue_v(c + 1, jq1, vI);
+    const int jc = jq0;
+    jq0 = jq1;
+    jq1 = jq2;
+    jq2 = block_of(c + 3);
+    const float mc = prelude(c, jc, sc);
     uint32_t pp[NP];
     // Two waves share each SIMD.  While one is in its S + softmax phase
     // (MFMAs interleaved with exp and convert work) it takes issue priority;
@@ -368,9 +377,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   if (n > 0) {
     floatx16 sA[NKT], sB[NKT];
     uint32_t pp0[NP];
-    issue_k(0, kb0);
-    issue_v(0, vb0);
-    if (n > 1) issue_k(1, kb1);
+    jq0 = block_of(0);
+    jq1 = block_of(1);
+    jq2 = block_of(2);
+    issue_k(0, jq0, kb0);
+    issue_v(0, jq0, vb0);
+    if (n > 1) issue_k(1, jq1, kb1);
     tile_barrier();
     s_and_p(std::true_type{}, std::false_type{}, kb0, sA, sB, 0.f, pp0);
     int c = 0;
