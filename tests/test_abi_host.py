@@ -154,6 +154,13 @@ def test_topk_and_decode_argument_validation():
     assert kcall(L.FSA_F32, 16, ws) == L.FSA_ERR_DTYPE
     assert kcall(L.FSA_BF16, 0, ws) == L.FSA_ERR_ARG
     assert kcall(L.FSA_BF16, 16, ws - 1) == L.FSA_ERR_WORKSPACE
+    # top-k supports sequences of up to 2^23 tokens (its select kernel keeps the
+    # lengths of every tile's candidate list in LDS)
+    big = _dshape(L, max_pages=(1 << 19) + 1, num_pages=64, max_seq_len=(1 << 23) + 16)
+    assert lib.topk_indices(L.FSA_BF16, FAKE, FAKE, FAKE, FAKE, ctypes.byref(big), 16, FAKE,
+                            None, FAKE, 1 << 62, None) == L.FSA_ERR_SHAPE
+    assert lib.topk_indices_kv(L.FSA_BF16, FAKE, FAKE, FAKE, FAKE, ctypes.byref(big), 16, FAKE,
+                               None, FAKE, 1 << 62, None) == L.FSA_ERR_SHAPE
     sel = L.KvSelect(L.FSA_SEL_SEGMENT, None, 0, FAKE.value, FAKE.value, 0, 0)
     assert dcall(sel) == L.FSA_ERR_ARG                       # max_seg 0
     sel = L.KvSelect(9, None, 0, None, None, 0, 0)

@@ -199,6 +199,41 @@ def test_index_decode_parity(name, n_split):
             assert abs(lse[b, h].item() - l) <= 1e-2
 
 
+@pytest.mark.parametrize("mode", ["index", "index_kv"])
+def test_listed_decode_spans_several_row_batches(mode):
+    """One split of 2500 listed positions: the kernel resolves positions to
+    pool rows 1024 at a time, so a split crosses three batches (the last one
+    ragged).  The list also repeats some positions and holds out-of-range ones
+    (skipped)."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, k = 2, 6000, 4, 2, 128, 2500
+    print(f"[listed decode case {mode}] B={B} N={N} k={k} one split", flush=True)
+    d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=1, seq_lens=[6000, 4000], seed=41,
+                                device="cpu")
+    rows = Hq if mode == "index" else Hkv
+    rng = np.random.default_rng(41)
+    idx = rng.integers(0, N, size=(B, rows, k)).astype(np.int32)
+    idx[:, :, :7] = -3          # out of range: skipped
+    idx[:, :, 7:20] = idx[:, :, 20:33]   # repeated positions count twice
+    L = d["layers"][0]
+    sel = fsa.SEL_INDEX if mode == "index" else fsa.SEL_INDEX_KV
+    out, lse = fsa.sparse_decode_attn(L["q"].cuda(), L["k"].cuda(), L["v"].cuda(),
+                                      d["page_table"].cuda(), d["seq_lens"].cuda(), mode=sel,
+                                      idx=torch.from_numpy(idx).cuda(), n_split=1)
+    out, lse = out.cpu(), lse.cpu()
+    q = workloads.to_f64(L["q"])
+    G = Hq // Hkv
+    for b in range(B):
+        n = int(d["seq_lens"][b])
+        for h in range(Hq):
+            K, V = seq_kv(d, 0, b, h // G)
+            ix = idx[b, h if mode == "index" else h // G]
+            ix = np.where(ix < n, ix, -1)
+            o, l = oracle.index_attention(q[b, h], K, V, ix, 1 / math.sqrt(D))
+            assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
+            assert abs(lse[b, h].item() - l) <= 1e-2
+
+
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_topk_kv_parity(name):
     """One index set per KV head from the max over its query heads' scores."""
