@@ -22,7 +22,8 @@
 //   * the softmax is online per lane group (one rescale per RB-row step);
 //     lane groups and waves merge through LDS at the end of the split and
 //     write an unnormalised (max, sum, output) partial in fp32;
-//   * combine_kernel merges the splits of one (sequence, head).
+//   * combine_kernel merges the splits of one (sequence, head); with a
+//     single split the split kernel normalises and writes the output itself.
 #include <math.h>
 
 #include "common.h"
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const int32_t* __restrict__ sl, int Hq, int Hkv, int max_pages, int num_pages,
     int max_seq_len, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ seg,
     const int32_t* __restrict__ nseg, int max_seg, int n_split, float scale_log2,
-    float* __restrict__ part) {
+    float* __restrict__ part, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int LPR = D / 8;            // lanes per key row
   constexpr int RG = 64 / LPR;          // row groups per wave
   constexpr int NSLOT = 4 * RG;         // row groups per workgroup
@@ -239,12 +240,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       L += w * sm_l[r][x];
       Ov += w * sm_o[r][x][d];
     }
-    float* pp = part + (((size_t)b * Hq + h0 + x) * n_split + s) * (D + 2);
-    if (d == 0) {
-      pp[0] = M;
-      pp[1] = L;
+    if (n_split == 1) {
+      // a single split is the whole result: normalise here (the same
+      // arithmetic as combine_kernel with one partial) and skip the combine
+      const size_t bh = (size_t)b * Hq + h0 + x;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      out[bh * D + d] = f32_to_bf16(Ov * inv);
+      if (lse != nullptr && d == 0) lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      float* pp = part + (((size_t)b * Hq + h0 + x) * n_split + s) * (D + 2);
+      if (d == 0) {
+        pp[0] = M;
+        pp[1] = L;
+      }
+      pp[2 + d] = Ov;
     }
-    pp[2 + d] = Ov;
   }
 }
 
@@ -278,9 +288,13 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
 int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split) {
   if (n_split > 0) return n_split;
   const int items = mode == FSA_SEL_INDEX ? d.B * d.Hq : d.B * d.Hkv;
-  const int len = (mode == FSA_SEL_INDEX || mode == FSA_SEL_INDEX_KV) ? k : d.max_seq_len;
-  // aim for >= 2048 workgroups and >= 256 positions per split
-  int ns = (2048 + items - 1) / items;
+  const bool listed = mode == FSA_SEL_INDEX || mode == FSA_SEL_INDEX_KV;
+  const int len = listed ? k : d.max_seq_len;
+  // aim for >= 2048 workgroups (1024 for listed positions: a single split then
+  // writes the output itself, with no combine launch) and >= 256 positions
+  // per split
+  const int target = listed ? 1024 : 2048;
+  int ns = (target + items - 1) / items;
   const int cap = (len + 255) / 256;
   if (ns > cap) ns = cap;
   return ns < 1 ? 1 : ns;
@@ -304,12 +318,14 @@ static hipError_t launch_dec_d(const void* q, const void* kp, const void* vp, co
   if (mode == FSA_SEL_INDEX) {
     hipLaunchKernelGGL((decode_split_kernel<D, 1, FSA_SEL_INDEX>), dim3(d.B * d.Hq * ns),
                        dim3(kDecThreads), 0, st, Q, Kp, Vp, pt, sl, d.Hq, d.Hkv, d.max_pages,
-                       d.num_pages, d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part);
+                       d.num_pages, d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part,
+                       static_cast<uint16_t*>(out), lse);
   } else {
 #define FSA_DEC(GG, MM)                                                                        \
   hipLaunchKernelGGL((decode_split_kernel<D, GG, MM>), dim3(d.B * d.Hkv * ns), dim3(kDecThreads), \
                      0, st, Q, Kp, Vp, pt, sl, d.Hq, d.Hkv, d.max_pages, d.num_pages,           \
-                     d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part)
+                     d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part,                \
+                     static_cast<uint16_t*>(out), lse)
 #define FSA_DEC_G(GG)                         \
   if (G == GG) {                              \
     if (mode == FSA_SEL_SEGMENT)              \
@@ -324,7 +340,7 @@ static hipError_t launch_dec_d(const void* q, const void* kp, const void* vp, co
 #undef FSA_DEC
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || ns == 1) return e;
   hipLaunchKernelGGL(combine_kernel<D>, dim3(d.B * d.Hq), dim3(64), 0, st, part, ns,
                      static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
