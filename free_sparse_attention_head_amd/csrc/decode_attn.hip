@@ -33,7 +33,7 @@ namespace fsa {
 
 constexpr int kDecThreads = 256;
 constexpr int kMaxSeg = 64;     // segments per sequence kept in LDS
-constexpr int kRowBatch = 1024;  // listed positions resolved to pool rows at a time
+constexpr int kRowBatch = 1024;  // positions resolved to pool rows at a time
 
 template <int D, int NH, int MODE>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ float sm_o[4][NH][D];
   __shared__ int seg_lo[kMaxSeg], seg_pre[kMaxSeg + 1];
   __shared__ int s_nseg;
-  __shared__ uint32_t rows_lds[kRowBatch];  // listed modes: pool row of each position
+  __shared__ uint32_t rows_lds[kRowBatch];  // pool row of each position of the batch
 
   const int G = Hq / Hkv;
   const int s = blockIdx.x % n_split;
@@ -120,42 +120,53 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int32_t* idxr = LISTED ? idx + ((size_t)b * per_b + hh) * k : nullptr;
 
   // pool row of token tok, or kNoRow (out of range, or a bad page id: such
-  // tokens are skipped, never read)
+  // tokens are skipped, never read).  The page-table read is issued for every
+  // token (a clamped in-range entry), so that a thread's lookups can all be
+  // in flight together.
   constexpr uint32_t kNoRow = 0xffffffffu;
   auto row_of = [&](int tok) -> uint32_t {
-    if (tok < 0 || tok >= n) return kNoRow;
-    const int page = ptb[tok >> 4];
-    if (page < 0 || page >= num_pages) return kNoRow;
-    return ((uint32_t)page * (uint32_t)Hkv + (uint32_t)g) * 16u + (uint32_t)(tok & 15);
+    const int page = ptb[min(max(tok, 0), max(n - 1, 0)) >> 4];
+    const bool ok = (tok >= 0) & (tok < n) & (page >= 0) & (page < num_pages);
+    const uint32_t row = ((uint32_t)page * (uint32_t)Hkv + (uint32_t)g) * 16u + (uint32_t)(tok & 15);
+    // a select, not a branch, so that the next lookup's read can issue first
+    return __builtin_unpredictable(ok) ? row : kNoRow;
   };
-  // Listed modes resolve up to kRowBatch positions (index, then page id) to
-  // pool rows in LDS before streaming them, so the K/V loads of a step depend
-  // on no other global load.
-  for (int b0 = p0; b0 < p1; b0 += kRowBatch) {
-    const int b1 = LISTED ? min(p1, b0 + kRowBatch) : p1;
+  // token at list position pos
+  auto token_of = [&](int pos) -> int {
     if constexpr (LISTED) {
-      __syncthreads();  // the previous batch's rows have been read
-      for (int x = tid; x < b1 - b0; x += kDecThreads) rows_lds[x] = row_of(idxr[b0 + x]);
-      __syncthreads();
+      return idxr[pos];
+    } else if constexpr (MODE == FSA_SEL_SEGMENT) {
+      int x = 0;
+      while (x + 1 < s_nseg && seg_pre[x + 1] <= pos) ++x;
+      return seg_lo[x] + (pos - seg_pre[x]);
+    } else {
+      return pos;
     }
+  };
+  // Positions are resolved (index or segment, then page id) to pool rows
+  // kRowBatch at a time into LDS before they are streamed, so the K/V loads
+  // of a step depend on no other global load.
+  for (int b0 = p0; b0 < p1; b0 += kRowBatch) {
+    const int b1 = min(p1, b0 + kRowBatch);
+    __syncthreads();  // the previous batch's rows have been read
+    uint32_t rw[kRowBatch / kDecThreads];  // all of a thread's lookups in flight at once
+#pragma unroll
+    for (int u = 0; u < kRowBatch / kDecThreads; ++u) {
+      const int x = u * kDecThreads + tid;
+      const bool in_batch = x < b1 - b0;
+      const uint32_t r = row_of(token_of(in_batch ? b0 + x : b0));
+      rw[u] = in_batch ? r : kNoRow;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowBatch / kDecThreads; ++u) rows_lds[u * kDecThreads + tid] = rw[u];
+    __syncthreads();
     for (int base = b0; base < b1; base += NSLOT * RB) {
       uint4 kr[RB], vr[RB];
       bool ok[RB];
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int pos = base + slot * RB + r;
-        uint32_t row = kNoRow;
-        if (pos < b1) {
-          if constexpr (LISTED) {
-            row = rows_lds[pos - b0];
-          } else if constexpr (MODE == FSA_SEL_SEGMENT) {
-            int x = 0;
-            while (x + 1 < s_nseg && seg_pre[x + 1] <= pos) ++x;
-            row = row_of(seg_lo[x] + (pos - seg_pre[x]));
-          } else {
-            row = row_of(pos);
-          }
-        }
+        const uint32_t row = pos < b1 ? rows_lds[pos - b0] : kNoRow;
         ok[r] = row != kNoRow;
         if (ok[r]) {
           kr[r] = *reinterpret_cast<const uint4*>(kpool + (size_t)row * D + dl * 8);
@@ -196,7 +207,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         l_run[x] = l_run[x] * alpha + ls;
       }
     }
-    if constexpr (!LISTED) break;  // one pass over [p0, p1)
   }
 
   // ---- merge the row groups of each wave (lanes LPR apart hold the same d
