@@ -70,24 +70,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   // ---- this split's range of list positions
   int total;
   if constexpr (MODE == FSA_SEL_SEGMENT) {
-    if (tid == 0) {
+    // wave 0: lane x reads segment x (clipped to [0, n)); the non-empty ones
+    // are compacted in order with their exclusive prefix of lengths
+    static_assert(kMaxSeg == 64, "one segment per lane of a wave");
+    if (wave == 0) {
       int ns = nseg[b];
       ns = ns < 0 ? 0 : (ns > max_seg ? max_seg : ns);
       ns = ns > kMaxSeg ? kMaxSeg : ns;
-      int run = 0, c = 0;
-      for (int x = 0; x < ns; ++x) {
-        int a = seg[((size_t)b * max_seg + x) * 2], e = seg[((size_t)b * max_seg + x) * 2 + 1];
-        a = a < 0 ? 0 : a;
-        e = e > n ? n : e;
-        if (e > a) {
-          seg_lo[c] = a;
-          seg_pre[c] = run;
-          run += e - a;
-          ++c;
-        }
+      int a = 0, len = 0;
+      if (l < ns) {
+        a = max(seg[((size_t)b * max_seg + l) * 2], 0);
+        len = max(min(seg[((size_t)b * max_seg + l) * 2 + 1], n) - a, 0);
       }
-      seg_pre[c] = run;
-      s_nseg = c;
+      const uint64_t valid = __ballot(len > 0);
+      const int rank = __popcll(valid & ((1ull << l) - 1ull));
+      const int inc = wave_incl_scan(len);
+      if (len > 0) {
+        seg_lo[rank] = a;
+        seg_pre[rank] = inc - len;
+      }
+      if (l == 63) {
+        seg_pre[__popcll(valid)] = inc;
+        s_nseg = __popcll(valid);
+      }
     }
     __syncthreads();
     total = seg_pre[s_nseg];
