@@ -15,9 +15,12 @@ One step runs every row of the hot path once over resident synthetic inputs:
     (4 sinks + 1024 window) masks, caches flushed before each small mode.
 Outside the timed steps: own dense baselines, and the attention kernel at 3%
 and 12% density and with the band + sink blocks only on the 128K prompt, and on
-the 32K prompt with 64-token blocks at 10%, and the Kascade group with one
-pooled index set per KV head shared by its query heads (skip with --no-sweep).
-Kernel times (medians) come from HIP events on the launch stream.  The headline value
+the 32K prompt with 64-token blocks at 10%, the Kascade group with one
+pooled index set per KV head shared by its query heads, the anchor layer's
+block lists reused by three later prefill layers, and the selectors compared
+at matched density on the 32K prompt (skip all with --no-sweep).
+Kernel times (medians, 50 timed steps after 5 warm-up steps by default) come
+from HIP events on the launch stream.  The headline value
 is the sparse prefill attention kernel's effective TFLOP/s on executed
 blocks (4*T*T*D FLOP per executed query-block/key-block pair); decode is
 reported as admitted KV bytes per second.
@@ -112,7 +115,7 @@ def make_prefill(fsa, workloads, density, seed=1002, P=None):
                                                       device="cuda"))
 
 
-def time_attention(fsa, pf, P, reps=5):
+def time_attention(fsa, pf, P, reps=20):
     """Median / min of `reps` attention launches (after 2 warm-ups) on pf's selection."""
     tm = Timer()
     for _ in range(2 + reps):
@@ -129,7 +132,7 @@ def time_attention(fsa, pf, P, reps=5):
             "frac_peak": round(flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
-def decode_kv_shared(fsa, dc, reps=5):
+def decode_kv_shared(fsa, dc, reps=20):
     """The per-KV-head Kascade variant on the decode group's inputs, outside
     the timed steps: pooled top-k per KV head, then the four layers attending
     at the shared indices (each K/V row read once for the G query heads)."""
@@ -498,8 +501,8 @@ def copy_probe():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--density", type=float, default=0.06)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
