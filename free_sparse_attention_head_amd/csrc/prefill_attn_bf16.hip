@@ -134,13 +134,27 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   const uint16_t* Kb = K + ((size_t)b * S * Hkv + g) * D;
   const uint16_t* Vb = V + ((size_t)b * S * Hkv + g) * D;
 
-  // Q tile -> registers (MFMA B operand, lane = query row)
-  bf16x8 qf[D / 16];
+  // Each wave owns a 32-row staging region in the K ring (free before the
+  // first K/V copies and again after the last S step): its Q rows come in
+  // through it and its O rows go out through it, so that every global access
+  // of either moves whole token rows (a wave's 32 rows are Hq * D elements
+  // apart in HBM; read or written straight from the MFMA layout, each
+  // instruction would touch 32 rows at 32 or 16 bytes apart).
+  static_assert(Tr::NW <= 2 * NKT, "two K tiles hold every wave's 32 rows");
+  constexpr int RPI = Tr::RPI;
+  unsigned char* stage = (wave / NKT ? kb1 : kb0) + (wave % NKT) * 32 * ROWB;
+  // a wave-uniform base plus a 32-bit per-lane byte offset (row r, 16-byte slot)
+  const uint32_t tok_bytes = (uint32_t)(Hq * D) * sizeof(uint16_t);  // token to token
+  const size_t row0 = ((size_t)b * S + (size_t)i * BLK + wave * 32) * Hq * D + (size_t)h * D;
+  auto row_ofs = [&](int r, int slot) { return (uint32_t)r * tok_bytes + (uint32_t)slot * 16u; };
+  // Q rows -> staging region (row-major, the K tile's slot swizzle)
   {
-    const uint16_t* qp = Q + (((size_t)b * S + (size_t)i * BLK + qrow) * Hq + h) * D;
+    const char* qsrc = reinterpret_cast<const char*>(Q + row0);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kk * 16 + lg * 8));
+    for (int m = 0; m < 32 / RPI; ++m) {
+      const int r = m * RPI + l / SLOTS, sl = l % SLOTS;
+      copy16_to_lds(qsrc + row_ofs(r, sl ^ k_swz<SLOTS>(r)), stage + m * 1024);
+    }
   }
 
   // the row's causal key blocks, compacted in order into LDS
@@ -158,6 +172,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   }
   __syncthreads();
   const int nchunks = nvalid * NCH;
+
+  // staged Q -> registers (MFMA B operand, lane = query row), read like a K
+  // fragment; the barrier keeps the ring untouched until every wave has it
+  const int kslot_x = lq & (SLOTS - 1);  // K row swizzle of rows lq, lq+32
+  // K fragment of MFMA step kk for key row rowp (two 8-element halves: lg)
+  auto kfrag = [&](const unsigned char* rowp, int kk) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                          rowp + (((2 * kk + lg) ^ kslot_x) * 16)));
+  };
+  bf16x8 qf[D / 16];
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) qf[kk] = kfrag(stage + lq * ROWB, kk);
+  __syncthreads();
 
   // HBM -> LDS copy of chunk c into tile buffer kt: a wave-uniform source
   // base plus fixed per-lane byte offsets (row, swizzled slot) and a
@@ -199,19 +227,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   // per-lane LDS offsets of the fragment reads
-  const int kslot_x = lq & (SLOTS - 1);      // K row swizzle of rows lq, lq+32
   const int li = l & 15, q16 = (l >> 4) & 1;  // transposing-read lane coordinates
   const int vrow = lg * 4 + (li >> 2);
   const int vcol_b = q16 * 32 + 8 * (li & 3);  // byte column inside a 64-byte dt stripe
   const int vphys_x = v_swz<SLOTS>(li >> 2);   // V row swizzle (row % 4 == li >> 2)
   constexpr int NKK = D / 16;                  // MFMA k-steps of S
   constexpr int NDT = D / 32, NM = (KC / 16) * NDT;  // MFMAs of PV
-
-  // K fragment of MFMA step kk for key row rowp (two 8-element halves: lg)
-  auto kfrag = [&](const unsigned char* rowp, int kk) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                          rowp + (((2 * kk + lg) ^ kslot_x) * 16)));
-  };
 
   // Causal mask (diagonal block only), row max in raw units and the lazy
   // rescale for chunk c; returns the exponent offset of P.  Register r of
@@ -398,20 +419,35 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     }
   }
 
-  // ---- epilogue: O = O^T / l, LSE
+  // ---- epilogue: O = O^T / l, LSE.  The last step reads no K tile and every
+  // wave has passed its barrier, so the staging regions are free again: the
+  // wave writes its rows there (lane: 4 values of row lq at d0) and stores
+  // them back as whole rows.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int t = i * BLK + qrow;
-  uint16_t* op = O + (((size_t)b * S + t) * Hq + h) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = dt * 32 + rg * 8 + lg * 4;
-      *reinterpret_cast<uint2*>(op + d0) =
+      const int slot = dt * 4 + rg;  // 16-byte slot of d0 = dt*32 + rg*8 (+ lg*4)
+      *reinterpret_cast<uint2*>(stage + lq * ROWB + ((slot ^ kslot_x) * 16) + lg * 8) =
           make_uint2(pack_bf16x2(oacc[dt][rg * 4] * inv, oacc[dt][rg * 4 + 1] * inv),
                      pack_bf16x2(oacc[dt][rg * 4 + 2] * inv, oacc[dt][rg * 4 + 3] * inv));
     }
+  // the region is this wave's alone: LDS serves a wave's accesses in order
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  char* odst = reinterpret_cast<char*>(O + row0);
+  // the lane id afresh, so that no offset of the Q copies is kept (in
+  // registers the main loop needs) until here
+  const int le = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+#pragma unroll
+  for (int m = 0; m < 32 / RPI; ++m) {
+    const int r = m * RPI + le / SLOTS, sl = le % SLOTS;
+    const uint4 w = *reinterpret_cast<const uint4*>(stage + r * ROWB + ((sl ^ k_swz<SLOTS>(r)) * 16));
+    *reinterpret_cast<uint4*>(odst + row_ofs(r, sl)) = w;
+  }
   if (LSE != nullptr && lg == 0)
     LSE[((size_t)b * Hq + h) * S + t] =
         l_tot > 0.f ? (m_run * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
