@@ -17,8 +17,9 @@ Outside the timed steps: own dense baselines, and the attention kernel at 3%
 and 12% density and with the band + sink blocks only on the 128K prompt, and on
 the 32K prompt with 64-token blocks at 10%, the Kascade group with one
 pooled index set per KV head shared by its query heads, the anchor layer's
-block lists reused by three later prefill layers, and the selectors compared
-at matched density on the 32K prompt (skip all with --no-sweep).
+block lists reused by three later prefill layers, and the selectors (and the
+ideal block top-k) compared at matched density on the 32K prompt for 64- and
+128-token blocks at 5, 10 and 20% (skip all with --no-sweep).
 Kernel times (medians, 50 timed steps after 5 warm-up steps by default) come
 from HIP events on the launch stream.  The headline value
 is the sparse prefill attention kernel's effective TFLOP/s on executed
@@ -192,37 +193,91 @@ def spike_recall(sel, spikes, device="cuda"):
     return round(((words >> (j % 32)) & 1).float().mean().item(), 4)
 
 
-def selector_quality(fsa, workloads, p32, density=0.10):
-    """Selectors compared at matched density on the 32K prompt with 64-token
-    blocks (RBS-Attention post, "Experimental data": actual retention, matched
-    density).  Retention of token t = the share of its causal softmax mass on
-    admitted keys = exp(lse_mask(t) - lse_dense(t)), both from the attention
-    kernel.  Spike recall: planted spikes whose block the selector keeps, on
-    this prompt (spikes of norm 6) and on one with spikes of norm 2 sqrt(D),
-    which then dominate the block radius."""
-    P = PREFILL_32K
-    T = P["T"]
+def block_mass(fsa, q, k, v, T, lse_d):
+    """Mean causal softmax mass of each query block i on each key block j, per
+    query head: mass[h, i, j] = mean over the T queries t of block i of
+    exp(lse_j(t) - lse_dense(t)), where lse_j comes from a sparse_prefill_attn
+    launch whose every row i >= j lists block j alone (rows i < j list
+    nothing and get mass 0).  One launch per key block; B = 1."""
+    _, S, Hq, _ = q.shape
+    nB = S // T
+    dev = q.device
+    mass = torch.zeros((Hq, nB, nB), dtype=torch.float32, device=dev)
+    idx = torch.zeros((1, Hq, nB, nB), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, Hq, nB), dtype=torch.int32, device=dev)
+    ar = torch.arange(nB, device=dev)
+    lse = torch.empty((1, Hq, S), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    for j in range(nB):
+        idx[..., 0] = j
+        cnt.copy_((ar >= j).to(torch.int32).view(1, 1, nB).expand(1, Hq, nB))
+        fsa.sparse_prefill_attn(q, k, v, T, idx, cnt, out=o, lse=lse)
+        mass[:, :, j] = torch.exp(lse[0] - lse_d[0]).view(Hq, nB, T).mean(-1)
+    return mass
+
+
+def ideal_selection(mass, cnt):
+    """Per row, the cnt[h, i] key blocks of largest mass (ties to the lower
+    block index), as ascending block lists: the mask that keeps the most mass
+    at those counts (no block selector can keep more)."""
+    Hq, nB, _ = mass.shape
+    order = torch.sort(-mass, dim=-1, stable=True).indices          # best block first
+    rank_ok = torch.arange(nB, device=mass.device).view(1, 1, nB) < cnt[0].unsqueeze(-1)
+    keep = torch.zeros_like(mass, dtype=torch.bool).scatter_(-1, order, rank_ok)
+    ar = torch.arange(nB, device=mass.device).view(1, 1, nB)
+    lists = torch.sort(torch.where(keep, ar, nB), dim=-1).values.clamp_(max=nB - 1)
+    return lists.to(torch.int32).unsqueeze(0).contiguous(), cnt
+
+
+def selector_quality(fsa, workloads, p32, densities=(0.05, 0.10, 0.20), blocks=(64, 128)):
+    """Selectors compared at matched density on the 32K prompt (RBS-Attention
+    post, "Experimental data": actual retention, matched density), for each
+    key/query block size and target density: the merged two-branch selector,
+    each branch alone, and the ideal block top-k at the merged selector's
+    per-row counts.  Retention of token t = the share of its causal softmax
+    mass on admitted keys = exp(lse_mask(t) - lse_dense(t)), both from the
+    attention kernel.  Spike recall (64-token blocks, 10%): planted spikes
+    whose block the selector keeps, on this prompt (spikes of norm 6) and on
+    one with spikes of norm 2 sqrt(D), which then dominate the block radius."""
+    names = {"both": "merged", "centroid": "centroid_only", "rescue": "rescue_only"}
     q, k, v = p32["q"], p32["k"], p32["v"]
-    _, lse_d = fsa.sparse_prefill_attn(q, k, v, T)
-    res = {"density_target": density, "retention_mean": {}, "retention_p10": {},
-           "spike_recall_norm6": {}, "spike_recall_norm2sqrtD": {}, "density": {}}
-    alt = workloads.prefill_inputs(1, P["S"], P["Hq"], P["Hkv"], P["D"], T, model="lowrank",
+    res = {"retention_mean": {}, "retention_p10": {}, "density": {},
+           "spike_recall_norm6": {}, "spike_recall_norm2sqrtD": {}}
+    for T in blocks:
+        P = dict(PREFILL_32K, T=T)
+        c, r = (p32["c"], p32["r"]) if T == PREFILL_32K["T"] else fsa.block_stats(k, T)
+        _, lse_d = fsa.sparse_prefill_attn(q, k, v, T)
+        mass = block_mass(fsa, q, k, v, T, lse_d)
+        for density in densities:
+            key = f"T{T}_d{int(round(density * 100)):02d}"
+            rm, rp, dn = {}, {}, {}
+            for br in ("both", "centroid", "rescue"):
+                _, dens, sel = tune_selector(fsa, q, c, r, P, density, branches=br)
+                lists = {names[br]: (sel["block_idx"], sel["block_cnt"])}
+                if br == "both":
+                    lists["ideal"] = ideal_selection(mass, sel["block_cnt"])
+                for name, (bi, bc) in lists.items():
+                    _, lse_m = fsa.sparse_prefill_attn(q, k, v, T, bi, bc)
+                    ret = torch.exp(lse_m - lse_d).flatten()
+                    rm[name] = round(ret.mean().item(), 4)
+                    rp[name] = round(torch.quantile(ret, 0.10).item(), 4)
+                    dn[name] = round(dens, 4)
+                    del lse_m, ret
+                if T == PREFILL_32K["T"] and abs(density - 0.10) < 1e-9:
+                    res["spike_recall_norm6"][names[br]] = spike_recall(dict(sel, T=T), p32["spikes"])
+                del sel, lists
+            res["retention_mean"][key], res["retention_p10"][key], res["density"][key] = rm, rp, dn
+        del mass, lse_d
+        torch.cuda.empty_cache()
+    P = PREFILL_32K
+    alt = workloads.prefill_inputs(1, P["S"], P["Hq"], P["Hkv"], P["D"], P["T"], model="lowrank",
                                    spike_scale=2 * math.sqrt(P["D"]), seed=1011, device="cuda")
-    c2, r2 = fsa.block_stats(alt["k"], T)
+    c2, r2 = fsa.block_stats(alt["k"], P["T"])
     for br in ("both", "centroid", "rescue"):
-        _, dens, sel = tune_selector(fsa, q, p32["c"], p32["r"], P, density, branches=br)
-        _, lse_m = fsa.sparse_prefill_attn(q, k, v, T, sel["block_idx"], sel["block_cnt"])
-        ret = torch.exp(lse_m - lse_d).flatten()
-        name = {"both": "merged", "centroid": "centroid_only", "rescue": "rescue_only"}[br]
-        res["density"][name] = round(dens, 4)
-        res["retention_mean"][name] = round(ret.mean().item(), 4)
-        res["retention_p10"][name] = round(torch.quantile(ret, 0.10).item(), 4)
-        res["spike_recall_norm6"][name] = spike_recall(dict(sel, T=T), p32["spikes"])
-        del sel, lse_m, ret
-        _, _, sel2 = tune_selector(fsa, alt["q"], c2, r2, P, density, branches=br)
-        res["spike_recall_norm2sqrtD"][name] = spike_recall(dict(sel2, T=T), alt["spikes"])
+        _, _, sel2 = tune_selector(fsa, alt["q"], c2, r2, P, 0.10, branches=br)
+        res["spike_recall_norm2sqrtD"][names[br]] = spike_recall(dict(sel2, T=P["T"]), alt["spikes"])
         del sel2
-    del alt, c2, r2, lse_d
+    del alt, c2, r2
     torch.cuda.empty_cache()
     return res
 

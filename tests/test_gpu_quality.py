@@ -118,3 +118,42 @@ def test_spike_recall_at_matched_density():
     print(f"[quality] spike recall {recall}")
     assert recall["rescue"] == 1.0
     assert recall["merged"] > recall["centroid"]
+
+
+def test_block_mass_and_ideal_selection_match_oracle():
+    """The GPU harness behind the selector-quality report: per-block mass from
+    single-block attention launches equals the oracle's mean softmax mass of
+    each query block on each key block, and the ideal selection it builds at a
+    selector's per-row counts keeps as much oracle mass as the oracle's ideal
+    set (the sets may differ only between blocks of equal mass up to the
+    rounding tolerance)."""
+    import bench
+    import free_sparse_attention_head_amd as fsa
+    inp, sel, _ = case()
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    _, lse_d = fsa.sparse_prefill_attn(q, k, v, T)
+    mass = bench.block_mass(fsa, q, k, v, T, lse_d).cpu().double().numpy()   # [Hq, nB, nB]
+    cnt = sel["merged"]["block_cnt"].cuda()
+    idx_i, cnt_i = bench.ideal_selection(torch.from_numpy(mass).float().cuda(), cnt)
+    idx_i, cnt_i = idx_i.cpu().numpy(), cnt_i.cpu().numpy()
+    q64, k64 = workloads.to_f64(inp["q"]), workloads.to_f64(inp["k"])
+    nB = S // T
+    scale = 1 / math.sqrt(D)
+    rows = list(range(0, nB, 5))
+    worst = 0.0
+    for h in (0, Hq - 1):
+        g = h // (Hq // Hkv)
+        ref = oracle.token_block_mass(q64[0, :, h], k64[0, :, g], T, scale, rows)
+        ideal = oracle.ideal_rows(q64[0, :, h], k64[0, :, g], T, scale, cnt_i[0, h], rows)
+        for i in rows:
+            want = ref[i].mean(axis=0)
+            err = np.abs(mass[h, i, :i + 1] - want).max()
+            worst = max(worst, err)
+            assert err <= TOL_RET, (h, i, err)
+            assert np.all(mass[h, i, i + 1:] == 0.0)
+            got_blocks = idx_i[0, h, i, :cnt_i[0, h, i]]
+            assert np.all(np.diff(got_blocks) > 0) and got_blocks.max(initial=0) <= i
+            kept = want[got_blocks].sum()
+            best = ideal[i][1].mean()
+            assert kept >= best - 2 * TOL_RET, (h, i, kept, best)
+    print(f"[quality] block mass max-abs difference GPU vs oracle {worst:.2e}")
