@@ -11,12 +11,13 @@
 //   2. centroid_score_kernel: Sc[b,h,i,j] = qbar_i . c_j for j <= i, as 64x64
 //      fp32 register-blocked tiles of the lower triangle (LDS-staged operands,
 //      4x4 outputs per thread, sequential accumulation over d).
-//   3. select_rows_kernel: one workgroup per row (b,h,i): Sr = Sc + ||qbar||*r,
-//      exact top-k of each branch by a 4-pass 8-bit radix select on
-//      order-preserving keys held in registers (ties go to the lower block
-//      index through an exclusive scan of the equal-key flags), union with
-//      the forced sink/band blocks, compaction into an ascending block list
-//      with a workgroup scan, and the bitmask row.
+//   3. select_rows_kernel: one wave per row (b,h,i): Sr = Sc + ||qbar||*r,
+//      exact top-k of each branch by a radix select in 8-bit digits on
+//      order-preserving keys held in registers (per-wave LDS histogram,
+//      early stop once the k-th key's bin is kept whole; remaining ties go to
+//      the lower block index through a wave scan of the equal-key flags),
+//      union with the forced sink/band blocks, compaction into an ascending
+//      block list with a wave scan, and the bitmask row.
 #include <math.h>
 
 #include "common.h"
@@ -120,85 +121,96 @@ __global__ __launch_bounds__(256) void centroid_score_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------- selection
-struct SelShared {
-  uint32_t hist[256];
-  int misc[2];
-  int scan[17];
-  uint32_t words[128];
-  float qn;
+// One wave per row (b, h, i), four rows per workgroup; no workgroup barriers.
+// Lane l holds the E consecutive entries j = l*E .. l*E+E-1 of the row, so
+// lane order is index order and a wave prefix sum ranks entries by index.
+constexpr int kRowsPerWg = 4;
+
+struct __align__(16) WaveShared {
+  uint32_t hist[256];   // radix histogram of one pass
+  uint32_t words[128];  // mask row (nB <= 4096)
 };
 
-// Exact k-th largest key among the valid entries (4 passes of 8-bit digits).
-// Returns the key value K* and how many entries equal to K* are still needed.
-template <int E>
-__device__ void radix_kth(const uint32_t (&key)[E], const bool (&valid)[E], int k, SelShared& sh,
-                          uint32_t& kstar, int& need_eq) {
-  uint32_t prefix = 0, pmask = 0;
-  int kk = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int q = threadIdx.x; q < 256; q += blockDim.x) sh.hist[q] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (valid[e] && (key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int l = threadIdx.x;
-      const int c0 = sh.hist[255 - 4 * l], c1 = sh.hist[254 - 4 * l];
-      const int c2 = sh.hist[253 - 4 * l], c3 = sh.hist[252 - 4 * l];
-      const int s = c0 + c1 + c2 + c3;
-      const int inc = wave_incl_scan(s);
-      const int exc = inc - s;
-      if (exc < kk && kk <= inc) {
-        int above = exc, d;
-        if (kk <= above + c0) {
-          d = 255 - 4 * l;
-        } else if (kk <= above + c0 + c1) {
-          above += c0;
-          d = 254 - 4 * l;
-        } else if (kk <= above + c0 + c1 + c2) {
-          above += c0 + c1;
-          d = 253 - 4 * l;
-        } else {
-          above += c0 + c1 + c2;
-          d = 252 - 4 * l;
-        }
-        sh.misc[0] = d;
-        sh.misc[1] = above;
-      }
-    }
-    __syncthreads();
-    kk -= sh.misc[1];
-    prefix |= (uint32_t)sh.misc[0] << shift;
-    pmask |= 255u << shift;
-  }
-  kstar = prefix;
-  need_eq = kk;
+// the wave's own LDS accesses are served in order; this keeps the compiler
+// from moving them across the point
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
-// Top-k membership flags, ties to the lower index (entries are contiguous per
-// thread, so a workgroup exclusive scan of equal-key counts ranks ties in
-// index order).
+// Top-k membership of the valid entries, largest keys first, ties to the
+// lower index: a radix select of the k-th largest key in 8-bit digits from
+// the top (histogram of the entries still matching the digits fixed so far,
+// counted from the largest bin down), stopping early once the k-th key's bin
+// is kept whole; the remaining ties are ranked by index with a wave scan.
 template <int E>
-__device__ void topk_flags(const uint32_t (&key)[E], const bool (&valid)[E], int k, SelShared& sh,
-                           bool (&sel)[E]) {
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], const bool (&valid)[E], int k,
+                                          int n, WaveShared& sh, bool (&sel)[E]) {
+  const int l = lane_id();
+  if (k >= n) {  // every valid entry
+#pragma unroll
+    for (int e = 0; e < E; ++e) sel[e] = valid[e];
+    return;
+  }
   if (k <= 0) {
 #pragma unroll
     for (int e = 0; e < E; ++e) sel[e] = false;
     return;
   }
-  uint32_t ks;
-  int need;
-  radix_kth<E>(key, valid, k, sh, ks, need);
+  uint32_t prefix = 0, pmask = 0;
+  int kk = k;  // entries still to take among those matching prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    reinterpret_cast<uint4*>(sh.hist)[l] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_fence();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (valid[e] && (key[e] & pmask) == prefix)
+        __hip_atomic_fetch_add(&sh.hist[(key[e] >> shift) & 255u], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+    wave_lds_fence();
+    // lane l: bins 255-4l (c0) down to 252-4l (c3); counts from the top
+    const uint4 h4 = reinterpret_cast<const uint4*>(sh.hist)[63 - l];
+    const int c0 = h4.w, c1 = h4.z, c2 = h4.y, c3 = h4.x;
+    const int sum = c0 + c1 + c2 + c3;
+    const int inc = wave_incl_scan(sum);
+    const int exc = inc - sum;
+    const bool mine = exc < kk && kk <= inc;
+    int d, above, cd;
+    {
+      int a = exc;
+      if (kk <= a + c0) {
+        d = 255 - 4 * l, cd = c0;
+      } else if (kk <= a + c0 + c1) {
+        a += c0, d = 254 - 4 * l, cd = c1;
+      } else if (kk <= a + c0 + c1 + c2) {
+        a += c0 + c1, d = 253 - 4 * l, cd = c2;
+      } else {
+        a += c0 + c1 + c2, d = 252 - 4 * l, cd = c3;
+      }
+      above = a;
+    }
+    const int src = __builtin_ctzll(__ballot(mine));  // exactly one lane (kk <= total)
+    d = __shfl(d, src, 64);
+    above = __shfl(above, src, 64);
+    cd = __shfl(cd, src, 64);
+    kk -= above;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 255u << shift;
+    if (cd == kk) {  // the k-th key's bin is kept whole
+#pragma unroll
+      for (int e = 0; e < E; ++e) sel[e] = valid[e] && (key[e] & pmask) >= prefix;
+      return;
+    }
+  }
+  // prefix is the k-th largest key; kk of its copies are kept, lowest index first
   int neq = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) neq += (valid[e] && key[e] == ks) ? 1 : 0;
-  int tot;
-  int rank = block_excl_scan(neq, sh.scan, &tot);
+  for (int e = 0; e < E; ++e) neq += (valid[e] && key[e] == prefix) ? 1 : 0;
+  int rank = wave_incl_scan(neq) - neq;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    bool eq = valid[e] && key[e] == ks;
-    sel[e] = valid[e] && (key[e] > ks || (eq && rank < need));
+    const bool eq = valid[e] && key[e] == prefix;
+    sel[e] = valid[e] && (key[e] > prefix || (eq && rank < kk));
     rank += eq ? 1 : 0;
   }
 }
@@ -211,29 +223,25 @@ __device__ __forceinline__ int k_of(double p, int n) {
 }
 
 template <int E>
-__global__ __launch_bounds__(256) void select_rows_kernel(
+__global__ __launch_bounds__(64 * kRowsPerWg) void select_rows_kernel(
     const float* __restrict__ qbar, const float* __restrict__ sc, const float* __restrict__ rad,
     uint32_t* __restrict__ mask, int32_t* __restrict__ bidx, int32_t* __restrict__ bcnt,
-    float* __restrict__ score_r, int Hq, int Hkv, int nB, int D, double p_c, double p_r,
-    int band, int sink) {
-  __shared__ SelShared sh;
-  const int row = blockIdx.x;  // (b*Hq + h)*nB + i
+    float* __restrict__ score_r, int rows, int Hq, int Hkv, int nB, int D, double p_c,
+    double p_r, int band, int sink) {
+  __shared__ WaveShared shw[kRowsPerWg];
+  const int wave = threadIdx.x >> 6, l = lane_id();
+  const int row = blockIdx.x * kRowsPerWg + wave;  // (b*Hq + h)*nB + i
+  if (row >= rows) return;
+  WaveShared& sh = shw[wave];
   const int i = row % nB, bh = row / nB, h = bh % Hq, b = bh / Hq;
   const int g = h / (Hq / Hkv);
   const int n = i + 1;
-  const int t = threadIdx.x;
   const int nw = (nB + 31) / 32;
 
-  if (t < 64) {
-    const float* qr = qbar + (size_t)row * D;
-    float s = 0.f;
-    for (int d = t; d < D; d += 64) s += qr[d] * qr[d];
-    s = wave_sum(s);
-    if (t == 0) sh.qn = sqrtf(s);
-  }
-  for (int w = t; w < nw; w += blockDim.x) sh.words[w] = 0u;
-  __syncthreads();
-  const float qn = sh.qn;
+  float s2 = 0.f;
+  const float* qr = qbar + (size_t)row * D;
+  for (int d = l; d < D; d += 64) s2 += qr[d] * qr[d];
+  const float qn = sqrtf(wave_sum(s2));
 
   uint32_t kc[E], kr[E];
   bool valid[E];
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(
   const float* rr = rad + ((size_t)b * Hkv + g) * nB;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = t * E + e;
+    const int j = l * E + e;
     valid[e] = j < n;
     const float s = valid[e] ? scr[j] : 0.f;
     const float r = valid[e] ? fmaf(qn, rr[j], s) : 0.f;
@@ -250,32 +258,37 @@ __global__ __launch_bounds__(256) void select_rows_kernel(
     if (score_r != nullptr && valid[e]) score_r[(size_t)row * nB + j] = r;
   }
   bool selc[E], selr[E];
-  topk_flags<E>(kc, valid, k_of(p_c, n), sh, selc);
-  topk_flags<E>(kr, valid, k_of(p_r, n), sh, selr);
+  wave_topk<E>(kc, valid, k_of(p_c, n), n, sh, selc);
+  wave_topk<E>(kr, valid, k_of(p_r, n), n, sh, selr);
 
   int cnt = 0;
   bool m[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = t * E + e;
+    const int j = l * E + e;
     const bool forced = (j < sink) || (band > 0 && j > i - band);
     m[e] = valid[e] && (selc[e] || selr[e] || forced);
     cnt += m[e] ? 1 : 0;
   }
-  int tot;
-  int pos = block_excl_scan(cnt, sh.scan, &tot);
+  const int inc = wave_incl_scan(cnt);
+  int pos = inc - cnt;
+  const int tot = __shfl(inc, 63, 64);
   int32_t* lst = bidx + (size_t)row * nB;
+  // mask bits of this lane's entries, gathered into 32-bit words in LDS
+  for (int w = l; w < nw; w += 64) sh.words[w] = 0u;
+  wave_lds_fence();
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (m[e]) {
-      const int j = t * E + e;
+      const int j = l * E + e;
       lst[pos++] = j;
-      atomicOr(&sh.words[j >> 5], 1u << (j & 31));
+      __hip_atomic_fetch_or(&sh.words[j >> 5], 1u << (j & 31), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WAVEFRONT);
     }
   }
-  if (t == 0) bcnt[row] = tot;
-  __syncthreads();
-  for (int w = t; w < nw; w += blockDim.x) mask[(size_t)row * nw + w] = sh.words[w];
+  if (l == 0) bcnt[row] = tot;
+  wave_lds_fence();
+  for (int w = l; w < nw; w += 64) mask[(size_t)row * nw + w] = sh.words[w];
 }
 
 size_t select_ws_bytes(const PrefillDims& d) {
@@ -308,20 +321,25 @@ hipError_t launch_select_blocks(bool f32, const void* q, const float* cen, const
                      sc, d.Hq, d.Hkv, nB, d.D, tiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid(d.B * d.Hq * nB);
-#define FSA_SEL(EE)                                                                            \
-  hipLaunchKernelGGL(select_rows_kernel<EE>, grid, dim3(256), 0, st, qbar, sc, rad, mask, bidx, \
-                     bcnt, score_r, d.Hq, d.Hkv, nB, d.D, p_c, p_r, band, sink)
-  if (nB <= 256)
+  const int rows = d.B * d.Hq * nB;
+  const dim3 grid((rows + kRowsPerWg - 1) / kRowsPerWg);
+#define FSA_SEL(EE)                                                                           \
+  hipLaunchKernelGGL(select_rows_kernel<EE>, grid, dim3(64 * kRowsPerWg), 0, st, qbar, sc, rad, \
+                     mask, bidx, bcnt, score_r, rows, d.Hq, d.Hkv, nB, d.D, p_c, p_r, band, sink)
+  if (nB <= 64)
     FSA_SEL(1);
-  else if (nB <= 512)
+  else if (nB <= 128)
     FSA_SEL(2);
-  else if (nB <= 1024)
+  else if (nB <= 256)
     FSA_SEL(4);
-  else if (nB <= 2048)
+  else if (nB <= 512)
     FSA_SEL(8);
-  else
+  else if (nB <= 1024)
     FSA_SEL(16);
+  else if (nB <= 2048)
+    FSA_SEL(32);
+  else
+    FSA_SEL(64);
 #undef FSA_SEL
   return hipGetLastError();
 }

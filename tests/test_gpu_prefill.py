@@ -209,3 +209,84 @@ def test_anchor_selection_reused_by_a_later_layer():
                                                1 / math.sqrt(D))
         assert np.abs(o[0, :, h].double().numpy() - ref).max() <= TOL_BF16
         assert np.abs(lse[0, h].double().numpy() - ref_lse).max() <= 10 * TOL_BF16
+
+
+def _exact_rows(res, pc, pr, band, sink, nB, rows=None):
+    """Every checked mask row equals the selection rule applied exactly to the
+    kernel's own fp32 scores: top k_of(p, i + 1) of each branch with ties to
+    the lower block index (oracle.topk on the same values), union the forced
+    blocks.  No near-threshold allowance: the same numbers, the same rule."""
+    B, Hq = res["block_cnt"].shape[:2]
+    rows = range(nB) if rows is None else rows
+    bad = 0
+    for b in range(B):
+        for h in range(Hq):
+            sc = res["score_c"][b, h].double().numpy()
+            sr = res["score_r"][b, h].double().numpy()
+            gm = lists_to_mask(res["block_idx"][b, h].numpy(), res["block_cnt"][b, h].numpy(), nB)
+            bm = bits_to_mask(res["mask"][b, h].numpy(), nB)
+            for i in rows:
+                n = i + 1
+                want = np.zeros(nB, dtype=bool)
+                for p, s in ((pc, sc), (pr, sr)):
+                    kk = oracle.k_of(p, n)
+                    if kk > 0:
+                        want[oracle.topk(s[i, :n], kk)[0]] = True
+                want[:min(sink, n)] = True
+                if band > 0:
+                    want[max(0, i - band + 1):n] = True
+                bad += int(not np.array_equal(gm[i], want)) + int(not np.array_equal(bm[i], want))
+    assert bad == 0, bad
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_selection_is_exact_top_k_of_kernel_scores(name):
+    B, S, Hq, Hkv, D, T, dt, model, nsp, pc, pr, band, sink = CASES[name]
+    _exact_rows(run(name), pc, pr, band, sink, S // T)
+
+
+def _select_on(q, k, T, pc, pr, band=0, sink=0):
+    import free_sparse_attention_head_amd as fsa
+    c, r = fsa.block_stats(k, T)
+    sel = fsa.select_blocks(q, c, r, T, pc, pr, band, sink, want_scores=True)
+    torch.cuda.synchronize()
+    return {x: y.cpu() for x, y in sel.items() if y is not None}
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "two_valued", "sparse_distinct"])
+def test_selection_ties(kind):
+    """Rows whose scores tie massively: every key the same (every score of a
+    row equal, radius 0), keys alternating between two vectors block by block
+    (two score values per row, the k-th inside a run of ties), and one
+    distinct key block among equal ones.  nB = 200: several mask words, a
+    ragged tail, four entries per lane."""
+    S, Hq, Hkv, D, T = 12800, 2, 1, 64, 64
+    nB = S // T
+    print(f"[select ties {kind}] S={S} T={T} nB={nB}", flush=True)
+    g = torch.Generator().manual_seed(77)
+    q = torch.randn((1, S, Hq, D), generator=g)
+    base = torch.randn(D, generator=g)
+    other = torch.randn(D, generator=g)
+    k = base.expand(1, S, Hkv, D).clone()
+    if kind == "two_valued":
+        blk = torch.arange(S) // T
+        k[0, blk % 2 == 1, 0] = other
+    elif kind == "sparse_distinct":
+        k[0, 37 * T:38 * T, 0] = other
+    q, k = q.to(torch.bfloat16).cuda(), k.to(torch.bfloat16).cuda()
+    for pc, pr, band, sink in ((0.10, 0.04, 0, 0), (0.5, -1.0, 3, 2), (-1.0, 0.3, 0, 1)):
+        _exact_rows(_select_on(q, k, T, pc, pr, band, sink), pc, pr, band, sink, nB)
+
+
+@pytest.mark.parametrize("nB", [2048, 4096])
+def test_selection_long_rows(nB):
+    """The largest row lengths (32 and 64 entries per lane): exact top-k of
+    the kernel's own scores on sampled rows, the longest included."""
+    T, D = 64, 64
+    S = nB * T
+    print(f"[select long rows] S={S} T={T} nB={nB}", flush=True)
+    g = torch.Generator().manual_seed(nB)
+    q = torch.randn((1, S, 1, D), generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn((1, S, 1, D), generator=g).to(torch.bfloat16).cuda()
+    rows = sorted(set([0, 1, 63, 64, 1000, nB // 2, nB - 2, nB - 1]))
+    _exact_rows(_select_on(q, k, T, 0.03, 0.01, 2, 1), 0.03, 0.01, 2, 1, nB, rows)
