@@ -43,8 +43,11 @@ int check_prefill_shape(const fsa_prefill_shape* s, PrefillDims* d) {
   if (s->D != 64 && s->D != 128) return FSA_ERR_SHAPE;
   if (s->T != 64 && s->T != 128) return FSA_ERR_SHAPE;
   if (s->S % s->T != 0 || s->S / s->T > 4096) return FSA_ERR_SHAPE;
-  // element counts used as 64-bit offsets; token rows as 32-bit ints
+  // element counts used as 64-bit offsets; token rows, (b, h, i) rows and
+  // byte strides of one token row (Hq * D * 4 bytes) as 32-bit ints
   if ((long long)s->B * s->S > (1LL << 31) - 1) return FSA_ERR_SHAPE;
+  if (s->Hq > 1024) return FSA_ERR_SHAPE;
+  if ((long long)s->B * s->Hq * (s->S / s->T) > (1LL << 31) - 1) return FSA_ERR_SHAPE;
   *d = PrefillDims{s->B, s->S, s->Hq, s->Hkv, s->D, s->T};
   return FSA_OK;
 }

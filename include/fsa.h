@@ -22,7 +22,8 @@
  * Prefill shapes: batch B, prompt length S, query heads Hq, KV heads Hkv
  * (Hq % Hkv == 0, G = Hq / Hkv, query head h reads KV head h / G), head dim
  * D in {64, 128}, block size T in {64, 128} (query block = key block),
- * S % T == 0, nB = S / T <= 4096.
+ * S % T == 0, nB = S / T <= 4096, Hq <= 1024, B * S < 2^31 and
+ * B * Hq * nB < 2^31 (else FSA_ERR_SHAPE).
  * Decode shapes: page size 16 tokens, KV pool [num_pages, Hkv, 16, D] bf16,
  * token j of sequence b at pool[page_table[b * max_pages + j / 16], g,
  * j % 16, :].

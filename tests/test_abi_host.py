@@ -65,7 +65,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 @pytest.mark.parametrize("kw,code", [
     (dict(D=96), -2), (dict(T=32), -2), (dict(S=1000), -2), (dict(Hq=3, Hkv=2), -2),
-    (dict(B=0), -2), (dict(S=64 * 5000), -2)])
+    (dict(B=0), -2), (dict(S=64 * 5000), -2), (dict(Hq=2048, Hkv=2), -2),
+    (dict(B=600, S=262144, Hq=1024, Hkv=1), -2)])
 def test_prefill_shape_validation(kw, code):
     L, lib = _lib()
     s = _shape(L, **kw)
