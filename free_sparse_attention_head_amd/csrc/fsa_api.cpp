@@ -66,6 +66,8 @@ int check_decode_shape(const fsa_decode_shape* s, DecodeDims* d) {
   if (s->num_pages < 1 || s->max_pages < 1 || s->max_seq_len < 1) return FSA_ERR_SHAPE;
   if ((long long)s->max_seq_len > 16LL * s->max_pages) return FSA_ERR_SHAPE;
   if (s->max_seq_len > (1 << 30)) return FSA_ERR_SHAPE;
+  // pool rows (page, head, slot) are 32-bit indices, the top one reserved
+  if ((long long)s->num_pages * s->Hkv * 16 >= 0xffffffffLL) return FSA_ERR_SHAPE;
   *d = DecodeDims{s->B, s->Hq, s->Hkv, s->D, s->num_pages, s->max_pages, s->max_seq_len};
   return FSA_OK;
 }

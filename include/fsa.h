@@ -24,7 +24,8 @@
  * D in {64, 128}, block size T in {64, 128} (query block = key block),
  * S % T == 0, nB = S / T <= 4096, Hq <= 1024, B * S < 2^31 and
  * B * Hq * nB < 2^31 (else FSA_ERR_SHAPE).
- * Decode shapes: page size 16 tokens, KV pool [num_pages, Hkv, 16, D] bf16,
+ * Decode shapes: page size 16 tokens, KV pool [num_pages, Hkv, 16, D] bf16
+ * with num_pages * Hkv * 16 < 2^32 - 1 (else FSA_ERR_SHAPE),
  * token j of sequence b at pool[page_table[b * max_pages + j / 16], g,
  * j % 16, :].
  */

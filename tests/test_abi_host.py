@@ -116,7 +116,8 @@ def _dshape(L, **kw):
 
 
 @pytest.mark.parametrize("kw", [dict(page_size=32), dict(Hq=6, Hkv=4), dict(Hq=32, Hkv=2),
-                                dict(D=80), dict(max_seq_len=16 * 32 + 1), dict(B=0)])
+                                dict(D=80), dict(max_seq_len=16 * 32 + 1), dict(B=0),
+                                dict(num_pages=1 << 27, Hq=16, Hkv=2)])
 def test_decode_shape_validation(kw):
     L, lib = _lib()
     s = _dshape(L, **kw)
