@@ -34,6 +34,11 @@ namespace fsa {
 constexpr int kDecThreads = 256;
 constexpr int kMaxSeg = 64;     // segments per sequence kept in LDS
 constexpr int kRowBatch = 1024;  // positions resolved to pool rows at a time
+// A split takes at least this many positions: the split count is fixed at
+// launch from the longest possible list, but a segment list may admit far
+// fewer tokens; surplus splits then take no positions and write empty
+// partials, which the combine skips.
+constexpr int kMinSplitPositions = 256;
 
 template <int D, int NH, int MODE>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     total = n;
   }
   int chunk = (total + n_split - 1) / n_split;
-  chunk = (chunk + 15) & ~15;
+  chunk = max((chunk + 15) & ~15, kMinSplitPositions);
   const int p0 = s * chunk;
   const int p1 = min(total, p0 + chunk);
 
@@ -277,20 +282,33 @@ template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part, int n_split,
                                                      uint16_t* __restrict__ out,
                                                      float* __restrict__ lse) {
+  // one wave per (b, h): the lanes read the splits' (max, sum) pairs in
+  // parallel, the weights go through LDS, and the output pass reads only the
+  // splits with a non-zero weight (empty splits hold max = -inf)
+  __shared__ float w_s[kMaxSplit];
   const int bh = blockIdx.x, l = threadIdx.x;
   const float* pp = part + (size_t)bh * n_split * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
+  for (int s = l; s < n_split; s += 64) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
+  M = wave_max(M);
   const float Mu = M == -INFINITY ? 0.f : M;
   float L = 0.f;
+  for (int s = l; s < n_split; s += 64) {
+    const float m = pp[(size_t)s * (D + 2)];
+    const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - Mu);
+    L += w * pp[(size_t)s * (D + 2) + 1];
+    w_s[s] = w;
+  }
+  L = wave_sum(L);
+  __syncthreads();
   constexpr int DPL = D / 64;
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
   for (int s = 0; s < n_split; ++s) {
+    const float w = w_s[s];
+    if (w == 0.f) continue;  // the same for every lane
     const float* ps = pp + (size_t)s * (D + 2);
-    const float w = __builtin_amdgcn_exp2f(ps[0] - Mu);
-    L += w * ps[1];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] += w * ps[2 + l * DPL + e];
   }

@@ -72,7 +72,7 @@ int check_decode_shape(const fsa_decode_shape* s, DecodeDims* d) {
   return FSA_OK;
 }
 
-constexpr int kMaxSplit = 4096;
+using fsa::kMaxSplit;
 constexpr int kMaxSegments = 64;
 
 int check_kv_select(const fsa_kv_select* sel, const DecodeDims& d) {

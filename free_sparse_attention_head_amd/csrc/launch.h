@@ -42,6 +42,8 @@ hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
 
 // topk.hip
 constexpr int kTopkMaxSeqLen = 1 << 23;  // tokens per sequence that top-k supports
+// decode splits per (sequence, head item), at most (n_split argument and combine)
+constexpr int kMaxSplit = 4096;
 size_t topk_ws_bytes(const DecodeDims& d, int k);
 // pooled: one index set per KV head from the max over its query heads' scores
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
