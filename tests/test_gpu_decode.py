@@ -349,3 +349,37 @@ def test_empty_segment_gives_zero_output():
     out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"], gpu["seq_lens"],
                                       mode=fsa.SEL_SEGMENT, segments=segs, n_seg=nseg, max_seq_len=8192)
     assert (out.cpu() == 0).all() and torch.isinf(lse.cpu()).all()
+
+
+@pytest.mark.parametrize("n_split", [64, 4096])
+def test_short_segments_with_many_splits(n_split):
+    """A few hundred admitted tokens (three short segments, 600 in all) against
+    many splits: a split takes at least 256 positions, so all but a few splits
+    are empty and write empty partials, which the combine must skip.  The
+    result equals the oracle's attention over the same ranges."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES["gqa4_d128"]
+    print(f"[short segments] n_split={n_split}", flush=True)
+    d, gpu = inputs("gqa4_d128")
+    L1 = gpu["layers"][1]
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(D)
+    ranges = [[(0, 16), (1024, 1280), (4000, 4328)], [(32, 48), (2000, 2256), (4900, 5003)],
+              [(0, 100)]]
+    segs = torch.zeros((B, 3, 2), dtype=torch.int32)
+    nseg = torch.zeros(B, dtype=torch.int32)
+    for b, rs in enumerate(ranges):
+        nseg[b] = len(rs)
+        for x, (a, e) in enumerate(rs):
+            segs[b, x, 0], segs[b, x, 1] = a, e
+    out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"],
+                                      gpu["seq_lens"], mode=fsa.SEL_SEGMENT, segments=segs.cuda(),
+                                      n_seg=nseg.cuda(), n_split=n_split, max_seq_len=N)
+    out, lse = out.cpu(), lse.cpu()
+    q1 = workloads.to_f64(d["layers"][1]["q"])
+    for b in range(B):
+        for h in range(Hq):
+            K, V = seq_kv(d, 1, b, h // G)
+            o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
+            assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
+            assert abs(lse[b, h].item() - l) <= 1e-2
