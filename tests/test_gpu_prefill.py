@@ -290,3 +290,36 @@ def test_selection_long_rows(nB):
     k = torch.randn((1, S, 1, D), generator=g).to(torch.bfloat16).cuda()
     rows = sorted(set([0, 1, 63, 64, 1000, nB // 2, nB - 2, nB - 1]))
     _exact_rows(_select_on(q, k, T, 0.03, 0.01, 2, 1), 0.03, 0.01, 2, 1, nB, rows)
+
+
+@pytest.mark.parametrize("T", [64, 128])
+def test_longest_prompt_block_lists(T):
+    """nB = 4096 key blocks (the most a row may list), for both block sizes:
+    the 4096-entry list instantiations.  Row i lists the sink block, one
+    earlier block picked by a fixed hash and its own diagonal block; sampled
+    rows (first and last blocks, around nB/2) against the oracle."""
+    import free_sparse_attention_head_amd as fsa
+    B, H, D = 1, 1, 64
+    nB = 4096
+    S = nB * T
+    print(f"[longest prompt] S={S} T={T} nB={nB}", flush=True)
+    inp = workloads.prefill_inputs(B, S, H, H, D, T, model="iid", n_spikes=0, seed=31, device="cpu")
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    bidx = torch.zeros((B, H, nB, nB), dtype=torch.int32)
+    bcnt = torch.zeros((B, H, nB), dtype=torch.int32)
+    mask = np.zeros((nB, nB), dtype=bool)
+    for i in range(nB):
+        blocks = sorted({0, (i * 7919 + 13) % (i + 1), i})
+        bidx[0, 0, i, :len(blocks)] = torch.tensor(blocks, dtype=torch.int32)
+        bcnt[0, 0, i] = len(blocks)
+        mask[i, blocks] = True
+    o, lse = fsa.sparse_prefill_attn(q, k, v, T, bidx.cuda(), bcnt.cuda())
+    o, lse = o.cpu(), lse.cpu()
+    qq, kk, vv = (workloads.to_f64(inp[x])[0, :, 0] for x in ("q", "k", "v"))
+    rows = []
+    for i in (0, 1, nB // 2 - 1, nB // 2, nB - 2, nB - 1):
+        rows += [i * T, i * T + T // 2, i * T + T - 1]
+    ref, ref_lse = oracle.masked_attention_rows(qq, kk, vv, mask, T, 1 / math.sqrt(D), rows)
+    got = o[0, rows, 0].double().numpy()
+    assert np.abs(got - ref).max() <= TOL_BF16
+    assert np.abs(lse[0, 0, rows].double().numpy() - ref_lse).max() <= 1e-2
