@@ -3,8 +3,9 @@ in index, per-KV-head index, segment and all modes) against the fp64 oracle,
 through the C ABI.
 
 The paged pools are shuffled, sequences are ragged (one shorter than k, one
-not a multiple of the page size), split counts vary (1, odd, automatic) and a
-GQA group of 8 with D = 64 is covered besides the 4 x D = 128 shape.
+not a multiple of the page size), split counts vary (1, odd, automatic), and
+every group size the kernels are built for is covered: 8 with D = 64, 4 with
+D = 128, 1 (one query head per KV head) with D = 128 and 2 with D = 64.
 """
 
 import math
@@ -23,6 +24,10 @@ SHAPES = {
     # name: (B, N, Hq, Hkv, D, seq_lens, k)
     "gqa4_d128": (3, 8192, 8, 2, 128, [8192, 5003, 100], 256),
     "gqa8_d64": (2, 4096, 8, 1, 64, [4096, 2048 + 7], 128),
+    # the other group sizes the kernels are built for: one query head per KV
+    # head, and pairs
+    "mha_d128": (2, 4096, 4, 4, 128, [4096, 1500], 64),
+    "gqa2_d64": (2, 4096, 4, 2, 64, [3000, 4096], 128),
 }
 
 _cache = {}
