@@ -3,8 +3,8 @@
 //
 // Kascade post, "What Kascade got right": reuse layers attend only at the
 // anchor layer's per-head top-k indices (index mode; the per-KV-head variant
-// shares one index set, and every K/V read, among a KV head's query heads).  Declarative Attention
-// post, "Declarative attention protocol": global / focus / local modes become
+// shares one index set, and every K/V read, among a KV head's query heads).
+// Declarative Attention post, "Declarative attention protocol": global / focus / local modes become
 // block-aligned token ranges that an unmodified attention kernel reads
 // (segment mode).  LoZA post, "4. From food delivery to AI":
 // SplitKV-and-Combine splits the KV reads and merges partial results.
@@ -22,8 +22,12 @@
 //   * the softmax is online per lane group (one rescale per RB-row step);
 //     lane groups and waves merge through LDS at the end of the split and
 //     write an unnormalised (max, sum, output) partial in fp32;
-//   * combine_kernel merges the splits of one (sequence, head); with a
-//     single split the split kernel normalises and writes the output itself.
+//   * a split takes at least kMinSplitPositions positions, so short segment
+//     lists leave surplus splits empty (max -inf, sum 0);
+//   * combine_kernel merges the splits of one (sequence, head): one wave
+//     reads every split's (max, sum) in parallel, then accumulates only the
+//     non-empty splits' outputs; with a single split the split kernel
+//     normalises and writes the output itself.
 #include <math.h>
 
 #include "common.h"
