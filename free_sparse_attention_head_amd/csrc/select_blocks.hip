@@ -40,20 +40,29 @@ __global__ __launch_bounds__(256) void pool_queries_kernel(const TI* __restrict_
     float acc[VPT];
 #pragma unroll
     for (int e = 0; e < VPT; ++e) acc[e] = 0.f;
-    for (int t = 0; t < T; ++t) {
-      uint4 w = *reinterpret_cast<const uint4*>(base + t * row_elems + cg * VPT);
-      if constexpr (sizeof(TI) == 2) {
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    // kU row loads in flight per thread before they are summed (T is a
+    // multiple of 64); the sum still runs over t in order
+    constexpr int kU = 8;
+    for (int t0 = 0; t0 < T; t0 += kU) {
+      uint4 w[kU];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_lo(ws[e]);
-          acc[2 * e + 1] += bf16_hi(ws[e]);
+      for (int u = 0; u < kU; ++u)
+        w[u] = *reinterpret_cast<const uint4*>(base + (size_t)(t0 + u) * row_elems + cg * VPT);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if constexpr (sizeof(TI) == 2) {
+          const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += bf16_lo(ws[e]);
+            acc[2 * e + 1] += bf16_hi(ws[e]);
+          }
+        } else {
+          acc[0] += __uint_as_float(w[u].x);
+          acc[1] += __uint_as_float(w[u].y);
+          acc[2] += __uint_as_float(w[u].z);
+          acc[3] += __uint_as_float(w[u].w);
         }
-      } else {
-        acc[0] += __uint_as_float(w.x);
-        acc[1] += __uint_as_float(w.y);
-        acc[2] += __uint_as_float(w.z);
-        acc[3] += __uint_as_float(w.w);
       }
     }
     const int h = (cg * VPT) / D, d0 = (cg * VPT) % D;
