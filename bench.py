@@ -12,7 +12,8 @@ One step runs every row of the hot path once over resident synthetic inputs:
     and the three reuse layers;
   segment decode, 1M context (B=4, same heads, shuffled pages): global, focus
     (2048-token chunk + 1024 local tail), local (1024) and streaming
-    (4 sinks + 1024 window) masks, caches flushed before each small mode.
+    (4 sinks + 1024 window) masks, and one mixed batch whose sequences draw
+    their modes by seed; caches flushed before each of the last four.
 Outside the timed steps: own dense baselines, and the attention kernel at 3%
 and 12% density and with the band + sink blocks only on the 128K prompt, and on
 the 32K prompt with 64-token blocks at 10%, the Kascade group with one
@@ -369,6 +370,22 @@ def make_segment(fsa, workloads, seed=1004):
                 segs[b, x, 0], segs[b, x, 1] = a, e
                 admitted += e - a
         modes[name] = dict(segs=segs.cuda(), nseg=nseg.cuda(), admitted=admitted)
+    # one mixed batch: each sequence's mode drawn by seed
+    codes = {"global": fsa.SEG_GLOBAL, "focus": fsa.SEG_FOCUS, "local": fsa.SEG_LOCAL,
+             "streaming": fsa.SEG_STREAMING}
+    draw = [list(codes)[int(x)] for x in np.random.default_rng(seed + 1).integers(0, 4, Sg["B"])]
+    segs = torch.zeros((Sg["B"], 2, 2), dtype=torch.int32)
+    nseg = torch.zeros(Sg["B"], dtype=torch.int32)
+    admitted = 0
+    for b, name in enumerate(draw):
+        st = int(rng.integers(0, n - 2048))
+        rs = fsa.build_segments(codes[name], n, chunk_start=st, chunk_len=2048, local_len=1024,
+                                n_sink=4, page=16)
+        nseg[b] = len(rs)
+        for x, (a, e) in enumerate(rs):
+            segs[b, x, 0], segs[b, x, 1] = a, e
+            admitted += e - a
+    modes["mixed"] = dict(segs=segs.cuda(), nseg=nseg.cuda(), admitted=admitted, draw=draw)
     d["modes"] = modes
     d["out"] = torch.empty((Sg["B"], Sg["Hq"], Sg["D"]), dtype=torch.bfloat16, device="cuda")
     d["flush"] = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -616,7 +633,7 @@ def main():
     group_ms = topk_ms + k_ms["decode_index_anchor"][0] + 3 * reuse_ms
     group_bytes = scan_bytes + 4 * idx_bytes - Dd["B"] * Dd["Hq"] * Dd["k"] * Dd["D"] * 2
     seg = {}
-    for name in ("global", "focus", "local", "streaming"):
+    for name in ("global", "focus", "local", "streaming", "mixed"):
         if name == "global":
             admitted = Sg["B"] * Sg["N"]
         else:
@@ -626,6 +643,7 @@ def main():
         seg[name] = {"ms": round(ms, 4), "GB": round(byts / 1e9, 4),
                      "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
                      "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    seg["mixed"]["modes"] = sg["modes"]["mixed"]["draw"]
 
     dense = {}
     if not args.no_dense:

@@ -388,3 +388,48 @@ def test_short_segments_with_many_splits(n_split):
             o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
             assert abs(lse[b, h].item() - l) <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["gqa4_d128", "gqa8_d64"])
+def test_segment_decode_mixed_batch(name):
+    """One batch whose sequences use different modes (drawn by seed: global,
+    focus, local or streaming per sequence), with automatic splits."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L1 = gpu["layers"][1]
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(D)
+    rng = np.random.default_rng(21)
+    kinds = ["global", "focus", "local", "streaming"]
+    draw = [kinds[(b + int(rng.integers(0, 4))) % 4] for b in range(B)]
+    print(f"[mixed batch {name}] modes {draw}", flush=True)
+    ranges = []
+    for b, mode in enumerate(draw):
+        n = sl[b]
+        if mode == "global":
+            ranges.append(oracle.build_segments(oracle.SEG_GLOBAL, n))
+        elif mode == "focus":
+            s = int(rng.integers(0, max(1, n - 2048)))
+            ranges.append(oracle.build_segments(oracle.SEG_FOCUS, n, s, 2048, 1024))
+        elif mode == "local":
+            ranges.append(oracle.build_segments(oracle.SEG_LOCAL, n, local_len=1024))
+        else:
+            ranges.append(oracle.build_segments(oracle.SEG_STREAMING, n, local_len=1024, n_sink=4))
+    segs = torch.zeros((B, 4, 2), dtype=torch.int32)
+    nseg = torch.zeros(B, dtype=torch.int32)
+    for b, rs in enumerate(ranges):
+        nseg[b] = len(rs)
+        for x, (a, e) in enumerate(rs):
+            segs[b, x, 0], segs[b, x, 1] = a, e
+    out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"],
+                                      gpu["seq_lens"], mode=fsa.SEL_SEGMENT, segments=segs.cuda(),
+                                      n_seg=nseg.cuda(), max_seq_len=N)
+    out, lse = out.cpu(), lse.cpu()
+    q1 = workloads.to_f64(d["layers"][1]["q"])
+    for b in range(B):
+        for h in range(Hq):
+            K, V = seq_kv(d, 1, b, h // G)
+            o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
+            assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
+            assert abs(lse[b, h].item() - l) <= 1e-2
