@@ -215,3 +215,16 @@ def test_build_segments_errors():
     assert lib.fsa_build_segments(0, 100, 0, 10, 10, 0, 0, buf, ctypes.byref(cnt)) == L.FSA_ERR_ARG
     assert lib.fsa_build_segments(0, 100, 0, 10, 10, 0, 16, None, ctypes.byref(cnt)) == L.FSA_ERR_NULL
     assert lib.fsa_build_segments_nb(1, 100, 0, 10, 10, 0, 16, -1, buf, ctypes.byref(cnt)) == L.FSA_ERR_ARG
+
+
+def test_missing_device_is_reported_not_crashed():
+    """With no GPU visible, the device probe and a fully valid call both return
+    FSA_ERR_NO_DEVICE (validation passes, nothing is launched)."""
+    import torch
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a GPU is visible: this checks the no-device path only")
+    L, lib = _lib()
+    assert lib.fsa_device_check() == L.FSA_ERR_NO_DEVICE
+    s = _shape(L)
+    rc = lib.block_stats(L.FSA_BF16, FAKE, ctypes.byref(s), FAKE, FAKE, None)
+    assert rc == L.FSA_ERR_NO_DEVICE
