@@ -93,7 +93,9 @@ enum { FSA_SEL_ALL = 0, FSA_SEL_INDEX = 1, FSA_SEL_SEGMENT = 2, FSA_SEL_INDEX_KV
  *                    [start, end), n_seg (device) int32 [B]; ranges of one
  *                    sequence must be sorted and disjoint, and are clipped
  *                    to [0, seq_lens[b]); shared by all heads.
- * n_split: split-KV factor per (sequence, head); 0 picks one. */
+ * n_split: split-KV factor per (sequence, head), 0 <= n_split <= 4096; 0
+ * picks one.  A split takes at least 256 list positions, so splits beyond
+ * what a short list needs stay empty (their partials carry no weight). */
 typedef struct {
   int32_t mode;
   const int32_t* idx;
