@@ -4,8 +4,8 @@ against the fp64 oracle, through the C ABI.
 Sizes are small enough for the oracle to finish in seconds but span several
 MFMA tiles, several 32-bit mask words with a ragged tail (nB = 40), both block
 sizes, both head dims, GQA groups, batch > 1, forced band/sink blocks, a
-switched-off branch, both branches off (forced blocks only) and fp32 as well
-as bf16 inputs.
+switched-off branch, both branches off (forced blocks only), and fp32 as well
+as bf16 inputs at every head-dim / block-size pair.
 """
 
 import math
@@ -28,6 +28,9 @@ CASES = {
     "bf16_D64_T128_rescue_off": (1, 1536, 2, 2, 64, 128, torch.bfloat16, "iid", 4, 0.30, -1.0, 0, 0),
     "fp32_D128_T128": (1, 1024, 4, 2, 128, 128, torch.float32, "lowrank", 10, 0.25, 0.10, 1, 0),
     "bf16_D64_T64_G4": (1, 1024, 8, 2, 64, 64, torch.bfloat16, "lowrank", 10, 0.2, 0.08, 2, 1),
+    # the other fp32 head-dim / block-size pairs
+    "fp32_D128_T64": (1, 1536, 4, 4, 128, 64, torch.float32, "lowrank", 8, 0.2, 0.08, 1, 1),
+    "fp32_D64_T128_G2": (2, 1024, 4, 2, 64, 128, torch.float32, "iid", 6, 0.3, 0.1, 0, 0),
     # both branches off: the forced band + sink only (a fixed-window mask)
     "bf16_forced_only_band8_sink1": (1, 4096, 4, 2, 128, 128, torch.bfloat16, "lowrank", 10,
                                      -1.0, -1.0, 8, 1),
