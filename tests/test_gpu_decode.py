@@ -4,8 +4,8 @@ through the C ABI.
 
 The paged pools are shuffled, sequences are ragged (one shorter than k, one
 not a multiple of the page size), split counts vary (1, odd, automatic), and
-every group size the kernels are built for is covered: 8 with D = 64, 4 with
-D = 128, 1 (one query head per KV head) with D = 128 and 2 with D = 64.
+every (head dim, group size) pair the kernels are built for is covered:
+D = 64 and 128 with 1, 2, 4 and 8 query heads per KV head.
 """
 
 import math
@@ -28,6 +28,11 @@ SHAPES = {
     # head, and pairs
     "mha_d128": (2, 4096, 4, 4, 128, [4096, 1500], 64),
     "gqa2_d64": (2, 4096, 4, 2, 64, [3000, 4096], 128),
+    # ... and the remaining (head dim, group size) pairs the kernels are built for
+    "mha_d64": (2, 2048, 2, 2, 64, [2048, 999], 64),
+    "gqa2_d128": (2, 2048, 4, 2, 128, [2048, 1040], 64),
+    "gqa4_d64": (2, 2048, 8, 2, 64, [1500, 2048], 64),
+    "gqa8_d128": (2, 2048, 16, 2, 128, [2048, 777], 64),
 }
 
 _cache = {}
