@@ -295,17 +295,18 @@ def test_selection_long_rows(nB):
     _exact_rows(_select_on(q, k, T, 0.03, 0.01, 2, 1), 0.03, 0.01, 2, 1, nB, rows)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T", [64, 128])
-def test_longest_prompt_block_lists(T):
-    """nB = 4096 key blocks (the most a row may list), for both block sizes:
-    the 4096-entry list instantiations.  Row i lists the sink block, one
+def test_longest_prompt_block_lists(T, D):
+    """nB = 4096 key blocks (the most a row may list), for both block sizes and
+    head dims: the 4096-entry list instantiations.  Row i lists the sink block, one
     earlier block picked by a fixed hash and its own diagonal block; sampled
     rows (first and last blocks, around nB/2) against the oracle."""
     import free_sparse_attention_head_amd as fsa
-    B, H, D = 1, 1, 64
+    B, H = 1, 1
     nB = 4096
     S = nB * T
-    print(f"[longest prompt] S={S} T={T} nB={nB}", flush=True)
+    print(f"[longest prompt] S={S} T={T} D={D} nB={nB}", flush=True)
     inp = workloads.prefill_inputs(B, S, H, H, D, T, model="iid", n_spikes=0, seed=31, device="cpu")
     q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
     bidx = torch.zeros((B, H, nB, nB), dtype=torch.int32)
