@@ -281,17 +281,18 @@ def test_selection_ties(kind):
         _exact_rows(_select_on(q, k, T, pc, pr, band, sink), pc, pr, band, sink, nB)
 
 
-@pytest.mark.parametrize("nB", [2048, 4096])
+@pytest.mark.parametrize("nB", [100, 300, 700, 2048, 4096])
 def test_selection_long_rows(nB):
-    """The largest row lengths (32 and 64 entries per lane): exact top-k of
-    the kernel's own scores on sampled rows, the longest included."""
+    """Row lengths for each selection instantiation not met elsewhere (2, 8,
+    16, 32 and 64 entries per lane): exact top-k of the kernel's own scores on
+    sampled rows, the longest included."""
     T, D = 64, 64
     S = nB * T
     print(f"[select long rows] S={S} T={T} nB={nB}", flush=True)
     g = torch.Generator().manual_seed(nB)
     q = torch.randn((1, S, 1, D), generator=g).to(torch.bfloat16).cuda()
     k = torch.randn((1, S, 1, D), generator=g).to(torch.bfloat16).cuda()
-    rows = sorted(set([0, 1, 63, 64, 1000, nB // 2, nB - 2, nB - 1]))
+    rows = sorted(set(x for x in [0, 1, 63, 64, 1000, nB // 2, nB - 2, nB - 1] if x < nB))
     _exact_rows(_select_on(q, k, T, 0.03, 0.01, 2, 1), 0.03, 0.01, 2, 1, nB, rows)
 
 
