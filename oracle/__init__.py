@@ -28,24 +28,27 @@ status per function:
   dense_attention, masked_attention, masked_attention_rows,
   index_attention, segment_attention, lse_combine  -- pinned
   block_stats, pool_queries, select_blocks           -- pinned
-  topk, topk_pooled                                   -- pinned
+  kv_head, anchor_scores, topk, anchor_topk           -- pinned
+  topk_pooled, union_sets, set_recall                 -- pinned
   gather_pages, build_segments                        -- pinned
-  token_block_mass, retention, ideal_rows             -- pinned
+  token_block_mass, retention, ideal_rows, index_mass -- pinned
 """
 
 from .attention import (dense_attention, masked_attention, masked_attention_rows,
                         index_attention, segment_attention, lse_combine,
                         attention_partial)
 from .blocks import block_stats, pool_queries, select_blocks, visible_count, k_of
-from .topk import topk, topk_pooled, near_kth_mask
+from .topk import (kv_head, anchor_scores, topk, anchor_topk, topk_pooled, union_sets,
+                   set_recall)
 from .paged import gather_pages
 from .segments import build_segments, SEG_GLOBAL, SEG_FOCUS, SEG_LOCAL, SEG_STREAMING
-from .quality import token_block_mass, retention, ideal_rows
+from .quality import token_block_mass, retention, ideal_rows, index_mass
 
 __all__ = [
     "dense_attention", "masked_attention", "masked_attention_rows", "index_attention",
     "segment_attention", "lse_combine", "attention_partial", "block_stats", "pool_queries",
-    "select_blocks", "visible_count", "k_of", "topk", "topk_pooled", "near_kth_mask", "gather_pages",
+    "select_blocks", "visible_count", "k_of", "kv_head", "anchor_scores", "topk", "anchor_topk",
+    "topk_pooled", "union_sets", "set_recall", "gather_pages",
     "build_segments", "SEG_GLOBAL", "SEG_FOCUS", "SEG_LOCAL", "SEG_STREAMING",
-    "token_block_mass", "retention", "ideal_rows",
+    "token_block_mass", "retention", "ideal_rows", "index_mass",
 ]

@@ -63,3 +63,17 @@ def ideal_rows(q, k, T, scale, counts, rows):
         keep = np.sort(order[:c])
         out[i] = (keep, m[:, keep].sum(axis=1))
     return out
+
+
+def index_mass(q, kseq, idx, scale):
+    """Decode counterpart of retention: the share of one query's softmax mass
+    over every cached key, softmax_j(scale * q . k_j) for j < N, that falls on
+    the keys listed in idx (negative entries are empty slots; a key listed
+    twice counts once).  q [D], kseq [N, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    kseq = np.asarray(kseq, dtype=np.float64)
+    s = scale * (kseq @ q)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    idx = np.unique(np.asarray(idx, dtype=np.int64))
+    return float(p[idx[idx >= 0]].sum())

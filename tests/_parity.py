@@ -5,6 +5,13 @@ import numpy as np
 BAND = 1e-3      # near-threshold band for masks and top-k sets
 TOL_BF16 = 2e-2  # max-abs output tolerance, bf16 inputs
 TOL_F32 = 1e-4   # max-abs output tolerance, fp32 inputs
+# log-sum-exp tolerance (natural log).  Scores are exact fp32 products of the
+# inputs and the row sum adds the same (bf16-rounded, for bf16 inputs)
+# probabilities that weight the values, so the LSE error is a few ulps of the
+# sum: these bounds leave an order of magnitude of room, and a constant bias
+# of 0.01 (bf16) or 1e-4 (fp32) nats fails them.
+LSE_TOL_BF16 = 1e-2
+LSE_TOL_F32 = 1e-4
 
 
 def lists_to_mask(block_idx, block_cnt, nB):

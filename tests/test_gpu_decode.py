@@ -79,8 +79,8 @@ def test_topk_parity(name):
                 assert np.isneginf(kth[b, h])
                 continue
             assert (np.diff(row) > 0).all() and row.min() >= 0 and row.max() < n
-            K, _ = seq_kv(d, 0, b, h // G)
-            scores = K @ q[b, h]
+            K, _ = seq_kv(d, 0, b, oracle.kv_head(h, Hq, Hkv))
+            scores = oracle.anchor_scores(q[b, h], K)
             ref_idx, ref_kth = oracle.topk(scores, k)
             dd, ee = topk_diff_excused(row, ref_idx, scores, ref_kth)
             n_diff += dd
@@ -101,8 +101,8 @@ def test_topk_k_equals_n_and_k_one():
     q = workloads.to_f64(d["layers"][0]["q"])
     for b in range(3):
         for h in range(8):
-            K, _ = seq_kv(d, 0, b, h // 4, n=3000)
-            s = K @ q[b, h]
+            K, _ = seq_kv(d, 0, b, oracle.kv_head(h, 8, 2), n=3000)
+            s = oracle.anchor_scores(q[b, h], K)
             assert abs(kth[b, h].item() - s.min()) <= 1e-3
             assert abs(kth1[b, h].item() - s.max()) <= 1e-3
             am = int(idx1[b, h, 0])
@@ -153,7 +153,7 @@ def test_topk_many_ties_uses_general_path_exactly():
     qq = workloads.to_f64(q)
     for h in range(Hq):
         K = oracle.gather_pages(workloads.to_f64(kp), pt[1].numpy(), N, 0)
-        ref, _ = oracle.topk(K @ qq[1, h], k)
+        ref, _ = oracle.anchor_topk(qq[1, h], K, k)
         assert (idx[1, h] == ref).all()
 
 
@@ -179,7 +179,7 @@ def test_topk_ties_across_pruned_tiles():
     idxp, _ = fsa.topk_indices_kv(q.cuda(), kp.cuda(), pt.cuda(), d["seq_lens"].cuda(), k)
     K = oracle.gather_pages(workloads.to_f64(kp), pt[0].numpy(), N, 0)
     qq = workloads.to_f64(q)
-    ref, _ = oracle.topk(K @ qq[0, 0], k)
+    ref, _ = oracle.anchor_topk(qq[0, 0], K, k)
     assert list(ref) == planted[:k]
     for h in range(Hq):
         assert (idx[0, h].cpu().numpy() == ref).all()
@@ -203,7 +203,7 @@ def test_index_decode_parity(name, n_split):
     scale = 1 / math.sqrt(D)
     for b in range(B):
         for h in range(Hq):
-            K, V = seq_kv(d, 1, b, h // G)
+            K, V = seq_kv(d, 1, b, oracle.kv_head(h, Hq, Hkv))
             o, l = oracle.index_attention(q1[b, h], K, V, idx[b, h], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
             assert abs(lse[b, h].item() - l) <= 1e-2
@@ -236,8 +236,8 @@ def test_listed_decode_spans_several_row_batches(mode):
     for b in range(B):
         n = int(d["seq_lens"][b])
         for h in range(Hq):
-            K, V = seq_kv(d, 0, b, h // G)
-            ix = idx[b, h if mode == "index" else h // G]
+            K, V = seq_kv(d, 0, b, oracle.kv_head(h, Hq, Hkv))
+            ix = idx[b, h if mode == "index" else oracle.kv_head(h, Hq, Hkv)]
             ix = np.where(ix < n, ix, -1)
             o, l = oracle.index_attention(q[b, h], K, V, ix, 1 / math.sqrt(D))
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
@@ -268,7 +268,8 @@ def test_topk_kv_parity(name):
                 continue
             assert (np.diff(row) > 0).all() and row.min() >= 0 and row.max() < n
             K, _ = seq_kv(d, 0, b, g)
-            scores = K @ q[b, g * G:(g + 1) * G].T        # [n, G]
+            heads = [h for h in range(Hq) if oracle.kv_head(h, Hq, Hkv) == g]
+            scores = np.stack([oracle.anchor_scores(q[b, h], K) for h in heads], axis=1)  # [n, G]
             ref_idx, ref_kth = oracle.topk_pooled(scores.T, k)
             dd, ee = topk_diff_excused(row, ref_idx, scores.max(axis=1), ref_kth)
             n_diff += dd
@@ -298,8 +299,8 @@ def test_index_kv_decode_parity(name, n_split):
     scale = 1 / math.sqrt(D)
     for b in range(B):
         for h in range(Hq):
-            K, V = seq_kv(d, 1, b, h // G)
-            o, l = oracle.index_attention(q1[b, h], K, V, idx[b, h // G], scale)
+            K, V = seq_kv(d, 1, b, oracle.kv_head(h, Hq, Hkv))
+            o, l = oracle.index_attention(q1[b, h], K, V, idx[b, oracle.kv_head(h, Hq, Hkv)], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
             assert abs(lse[b, h].item() - l) <= 1e-2
 
@@ -344,7 +345,7 @@ def test_segment_decode_parity(name, mode):
     q1 = workloads.to_f64(d["layers"][1]["q"])
     for b in range(B):
         for h in range(Hq):
-            K, V = seq_kv(d, 1, b, h // G)
+            K, V = seq_kv(d, 1, b, oracle.kv_head(h, Hq, Hkv))
             o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
             assert abs(lse[b, h].item() - l) <= 1e-2
@@ -389,7 +390,7 @@ def test_short_segments_with_many_splits(n_split):
     q1 = workloads.to_f64(d["layers"][1]["q"])
     for b in range(B):
         for h in range(Hq):
-            K, V = seq_kv(d, 1, b, h // G)
+            K, V = seq_kv(d, 1, b, oracle.kv_head(h, Hq, Hkv))
             o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
             assert abs(lse[b, h].item() - l) <= 1e-2
@@ -434,7 +435,7 @@ def test_segment_decode_mixed_batch(name):
     q1 = workloads.to_f64(d["layers"][1]["q"])
     for b in range(B):
         for h in range(Hq):
-            K, V = seq_kv(d, 1, b, h // G)
+            K, V = seq_kv(d, 1, b, oracle.kv_head(h, Hq, Hkv))
             o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
             assert abs(lse[b, h].item() - l) <= 1e-2

@@ -13,7 +13,11 @@ times, checked on sampled outputs that the fp64 oracle computes one by one.
 
 Sampled rows: block statistics and selector rows against the oracle
 (bit-exact up to near-threshold entries), attention outputs against the
-oracle evaluated on the GPU's own mask or indices (2e-2 max-abs, bf16).
+oracle evaluated on the GPU's own mask or indices (2e-2 max-abs, bf16) and
+log-sum-exps within 1e-2.  Decode keys and values reach the oracle through
+its own paged gather: the pages a sequence uses are copied to the host whole,
+in page-id order, and oracle.gather_pages reads them through the sequence's
+page table (remapped to that copy).
 """
 
 import math
@@ -24,7 +28,8 @@ import torch
 
 import oracle
 import workloads
-from tests._parity import BAND, TOL_BF16, lists_to_mask, mask_diff_excused, topk_diff_excused
+from tests._parity import (BAND, LSE_TOL_BF16, TOL_BF16, lists_to_mask, mask_diff_excused,
+                           topk_diff_excused)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,13 +67,15 @@ def _check_prefill(name, S, Hq, Hkv, T, band, sink, density, seed, n_rows=6, n_t
     rng = np.random.default_rng(seed)
     scale = 1 / math.sqrt(D)
     n_diff = n_exc = 0
+    worst_lse = 0.0
     for g in rng.choice(Hkv, size=min(2, Hkv), replace=False):
         kk = workloads.to_f64(k[0, :, g])
         vv = workloads.to_f64(v[0, :, g])
         c_ref, r_ref = oracle.block_stats(kk, T)
         assert np.abs(c[0, g].double().cpu().numpy() - c_ref).max() <= 1e-5
         assert np.abs(r[0, g].double().cpu().numpy() - r_ref).max() <= 1e-4 * r_ref.max()
-        for h in rng.choice(np.arange(g * G, (g + 1) * G), size=2, replace=False):
+        heads = [h for h in range(Hq) if oracle.kv_head(h, Hq, Hkv) == g]
+        for h in rng.choice(heads, size=2, replace=False):
             qh = workloads.to_f64(q[0, :, h])
             qbar = oracle.pool_queries(qh, T)
             cnt = sel["block_cnt"][0, h].cpu().numpy()
@@ -92,9 +99,11 @@ def _check_prefill(name, S, Hq, Hkv, T, band, sink, density, seed, n_rows=6, n_t
                 o_ref, l_ref = oracle.masked_attention_rows(qh, kk, vv, m, T, scale, toks)
                 got = o[0, toks, h].double().cpu().numpy()
                 assert np.abs(got - o_ref).max() <= TOL_BF16, (g, h, i)
-                assert np.abs(lse[0, h, toks].double().cpu().numpy() - l_ref).max() <= 10 * TOL_BF16
+                err = np.abs(lse[0, h, toks].double().cpu().numpy() - l_ref).max()
+                worst_lse = max(worst_lse, err)
+                assert err <= LSE_TOL_BF16, (g, h, i, err)
     print(f"[fullsize {name}] density {dens:.4f}; sampled mask entries differing {n_diff}, "
-          f"excused {n_exc}", flush=True)
+          f"excused {n_exc}; worst lse error {worst_lse:.2e}", flush=True)
     assert n_diff == n_exc
 
 
@@ -107,12 +116,16 @@ def test_prefill_128k_block128(density):
     _check_prefill(f"prefill128k-{density}", 131072, 32, 4, 128, 8, 1, density, seed=1002)
 
 
-def _seq_kv_gpu(pool, page_table_row, n, g):
-    """Contiguous K or V of one sequence / KV head, gathered on the GPU and
-    widened exactly on the host (the oracle's gather is pinned separately)."""
-    pages = page_table_row[: (n + 15) // 16].long()
-    blk = pool[pages, g].reshape(-1, pool.shape[-1])[:n]
-    return workloads.to_f64(blk)
+def _seq_kv(pool, page_table_row, n, g, start=0):
+    """K or V of tokens [start, start + n) of one sequence and KV head (start
+    page-aligned), through the oracle's paged gather: the pages the range uses
+    are copied to the host whole, in page-id order, and oracle.gather_pages
+    reads them through the range's page-table entries remapped to that copy."""
+    assert start % 16 == 0
+    ids = page_table_row[start // 16: (start + n + 15) // 16].long()
+    uniq, inv = torch.unique(ids, sorted=True, return_inverse=True)
+    sub = workloads.to_f64(pool[uniq, g:g + 1])          # [pages, 1, 16, D]
+    return oracle.gather_pages(sub, inv.cpu().numpy(), n, 0)
 
 
 def test_kascade_decode_128k_group():
@@ -127,13 +140,12 @@ def test_kascade_decode_128k_group():
     torch.cuda.synchronize()
     idx_h, kth_h = idx.cpu().numpy(), kth.cpu().numpy()
     rng = np.random.default_rng(3)
-    G = Hq // Hkv
     n_diff = n_exc = 0
     for b in rng.choice(B, size=3, replace=False):
         for h in rng.choice(Hq, size=3, replace=False):
-            g = h // G
-            K0 = _seq_kv_gpu(d["layers"][0]["k"], pt[b], N, g)
-            s = K0 @ workloads.to_f64(d["layers"][0]["q"][b, h])
+            g = oracle.kv_head(h, Hq, Hkv)
+            K0 = _seq_kv(d["layers"][0]["k"], pt[b], N, g)
+            s = oracle.anchor_scores(workloads.to_f64(d["layers"][0]["q"][b, h]), K0)
             ref_idx, ref_kth = oracle.topk(s, k)
             row = idx_h[b, h]
             assert (np.diff(row) > 0).all()
@@ -141,8 +153,8 @@ def test_kascade_decode_128k_group():
             n_diff, n_exc = n_diff + dd, n_exc + ee
             assert abs(kth_h[b, h] - ref_kth) <= BAND
             for li in range(L):
-                Kl = K0 if li == 0 else _seq_kv_gpu(d["layers"][li]["k"], pt[b], N, g)
-                Vl = _seq_kv_gpu(d["layers"][li]["v"], pt[b], N, g)
+                Kl = K0 if li == 0 else _seq_kv(d["layers"][li]["k"], pt[b], N, g)
+                Vl = _seq_kv(d["layers"][li]["v"], pt[b], N, g)
                 o_ref, _ = oracle.index_attention(workloads.to_f64(d["layers"][li]["q"][b, h]), Kl, Vl,
                                                   row, 1 / math.sqrt(D))
                 assert np.abs(outs[li][b, h].double().cpu().numpy() - o_ref).max() <= TOL_BF16
@@ -165,12 +177,13 @@ def test_kascade_kv_shared_decode_128k_group():
     torch.cuda.synchronize()
     idx_h, kth_h = idx.cpu().numpy(), kth.cpu().numpy()
     rng = np.random.default_rng(5)
-    G = Hq // Hkv
     n_diff = n_exc = 0
     for b in rng.choice(B, size=3, replace=False):
         for g in rng.choice(Hkv, size=2, replace=False):
-            K0 = _seq_kv_gpu(d["layers"][0]["k"], pt[b], N, g)
-            s = K0 @ workloads.to_f64(d["layers"][0]["q"][b, g * G:(g + 1) * G]).T
+            heads = [h for h in range(Hq) if oracle.kv_head(h, Hq, Hkv) == g]
+            K0 = _seq_kv(d["layers"][0]["k"], pt[b], N, g)
+            s = np.stack([oracle.anchor_scores(workloads.to_f64(d["layers"][0]["q"][b, h]), K0)
+                          for h in heads], axis=1)         # [N, G]
             ref_idx, ref_kth = oracle.topk_pooled(s.T, k)
             row = idx_h[b, g]
             assert (np.diff(row) > 0).all()
@@ -178,9 +191,9 @@ def test_kascade_kv_shared_decode_128k_group():
             n_diff, n_exc = n_diff + dd, n_exc + ee
             assert abs(kth_h[b, g] - ref_kth) <= BAND
             for li in range(L):
-                Kl = K0 if li == 0 else _seq_kv_gpu(d["layers"][li]["k"], pt[b], N, g)
-                Vl = _seq_kv_gpu(d["layers"][li]["v"], pt[b], N, g)
-                for h in (g * G, g * G + G - 1):
+                Kl = K0 if li == 0 else _seq_kv(d["layers"][li]["k"], pt[b], N, g)
+                Vl = _seq_kv(d["layers"][li]["v"], pt[b], N, g)
+                for h in (heads[0], heads[-1]):
                     o_ref, _ = oracle.index_attention(workloads.to_f64(d["layers"][li]["q"][b, h]),
                                                       Kl, Vl, row, 1 / math.sqrt(D))
                     assert np.abs(outs[li][b, h].double().cpu().numpy() - o_ref).max() <= TOL_BF16
@@ -196,7 +209,6 @@ def test_segment_decode_1m_all_modes():
     pt, sl = d["page_table"], d["seq_lens"]
     Lr = d["layers"][0]
     rng = np.random.default_rng(4)
-    G = Hq // Hkv
     modes = {"global": fsa.SEG_GLOBAL, "focus": fsa.SEG_FOCUS, "local": fsa.SEG_LOCAL,
              "streaming": fsa.SEG_STREAMING}
     for name, code in modes.items():
@@ -213,27 +225,20 @@ def test_segment_decode_1m_all_modes():
         torch.cuda.synchronize()
         for b in rng.choice(B, size=2, replace=False):
             for h in rng.choice(Hq, size=2, replace=False):
-                g = h // G
-                keep = np.zeros(N, dtype=bool)
-                for a, e in ranges[b]:
-                    keep[a:e] = True
-                toks = np.flatnonzero(keep)
+                g = oracle.kv_head(h, Hq, Hkv)
+                qh = workloads.to_f64(Lr["q"][b, h])
                 if name == "global":
-                    K = _seq_kv_gpu(Lr["k"], pt[b], N, g)
-                    V = _seq_kv_gpu(Lr["v"], pt[b], N, g)
-                    o_ref, l_ref = oracle.segment_attention(workloads.to_f64(Lr["q"][b, h]), K, V,
-                                                            ranges[b], 1 / math.sqrt(D))
+                    K = _seq_kv(Lr["k"], pt[b], N, g)
+                    V = _seq_kv(Lr["v"], pt[b], N, g)
+                    o_ref, l_ref = oracle.segment_attention(qh, K, V, ranges[b], 1 / math.sqrt(D))
                 else:
-                    pages = torch.from_numpy(np.unique(toks // 16)).cuda()
-                    prow = pt[b].long()[pages]
-                    Kb = Lr["k"][prow, g].reshape(-1, D)
-                    Vb = Lr["v"][prow, g].reshape(-1, D)
-                    # positions of the admitted tokens inside the gathered pages
-                    pos = np.searchsorted(np.unique(toks // 16), toks // 16) * 16 + toks % 16
-                    K = workloads.to_f64(Kb)[pos]
-                    V = workloads.to_f64(Vb)[pos]
-                    o_ref, l_ref = oracle.index_attention(workloads.to_f64(Lr["q"][b, h]), K, V,
-                                                          np.arange(len(toks)), 1 / math.sqrt(D))
+                    # each range starts on a page boundary (rounded outward, or
+                    # token 0 / N - 1024): gather the ranges alone and attend
+                    # over all of their tokens
+                    K = np.concatenate([_seq_kv(Lr["k"], pt[b], e - a, g, start=a) for a, e in ranges[b]])
+                    V = np.concatenate([_seq_kv(Lr["v"], pt[b], e - a, g, start=a) for a, e in ranges[b]])
+                    o_ref, l_ref = oracle.index_attention(qh, K, V, np.arange(K.shape[0]),
+                                                          1 / math.sqrt(D))
                 assert np.abs(out[b, h].double().cpu().numpy() - o_ref).max() <= TOL_BF16, (name, b, h)
-                assert abs(lse[b, h].item() - l_ref) <= 1e-2
+                assert abs(lse[b, h].item() - l_ref) <= LSE_TOL_BF16
         print(f"[fullsize segment] mode {name} ok", flush=True)

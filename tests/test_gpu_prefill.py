@@ -16,7 +16,8 @@ import torch
 
 import oracle
 import workloads
-from tests._parity import (TOL_BF16, TOL_F32, bits_to_mask, lists_to_mask, mask_diff_excused)
+from tests._parity import (LSE_TOL_BF16, LSE_TOL_F32, TOL_BF16, TOL_F32, bits_to_mask,
+                           lists_to_mask, mask_diff_excused)
 
 pytestmark = pytest.mark.gpu
 
@@ -82,14 +83,13 @@ def test_select_blocks_parity(name):
     B, S, Hq, Hkv, D, T, dt, model, nsp, pc, pr, band, sink = CASES[name]
     res = run(name)
     nB = S // T
-    G = Hq // Hkv
     q = workloads.to_f64(res["inp"]["q"])
     k = workloads.to_f64(res["inp"]["k"])
     n_diff = n_exc = 0
     for b in range(B):
         for g in range(Hkv):
             c, r = oracle.block_stats(k[b, :, g], T)
-            for h in range(g * G, (g + 1) * G):
+            for h in [x for x in range(Hq) if oracle.kv_head(x, Hq, Hkv) == g]:
                 ref = oracle.select_blocks(oracle.pool_queries(q[b, :, h], T), c, r, pc, pr,
                                            band, sink)
                 cnt = res["block_cnt"][b, h].numpy()
@@ -116,36 +116,43 @@ def test_sparse_prefill_attn_parity(name):
     B, S, Hq, Hkv, D, T, dt = CASES[name][:7]
     res = run(name)
     nB = S // T
-    G = Hq // Hkv
     tol = TOL_F32 if dt == torch.float32 else TOL_BF16
+    ltol = LSE_TOL_F32 if dt == torch.float32 else LSE_TOL_BF16
     q, k, v = (workloads.to_f64(res["inp"][x]) for x in ("q", "k", "v"))
     scale = 1 / math.sqrt(D)
-    worst = 0.0
+    worst = worst_lse = 0.0
     for b in range(B):
         for h in range(Hq):
-            g = h // G
+            g = oracle.kv_head(h, Hq, Hkv)
             m = lists_to_mask(res["block_idx"][b, h].numpy(), res["block_cnt"][b, h].numpy(), nB)
             o, lse = oracle.masked_attention(q[b, :, h], k[b, :, g], v[b, :, g], m, T, scale)
             err = np.abs(res["o_sp"][b, :, h].double().numpy() - o).max()
             worst = max(worst, err)
             assert err <= tol, (b, h, err)
-            assert np.abs(res["lse_sp"][b, h].double().numpy() - lse).max() <= 10 * tol
-    print(f"[{name}] sparse max-abs error {worst:.3e}")
+            lerr = np.abs(res["lse_sp"][b, h].double().numpy() - lse).max()
+            worst_lse = max(worst_lse, lerr)
+            assert lerr <= ltol, (b, h, lerr)
+    print(f"[{name}] sparse max-abs error {worst:.3e}, worst lse error {worst_lse:.3e}")
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_dense_mode_matches_dense_oracle(name):
     B, S, Hq, Hkv, D, T, dt = CASES[name][:7]
     res = run(name)
-    G = Hq // Hkv
     tol = TOL_F32 if dt == torch.float32 else TOL_BF16
+    ltol = LSE_TOL_F32 if dt == torch.float32 else LSE_TOL_BF16
     q, k, v = (workloads.to_f64(res["inp"][x]) for x in ("q", "k", "v"))
     scale = 1 / math.sqrt(D)
+    worst_lse = 0.0
     for b in range(B):
         for h in sorted({0, Hq - 1}):
-            o, lse = oracle.dense_attention(q[b, :, h], k[b, :, h // G], v[b, :, h // G], scale)
+            g = oracle.kv_head(h, Hq, Hkv)
+            o, lse = oracle.dense_attention(q[b, :, h], k[b, :, g], v[b, :, g], scale)
             assert np.abs(res["o_dn"][b, :, h].double().numpy() - o).max() <= tol
-            assert np.abs(res["lse_dn"][b, h].double().numpy() - lse).max() <= 10 * tol
+            lerr = np.abs(res["lse_dn"][b, h].double().numpy() - lse).max()
+            worst_lse = max(worst_lse, lerr)
+            assert lerr <= ltol, (b, h, lerr)
+    print(f"[{name}] dense worst lse error {worst_lse:.3e}")
 
 
 def test_all_blocks_mask_equals_dense_kernel():
@@ -208,10 +215,11 @@ def test_anchor_selection_reused_by_a_later_layer():
     q, k, v = (workloads.to_f64(later[x]) for x in ("q", "k", "v"))
     for h in range(Hq):
         m = lists_to_mask(sel["block_idx"][0, h].cpu().numpy(), sel["block_cnt"][0, h].cpu().numpy(), nB)
-        ref, ref_lse = oracle.masked_attention(q[0, :, h], k[0, :, h // 2], v[0, :, h // 2], m, T,
+        g = oracle.kv_head(h, Hq, Hkv)
+        ref, ref_lse = oracle.masked_attention(q[0, :, h], k[0, :, g], v[0, :, g], m, T,
                                                1 / math.sqrt(D))
         assert np.abs(o[0, :, h].double().numpy() - ref).max() <= TOL_BF16
-        assert np.abs(lse[0, h].double().numpy() - ref_lse).max() <= 10 * TOL_BF16
+        assert np.abs(lse[0, h].double().numpy() - ref_lse).max() <= LSE_TOL_BF16
 
 
 def _exact_rows(res, pc, pr, band, sink, nB, rows=None):

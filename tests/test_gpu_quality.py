@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import workloads
-from tests._parity import lists_to_mask
+from tests._parity import LSE_TOL_BF16, lists_to_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -37,10 +37,13 @@ def _case():
                                 ("rescue", -1.0, 0.14))}
     _, lse_d = fsa.sparse_prefill_attn(q, k, v, T)
     ret = {}
+    lses = {"dense": lse_d[0].cpu().double().numpy()}
     for name, s in sel.items():
         _, lse_m = fsa.sparse_prefill_attn(q, k, v, T, s["block_idx"], s["block_cnt"])
         ret[name] = torch.exp(lse_m - lse_d)[0].cpu().double().numpy()   # [Hq, S]
-    return inp, {n: {x: y.cpu() for x, y in s.items() if y is not None} for n, s in sel.items()}, ret
+        lses[name] = lse_m[0].cpu().double().numpy()
+    sel = {n: {x: y.cpu() for x, y in s.items() if y is not None} for n, s in sel.items()}
+    return inp, sel, ret, lses
 
 
 _cache = []
@@ -53,7 +56,7 @@ def case():
 
 
 def test_retention_from_lse_matches_oracle():
-    inp, sel, ret = case()
+    inp, sel, ret, _ = case()
     q, k = workloads.to_f64(inp["q"]), workloads.to_f64(inp["k"])
     nB = S // T
     scale = 1 / math.sqrt(D)
@@ -61,7 +64,7 @@ def test_retention_from_lse_matches_oracle():
     for name in sel:
         for h in (0, Hq - 1):
             m = lists_to_mask(sel[name]["block_idx"][0, h].numpy(), sel[name]["block_cnt"][0, h].numpy(), nB)
-            ref = oracle.retention(q[0, :, h], k[0, :, h // (Hq // Hkv)], m, T, scale)
+            ref = oracle.retention(q[0, :, h], k[0, :, oracle.kv_head(h, Hq, Hkv)], m, T, scale)
             for i in range(nB):
                 err = np.abs(ret[name][h, i * T:(i + 1) * T] - ref[i]).max()
                 worst = max(worst, err)
@@ -69,11 +72,36 @@ def test_retention_from_lse_matches_oracle():
     print(f"[quality] retention max-abs difference GPU vs oracle {worst:.2e}")
 
 
+def test_retention_lses_match_oracle_lses():
+    """The two log-sum-exps behind each retention figure, each against the
+    oracle's own (masked and dense attention on the same inputs), so that a
+    bias the ratio would cancel still fails."""
+    inp, sel, _, lses = case()
+    q, k, v = (workloads.to_f64(inp[x]) for x in ("q", "k", "v"))
+    nB = S // T
+    scale = 1 / math.sqrt(D)
+    toks = np.array([0, 1, T - 1, T, 17 * T + 5, S // 2, S - T, S - 1])
+    worst = 0.0
+    for h in (0, Hq - 1):
+        g = oracle.kv_head(h, Hq, Hkv)
+        full = np.tril(np.ones((nB, nB), dtype=bool))
+        _, ref_d = oracle.masked_attention_rows(q[0, :, h], k[0, :, g], v[0, :, g], full, T, scale,
+                                                toks)
+        worst = max(worst, np.abs(lses["dense"][h, toks] - ref_d).max())
+        for name in sel:
+            m = lists_to_mask(sel[name]["block_idx"][0, h].numpy(), sel[name]["block_cnt"][0, h].numpy(), nB)
+            _, ref_m = oracle.masked_attention_rows(q[0, :, h], k[0, :, g], v[0, :, g], m, T, scale,
+                                                    toks)
+            worst = max(worst, np.abs(lses[name][h, toks] - ref_m).max())
+    print(f"[quality] worst lse error behind the retention figures {worst:.2e}")
+    assert worst <= LSE_TOL_BF16
+
+
 def test_ideal_mask_bounds_every_selector_row():
     """At each row's own block count, the oracle's ideal mask keeps at least
     as much mass as any selector's mask (and the report shows how far each
     selector is from it)."""
-    inp, sel, ret = case()
+    inp, sel, ret, _ = case()
     q, k = workloads.to_f64(inp["q"]), workloads.to_f64(inp["k"])
     nB = S // T
     scale = 1 / math.sqrt(D)
@@ -81,7 +109,8 @@ def test_ideal_mask_bounds_every_selector_row():
     rows = list(range(0, nB, 3))
     for name in sel:
         cnt = sel[name]["block_cnt"][0, h].numpy()
-        ideal = oracle.ideal_rows(q[0, :, h], k[0, :, h // (Hq // Hkv)], T, scale, cnt, rows)
+        ideal = oracle.ideal_rows(q[0, :, h], k[0, :, oracle.kv_head(h, Hq, Hkv)], T, scale, cnt,
+                                  rows)
         got = [ret[name][h, i * T:(i + 1) * T].mean() for i in rows]
         best = [ideal[i][1].mean() for i in rows]
         for g_, b_ in zip(got, best):
@@ -95,10 +124,9 @@ def test_spike_recall_at_matched_density():
     branch keeps every spike block and the merged selector more of them than
     the centroid branch alone at about the same density.  The GPU masks'
     recall equals the oracle selector's on the same inputs."""
-    inp, sel, ret = case()
+    inp, sel, ret, _ = case()
     q, k = workloads.to_f64(inp["q"]), workloads.to_f64(inp["k"])
     nB = S // T
-    G = Hq // Hkv
     params = {"merged": (0.10, 0.04), "centroid": (0.14, -1.0), "rescue": (-1.0, 0.14)}
     recall = {}
     for name, (pc, pr) in params.items():
@@ -106,7 +134,7 @@ def test_spike_recall_at_matched_density():
         masks = {}
         for g in range(Hkv):
             c, r = oracle.block_stats(k[0, :, g], T)
-            for h in range(g * G, (g + 1) * G):
+            for h in [x for x in range(Hq) if oracle.kv_head(x, Hq, Hkv) == g]:
                 masks[h] = oracle.select_blocks(oracle.pool_queries(q[0, :, h], T), c, r, pc, pr)["M"]
         for (b, g, tok, h, i) in inp["spikes"]:
             gm = lists_to_mask(sel[name]["block_idx"][0, h].numpy(), sel[name]["block_cnt"][0, h].numpy(), nB)
@@ -129,7 +157,7 @@ def test_block_mass_and_ideal_selection_match_oracle():
     rounding tolerance)."""
     import bench
     import free_sparse_attention_head_amd as fsa
-    inp, sel, _ = case()
+    inp, sel, _, _ = case()
     q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
     _, lse_d = fsa.sparse_prefill_attn(q, k, v, T)
     mass = bench.block_mass(fsa, q, k, v, T, lse_d).cpu().double().numpy()   # [Hq, nB, nB]
@@ -142,7 +170,7 @@ def test_block_mass_and_ideal_selection_match_oracle():
     rows = list(range(0, nB, 5))
     worst = 0.0
     for h in (0, Hq - 1):
-        g = h // (Hq // Hkv)
+        g = oracle.kv_head(h, Hq, Hkv)
         ref = oracle.token_block_mass(q64[0, :, h], k64[0, :, g], T, scale, rows)
         ideal = oracle.ideal_rows(q64[0, :, h], k64[0, :, g], T, scale, cnt_i[0, h], rows)
         for i in rows:

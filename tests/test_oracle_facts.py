@@ -17,9 +17,10 @@ import pytest
 import torch
 
 import oracle
-from oracle import (block_stats, build_segments, dense_attention, gather_pages, ideal_rows,
-                    index_attention, lse_combine, masked_attention, pool_queries, retention,
-                    segment_attention, select_blocks, token_block_mass, topk, topk_pooled)
+from oracle import (anchor_scores, anchor_topk, block_stats, build_segments, dense_attention,
+                    gather_pages, ideal_rows, index_attention, index_mass, kv_head, lse_combine,
+                    masked_attention, pool_queries, retention, segment_attention, select_blocks,
+                    set_recall, token_block_mass, topk, topk_pooled, union_sets)
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -559,3 +560,99 @@ def test_Q3_ideal_rows_brute_force_over_block_subsets():
         blocks, ret = ideal[i]
         assert tuple(blocks) == best_set
         assert abs(ret.mean() - best) < 1e-12
+
+
+# ---- anchor-layer scores and the GQA head mapping (Kascade post, "What
+# Kascade got right": the anchor scores every cached key; "Head-aware is the
+# key to accuracy": per attention head)
+
+def test_kv_head_matches_library_gqa_attention():
+    """Query heads attending through kv_head equal torch's grouped-query SDPA
+    (enable_gqa: consecutive query heads share a KV head), which a mapping
+    h % Hkv (interleaved heads) or any other grouping would break."""
+    rng = _rng(41)
+    Hq, Hkv, N, D = 8, 2, 11, 4
+    q = rng.standard_normal((Hq, D))
+    k = rng.standard_normal((Hkv, N, D))
+    v = rng.standard_normal((Hkv, N, 3))
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))[None]
+    lib = torch.nn.functional.scaled_dot_product_attention(
+        t(q[:, None, :]), t(k), t(v), scale=0.5, enable_gqa=True)[0, :, 0].numpy()
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        o, _ = index_attention(q[h], k[g], v[g], np.arange(N), 0.5)
+        assert np.abs(o - lib[h]).max() <= 1e-12
+    assert [kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [kv_head(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]
+    with pytest.raises(ValueError):
+        kv_head(0, 6, 4)
+
+
+def test_anchor_scores_closed_forms_brute_force_and_library_softmax():
+    """Basis keys read the query's coordinates back; scores equal scalar
+    math.fsum dot products; their softmax equals torch SDPA with identity
+    values (the attention weights themselves), which a dropped coordinate, a
+    flipped sign or a transposed operand would break."""
+    rng = _rng(42)
+    D, N = 6, 9
+    q = rng.standard_normal(D)
+    basis = np.zeros((N, D))
+    for j in range(N):
+        basis[j, j % D] = j + 1.0
+    s = anchor_scores(q, basis)
+    assert np.array_equal(s, np.array([(j + 1.0) * q[j % D] for j in range(N)]))
+    K = rng.standard_normal((N, D))
+    s = anchor_scores(q, K)
+    for j in range(N):
+        assert abs(s[j] - math.fsum(q[d] * K[j, d] for d in range(D))) <= 1e-14
+    w = _sdpa(q[None], K, np.eye(N), 0.8, causal=False)[0]
+    p = np.exp(0.8 * s - (0.8 * s).max())
+    assert np.abs(p / p.sum() - w).max() <= 1e-13
+    idx, kth = anchor_topk(q, K, 3)
+    assert list(idx) == sorted(np.argsort(-s, kind="stable")[:3].tolist())
+    assert kth == np.sort(s)[-3]
+
+
+# ---- GQA-shared index sets (Kascade post, "Head-aware is the key to
+# accuracy": per-head sets versus one set shared by a KV head's query heads)
+
+def test_union_sets_brute_force_and_closed_forms():
+    rng = _rng(43)
+    sets = [np.sort(rng.choice(200, 30, replace=False)) for _ in range(4)]
+    u = union_sets(sets)
+    want = set()
+    for x in sets:
+        want |= set(x.tolist())
+    assert u.tolist() == sorted(want)
+    assert (np.diff(u) > 0).all()
+    for x in sets:
+        assert set(x.tolist()) <= set(u.tolist())
+    assert union_sets([np.arange(5), np.arange(5, 9)]).tolist() == list(range(9))
+    assert union_sets([np.arange(5), np.arange(5)]).tolist() == list(range(5))
+    assert union_sets([np.array([3, -1, -1]), np.array([-1, 2, -1])]).tolist() == [2, 3]
+
+
+def test_set_recall_closed_forms():
+    assert set_recall(np.arange(10), np.arange(20)) == 1.0
+    assert set_recall(np.arange(10), np.arange(10, 20)) == 0.0
+    assert set_recall(np.arange(10), np.arange(5, 15)) == 0.5
+    assert set_recall(np.array([0, 1, -1, -1]), np.array([1, 7])) == 0.5
+    with pytest.raises(ValueError):
+        set_recall(np.array([-1, -1]), np.arange(3))
+
+
+def test_index_mass_full_set_complement_and_library_weights():
+    """Every key listed -> mass 1; a set and its complement split the mass;
+    the mass equals torch SDPA's attention weights (identity values) summed
+    over the set; duplicates and empty slots do not count twice."""
+    rng = _rng(44)
+    N, D, scale = 40, 8, 0.6
+    q, K = rng.standard_normal(D), rng.standard_normal((N, D))
+    assert abs(index_mass(q, K, np.arange(N), scale) - 1.0) <= 1e-12
+    sel = np.sort(rng.choice(N, 13, replace=False))
+    rest = np.setdiff1d(np.arange(N), sel)
+    assert abs(index_mass(q, K, sel, scale) + index_mass(q, K, rest, scale) - 1.0) <= 1e-12
+    w = _sdpa(q[None], K, np.eye(N), scale, causal=False)[0]
+    assert abs(index_mass(q, K, sel, scale) - w[sel].sum()) <= 1e-12
+    dup = np.concatenate([sel, sel[:4], [-1, -1]])
+    assert abs(index_mass(q, K, dup, scale) - w[sel].sum()) <= 1e-12

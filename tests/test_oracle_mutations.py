@@ -102,6 +102,43 @@ def _ideal_keeps_least(q, k, T, scale, counts, rows):
     return out
 
 
+def _kv_head_interleaved(h, Hq, Hkv):
+    return h % Hkv
+
+
+def _scores_drop_last_coordinate(q, kseq):
+    q = np.asarray(q, dtype=np.float64)
+    kseq = np.asarray(kseq, dtype=np.float64)
+    return kseq[:, :-1] @ q[:-1]
+
+
+def _scores_sign_flipped(q, kseq):
+    return -(np.asarray(kseq, dtype=np.float64) @ np.asarray(q, dtype=np.float64))
+
+
+def _union_keeps_intersection(sets):
+    keep = None
+    for s in sets:
+        x = {int(v) for v in np.asarray(s).ravel() if v >= 0}
+        keep = x if keep is None else keep & x
+    return np.array(sorted(keep), dtype=np.int64)
+
+
+def _recall_over_shared(own, shared):
+    own = {int(x) for x in np.asarray(own).ravel() if x >= 0}
+    shared = {int(x) for x in np.asarray(shared).ravel() if x >= 0}
+    return len(own & shared) / len(shared)
+
+
+def _mass_renormalised_over_set(q, kseq, idx, scale):
+    q, kseq = np.asarray(q, dtype=np.float64), np.asarray(kseq, dtype=np.float64)
+    idx = np.unique(np.asarray(idx, dtype=np.int64))
+    idx = idx[idx >= 0]
+    s = scale * (kseq[idx] @ q)
+    p = np.exp(s - s.max())
+    return float((p / p.sum()).sum())
+
+
 CASES = [
     ("select_blocks", _rescue_sign_flipped,
      [pins.test_F4_planted_spike_dropped_by_centroid_recovered_by_rescue]),
@@ -123,6 +160,15 @@ CASES = [
     ("retention", _retention_of_complement,
      [pins.test_Q1_full_mask_retains_everything_and_complement_sums_to_one]),
     ("ideal_rows", _ideal_keeps_least, [pins.test_Q3_ideal_rows_brute_force_over_block_subsets]),
+    ("kv_head", _kv_head_interleaved, [pins.test_kv_head_matches_library_gqa_attention]),
+    ("anchor_scores", _scores_drop_last_coordinate,
+     [pins.test_anchor_scores_closed_forms_brute_force_and_library_softmax]),
+    ("anchor_scores", _scores_sign_flipped,
+     [pins.test_anchor_scores_closed_forms_brute_force_and_library_softmax]),
+    ("union_sets", _union_keeps_intersection, [pins.test_union_sets_brute_force_and_closed_forms]),
+    ("set_recall", _recall_over_shared, [pins.test_set_recall_closed_forms]),
+    ("index_mass", _mass_renormalised_over_set,
+     [pins.test_index_mass_full_set_complement_and_library_weights]),
 ]
 
 
