@@ -40,6 +40,41 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+# Argument checks.  The library receives raw pointers and trusts the shapes it
+# is given, so every tensor is checked against them here, before any call:
+# a wrong dtype or a short buffer would otherwise be read or written past its
+# end on the device.
+
+def _need(t, name, dtype=None, shape=None, ndim=None):
+    """Raise ValueError unless tensor t has the given dtype / shape / rank."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+_FLOATS = (torch.bfloat16, torch.float32)
+
+
+def _same_device(ref, *ts):
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"every tensor must live on {ref.device}, found one on {t.device}")
+
+
+def _same_dtype(ref, *named):
+    for t, name in named:
+        if t.dtype != ref.dtype:
+            raise ValueError(f"{name} must have the query's dtype {ref.dtype}, got {t.dtype}")
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -86,13 +121,19 @@ def block_stats(k, T, centroid=None, radius=None):
     """Centroid [B,Hkv,nB,D] and radius [B,Hkv,nB] (fp32) of every key block of
     k [B,S,Hkv,D] (bf16 or fp32)."""
     lib = L.load()
+    _need(k, "k", _FLOATS, ndim=4)
     B, S, Hkv, D = k.shape
+    if T <= 0 or S % T:
+        raise ValueError("the prompt length must be a multiple of the block size")
     nB = S // T
     shape = L.PrefillShape(B, S, Hkv, Hkv, D, T)
     if centroid is None:
         centroid = torch.empty((B, Hkv, nB, D), dtype=torch.float32, device=k.device)
     if radius is None:
         radius = torch.empty((B, Hkv, nB), dtype=torch.float32, device=k.device)
+    _need(centroid, "centroid", torch.float32, (B, Hkv, nB, D))
+    _need(radius, "radius", torch.float32, (B, Hkv, nB))
+    _same_device(k, centroid, radius)
     L.check("block_stats", lib.block_stats(_dtype_code(k), _ptr(k), ctypes.byref(shape),
                                            _ptr(centroid), _ptr(radius), _stream(k.device)))
     return centroid, radius
@@ -104,9 +145,15 @@ def select_blocks(q, centroid, radius, T, p_centroid, p_rescue, band_blocks=0, s
     Returns dict(mask [B,Hq,nB,ceil(nB/32)] int32 view of uint32 bits,
     block_idx [B,Hq,nB,nB], block_cnt [B,Hq,nB], score_c, score_r)."""
     lib = L.load()
+    _need(q, "q", _FLOATS, ndim=4)
     B, S, Hq, D = q.shape
-    Hkv = centroid.shape[1]
+    if T <= 0 or S % T:
+        raise ValueError("the prompt length must be a multiple of the block size")
     nB = S // T
+    _need(centroid, "centroid", torch.float32, ndim=4)
+    Hkv = centroid.shape[1]
+    _need(centroid, "centroid", shape=(B, Hkv, nB, D))
+    _need(radius, "radius", torch.float32, (B, Hkv, nB))
     shape = L.PrefillShape(B, S, Hq, Hkv, D, T)
     params = L.SelectParams(float(p_centroid), float(p_rescue), int(band_blocks), int(sink_blocks))
     dev = q.device
@@ -120,10 +167,14 @@ def select_blocks(q, centroid, radius, T, p_centroid, p_rescue, band_blocks=0, s
     bcnt = o.get("block_cnt")
     if bcnt is None:
         bcnt = torch.empty((B, Hq, nB), dtype=torch.int32, device=dev)
+    _need(mask, "mask", torch.int32, (B, Hq, nB, (nB + 31) // 32))
+    _need(bidx, "block_idx", torch.int32, (B, Hq, nB, nB))
+    _need(bcnt, "block_cnt", torch.int32, (B, Hq, nB))
     sc = sr = None
     if want_scores:
         sc = torch.full((B, Hq, nB, nB), float("nan"), dtype=torch.float32, device=dev)
         sr = torch.full((B, Hq, nB, nB), float("nan"), dtype=torch.float32, device=dev)
+    _same_device(q, centroid, radius, mask, bidx, bcnt, ws)
     wsb = workspace_size("select", shape)
     ws, wsn = _ws(wsb, dev, ws)
     L.check("select_blocks", lib.select_blocks(
@@ -138,25 +189,52 @@ def sparse_prefill_attn(q, k, v, T, block_idx=None, block_cnt=None, scale=None, 
     """Block-sparse causal attention; block_idx None means dense causal.
     Returns (out [B,S,Hq,D] in q's dtype, lse [B,Hq,S] fp32 or None)."""
     lib = L.load()
+    _need(q, "q", _FLOATS, ndim=4)
     B, S, Hq, D = q.shape
+    _need(k, "k", ndim=4)
+    _same_dtype(q, (k, "k"), (v, "v"))
+    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
+        raise ValueError(f"k must be [B, S, Hkv, D] = [{B}, {S}, Hkv, {D}], got {tuple(k.shape)}")
+    _need(v, "v", shape=k.shape)
+    if T <= 0 or S % T:
+        raise ValueError("the prompt length must be a multiple of the block size")
+    nB = S // T
+    if (block_idx is None) != (block_cnt is None):
+        raise ValueError("block_idx and block_cnt go together")
+    if block_idx is not None:
+        _need(block_idx, "block_idx", torch.int32, (B, Hq, nB, nB))
+        _need(block_cnt, "block_cnt", torch.int32, (B, Hq, nB))
     shape = _prefill_shape(q, k, T)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     if not want_lse:
         lse = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, S))
+    _same_device(q, k, v, block_idx, block_cnt, out, lse)
     L.check("sparse_prefill_attn", lib.sparse_prefill_attn(
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(shape), _ptr(block_idx),
         _ptr(block_cnt), float(scale), _ptr(out), _ptr(lse), None, 0, _stream(q.device)))
     return out, lse
 
 
-def _decode_shape(q, k_pool, page_table, max_seq_len):
+def _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens=None):
+    _need(q, "q", torch.bfloat16, ndim=3)
     B, Hq, D = q.shape
-    num_pages, Hkv, P, _ = k_pool.shape
+    _need(k_pool, "k_pool", torch.bfloat16, ndim=4)
+    num_pages, Hkv, P, Dk = k_pool.shape
+    if Dk != D:
+        raise ValueError(f"k_pool head dim {Dk} differs from the query's {D}")
+    _need(page_table, "page_table", torch.int32, ndim=2)
+    if page_table.shape[0] != B:
+        raise ValueError(f"page_table must have {B} rows, got {page_table.shape[0]}")
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32, (B,))
     max_pages = page_table.shape[1]
     if max_seq_len is None:
         max_seq_len = P * max_pages
@@ -165,12 +243,15 @@ def _decode_shape(q, k_pool, page_table, max_seq_len):
 
 def _topk(name, rows, q, k_pool, page_table, seq_lens, k, max_seq_len, idx, kth, ws):
     lib = L.load()
-    shape = _decode_shape(q, k_pool, page_table, max_seq_len)
+    shape = _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
     B = q.shape[0]
     if idx is None:
         idx = torch.empty((B, rows, k), dtype=torch.int32, device=q.device)
     if kth is None:
         kth = torch.empty((B, rows), dtype=torch.float32, device=q.device)
+    _need(idx, "idx", torch.int32, (B, rows, k))
+    _need(kth, "kth", torch.float32, (B, rows))
+    _same_device(q, k_pool, page_table, seq_lens, idx, kth, ws)
     wsb = workspace_size("topk", shape, int(k))
     ws, wsn = _ws(wsb, q.device, ws)
     L.check(name, getattr(lib, name)(
@@ -197,17 +278,35 @@ def topk_indices_kv(q, k_pool, page_table, seq_lens, k, max_seq_len=None, idx=No
                  max_seq_len, idx, kth, ws)
 
 
-def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, idx=None,
-                       segments=None, n_seg=None, scale=None, n_split=0, max_seq_len=None,
-                       want_lse=True, out=None, lse=None, ws=None):
-    """Split-KV paged decode attention.  mode SEL_ALL / SEL_INDEX (idx [B,Hq,k]) /
-    SEL_INDEX_KV (idx [B,Hkv,k]) / SEL_SEGMENT (segments [B,max_seg,2], n_seg [B]).
-    Returns (out bf16 [B,Hq,D], lse fp32 [B,Hq] or None)."""
-    lib = L.load()
-    shape = _decode_shape(q, k_pool, page_table, max_seq_len)
+def _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments, n_seg, n_split,
+                 max_seq_len, want_lse, out, lse):
+    """Checks of a decode call's tensors; returns (KvSelect, out, lse)."""
+    _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
     B, Hq, D = q.shape
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+    Hkv = k_pool.shape[1]
+    _need(v_pool, "v_pool", torch.bfloat16, k_pool.shape)
+    if mode in (SEL_INDEX, SEL_INDEX_KV):
+        _need(idx, "idx", torch.int32, ndim=3)
+        heads = Hq if mode == SEL_INDEX else Hkv
+        if idx.shape[0] != B or idx.shape[1] != heads:
+            raise ValueError(f"idx must be [{B}, {heads}, k], got {tuple(idx.shape)}")
+    elif mode == SEL_SEGMENT:
+        _need(segments, "segments", torch.int32, ndim=3)
+        if segments.shape[0] != B or segments.shape[2] != 2:
+            raise ValueError(f"segments must be [{B}, max_seg, 2], got {tuple(segments.shape)}")
+        _need(n_seg, "n_seg", torch.int32, (B,))
+    elif mode != SEL_ALL:
+        raise ValueError(f"unknown mode {mode}")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, Hq, D))
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if not want_lse:
+        lse = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq))
+    _same_device(q, k_pool, v_pool, page_table, seq_lens, idx, segments, n_seg, out, lse)
     sel = L.KvSelect(int(mode), None, 0, None, None, 0, int(n_split))
     if mode in (SEL_INDEX, SEL_INDEX_KV):
         sel.idx = _ptr(idx).value
@@ -216,12 +315,22 @@ def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, id
         sel.segments = _ptr(segments).value
         sel.n_seg = _ptr(n_seg).value
         sel.max_seg = segments.shape[1]
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if not want_lse:
-        lse = None
+    return sel, out, lse
+
+
+def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, idx=None,
+                       segments=None, n_seg=None, scale=None, n_split=0, max_seq_len=None,
+                       want_lse=True, out=None, lse=None, ws=None):
+    """Split-KV paged decode attention.  mode SEL_ALL / SEL_INDEX (idx [B,Hq,k]) /
+    SEL_INDEX_KV (idx [B,Hkv,k]) / SEL_SEGMENT (segments [B,max_seg,2], n_seg [B]).
+    Returns (out bf16 [B,Hq,D], lse fp32 [B,Hq] or None)."""
+    lib = L.load()
+    sel, out, lse = _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments,
+                                 n_seg, n_split, max_seq_len, want_lse, out, lse)
+    shape = _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
+    D = q.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
     wsb = workspace_size("decode", shape, sel)
     ws, wsn = _ws(wsb, q.device, ws)
     L.check("sparse_decode_attn", lib.sparse_decode_attn(

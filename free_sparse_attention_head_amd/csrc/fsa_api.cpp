@@ -185,7 +185,9 @@ int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* 
   if ((rc = check_dtype_prefill(dt))) return rc;
   if (!q || !k || !v || !out) return FSA_ERR_NULL;
   if ((block_idx == nullptr) != (block_cnt == nullptr)) return FSA_ERR_NULL;
-  if (!isfinite(scale)) return FSA_ERR_ARG;
+  // the kernels track the running row maximum in unscaled score units, which
+  // orders scaled scores the same way only for a positive scale
+  if (!isfinite(scale) || !(scale > 0.f)) return FSA_ERR_ARG;
   if ((rc = device_check())) return rc;
   return launch_status(fsa::launch_prefill_attn(dt == FSA_F32, q, k, v, d, block_idx, block_cnt,
                                                 scale, out, lse, st));

@@ -151,7 +151,8 @@ int select_blocks(fsa_dtype dt, const void* q, const float* centroid, const floa
  * outside [0, i] are skipped.  block_idx == NULL (and block_cnt == NULL)
  * means every causal block (dense causal attention).  bf16 inputs use bf16
  * MFMA with fp32 accumulation and an fp32 online softmax; fp32 inputs use
- * fp32 MFMA throughout.  An empty list gives O = 0, lse = -inf.
+ * fp32 MFMA throughout.  An empty list gives O = 0, lse = -inf.  scale must
+ * be finite and > 0 (else FSA_ERR_ARG).
  *   q (device) [B,S,Hq,D]; k, v (device) [B,S,Hkv,D]; all of dtype dt
  *   out (device) [B,S,Hq,D] dtype dt; lse (device, nullable) fp32 [B,Hq,S]
  *   (natural log).  ws may be NULL when the workspace size is 0. */

@@ -228,3 +228,66 @@ def test_missing_device_is_reported_not_crashed():
     s = _shape(L)
     rc = lib.block_stats(L.FSA_BF16, FAKE, ctypes.byref(s), FAKE, FAKE, None)
     assert rc == L.FSA_ERR_NO_DEVICE
+
+
+def test_prefill_scale_must_be_positive():
+    """The kernels order scores by their unscaled values, which agrees with
+    the scaled order only for scale > 0."""
+    L, lib = _lib()
+    s = _shape(L)
+    for bad in (0.0, -0.125, float("nan")):
+        assert lib.sparse_prefill_attn(L.FSA_BF16, FAKE, FAKE, FAKE, ctypes.byref(s), None, None,
+                                       bad, FAKE, None, None, 0, None) == L.FSA_ERR_ARG
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python binding checks dtypes and shapes against each other before
+    any pointer reaches the library (CPU tensors: every rejection happens
+    before the device is touched)."""
+    import torch
+    import free_sparse_attention_head_amd as fsa
+    B, S, Hq, Hkv, D, T = 1, 256, 4, 2, 64, 64
+    nB = S // T
+    q = torch.zeros((B, S, Hq, D), dtype=torch.float32)
+    k = torch.zeros((B, S, Hkv, D), dtype=torch.bfloat16)
+    v = torch.zeros((B, S, Hkv, D), dtype=torch.bfloat16)
+    bidx = torch.zeros((B, Hq, nB, nB), dtype=torch.int32)
+    bcnt = torch.zeros((B, Hq, nB), dtype=torch.int32)
+
+    def rejects(fn, what):
+        with pytest.raises(ValueError, match=what):
+            fn()
+
+    rejects(lambda: fsa.sparse_prefill_attn(q, k, v, T), "dtype")            # fp32 q, bf16 k/v
+    qb = q.to(torch.bfloat16)
+    rejects(lambda: fsa.sparse_prefill_attn(qb, k, v[:, :128], T), "shape")  # short v
+    rejects(lambda: fsa.sparse_prefill_attn(qb, k[:, :128], v[:, :128], T), "k must be")
+    rejects(lambda: fsa.sparse_prefill_attn(qb, k, v, T, bidx[:, :, :2], bcnt), "block_idx")
+    rejects(lambda: fsa.sparse_prefill_attn(qb, k, v, T, bidx.long(), bcnt), "block_idx")
+    rejects(lambda: fsa.sparse_prefill_attn(qb, k, v, T, bidx, None), "together")
+    rejects(lambda: fsa.sparse_prefill_attn(qb, k, v, 100), "multiple")
+    c = torch.zeros((B, Hkv, nB, D), dtype=torch.float32)
+    r = torch.zeros((B, Hkv, nB), dtype=torch.float32)
+    rejects(lambda: fsa.select_blocks(qb, c.double(), r, T, 0.1, 0.04), "centroid")
+    rejects(lambda: fsa.select_blocks(qb, c, r[:, :, :2], T, 0.1, 0.04), "radius")
+    rejects(lambda: fsa.block_stats(k, T, centroid=c[:, :, :1]), "centroid")
+    # decode
+    Bd, N, P = 2, 512, 16
+    qd = torch.zeros((Bd, 8, 128), dtype=torch.bfloat16)
+    pool = torch.zeros((64, 2, P, 128), dtype=torch.bfloat16)
+    pt = torch.zeros((Bd, N // P), dtype=torch.int32)
+    sl = torch.full((Bd,), N, dtype=torch.int32)
+    idx = torch.zeros((Bd, 8, 16), dtype=torch.int64)
+    rejects(lambda: fsa.sparse_decode_attn(qd, pool, pool, pt, sl, mode=fsa.SEL_INDEX, idx=idx), "idx")
+    rejects(lambda: fsa.sparse_decode_attn(qd, pool, pool, pt, sl, mode=fsa.SEL_INDEX_KV,
+                                           idx=idx.int()), r"idx must be \[2, 2, k\]")
+    rejects(lambda: fsa.sparse_decode_attn(qd, pool, pool[:32], pt, sl), "v_pool")
+    rejects(lambda: fsa.sparse_decode_attn(qd.float(), pool, pool, pt, sl), "q must be")
+    rejects(lambda: fsa.sparse_decode_attn(qd, pool, pool, pt.long(), sl), "page_table")
+    rejects(lambda: fsa.sparse_decode_attn(qd, pool, pool, pt, sl[:1]), "seq_lens")
+    rejects(lambda: fsa.sparse_decode_attn(qd, pool, pool, pt, sl, mode=fsa.SEL_SEGMENT,
+                                           segments=torch.zeros((Bd, 2, 3), dtype=torch.int32),
+                                           n_seg=sl), "segments")
+    rejects(lambda: fsa.topk_indices(qd, pool[..., :64], pt, sl, 16), "head dim")
+    rejects(lambda: fsa.topk_indices(qd, pool, pt, sl, 16, idx=torch.zeros((Bd, 8, 8), dtype=torch.int32)),
+            "idx")
