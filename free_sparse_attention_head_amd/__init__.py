@@ -21,7 +21,7 @@ import torch
 from . import _lib as L
 
 __all__ = ["block_stats", "select_blocks", "sparse_prefill_attn", "topk_indices",
-           "topk_indices_kv", "sparse_decode_attn", "build_segments", "workspace_size", "FsaError",
+           "topk_indices_kv", "sparse_decode_attn", "sparse_decode_attn_noalloc", "build_segments", "workspace_size", "FsaError",
            "SEL_ALL", "SEL_INDEX", "SEL_SEGMENT", "SEL_INDEX_KV", "SEG_GLOBAL", "SEG_FOCUS",
            "SEG_LOCAL", "SEG_STREAMING"]
 
@@ -337,6 +337,26 @@ def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, id
         _dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(seq_lens),
         ctypes.byref(shape), ctypes.byref(sel), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
         wsn, _stream(q.device)))
+    return out, lse
+
+
+def sparse_decode_attn_noalloc(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, idx=None,
+                               segments=None, n_seg=None, scale=None, n_split=0,
+                               max_seq_len=None, want_lse=True, out=None, lse=None):
+    """sparse_decode_attn without a workspace: the library keeps the split
+    partials in its own device array (FSA_NOALLOC_SCRATCH_BYTES per GPU).
+    Calls that overlap on one GPU race.  Pass out (and lse) to allocate
+    nothing here either."""
+    lib = L.load()
+    sel, out, lse = _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments,
+                                 n_seg, n_split, max_seq_len, want_lse, out, lse)
+    shape = _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[2])
+    L.check("sparse_decode_attn_noalloc", lib.sparse_decode_attn_noalloc(
+        _dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(seq_lens),
+        ctypes.byref(shape), ctypes.byref(sel), float(scale), _ptr(out), _ptr(lse),
+        _stream(q.device)))
     return out, lse
 
 

@@ -16,6 +16,7 @@ FSA_BF16, FSA_F32 = 0, 1
 FSA_SEL_ALL, FSA_SEL_INDEX, FSA_SEL_SEGMENT, FSA_SEL_INDEX_KV = 0, 1, 2, 3
 FSA_OP_SELECT_BLOCKS, FSA_OP_PREFILL_ATTN, FSA_OP_TOPK, FSA_OP_DECODE_ATTN = 1, 2, 3, 4
 FSA_SEG_GLOBAL, FSA_SEG_FOCUS, FSA_SEG_LOCAL, FSA_SEG_STREAMING = 0, 1, 2, 3
+FSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 c_int, c_float, c_double, c_size_t, c_void_p = (ctypes.c_int, ctypes.c_float, ctypes.c_double,
                                                  ctypes.c_size_t, ctypes.c_void_p)
@@ -61,6 +62,10 @@ SIGNATURES = {
     "sparse_decode_attn": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    ctypes.POINTER(DecodeShape), ctypes.POINTER(KvSelect),
                                    c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "sparse_decode_attn_noalloc": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, ctypes.POINTER(DecodeShape),
+                                           ctypes.POINTER(KvSelect), c_float, c_void_p, c_void_p,
+                                           c_void_p]),
     "fsa_workspace_size": (c_size_t, [c_int, c_void_p, c_void_p]),
     "fsa_build_segments": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int32_p,
                                    ctypes.POINTER(c_int)]),

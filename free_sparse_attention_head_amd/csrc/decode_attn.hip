@@ -30,6 +30,8 @@
 //     normalises and writes the output itself.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -398,6 +400,44 @@ hipError_t launch_decode_attn(const void* q, const void* kpool, const void* vpoo
     return launch_dec_d<64>(q, kpool, vpool, pt, sl, d, mode, idx, k, seg, nseg, max_seg, ns,
                             sl2, out, lse, part, st);
   return hipErrorInvalidValue;
+}
+
+
+// ---- the variant that allocates nothing ---------------------------------
+//
+// Callers that cannot allocate device memory (code under HIP graph capture,
+// serving loops that forbid it) get the split partials from a file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): the device address is looked up once per device, with that
+// device current, and kept.  Every call on a GPU shares that GPU's array, so
+// calls that overlap on one GPU race.  Nothing in it has to start at zero:
+// every split of a launch writes its partial before the combine reads it.
+namespace {
+
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fsa

@@ -1,6 +1,8 @@
 // C-ABI layer of the library: host-side validation, workspace sizing, device
 // check and dispatch to the kernel launchers.  No allocation, no global
-// mutable state besides the per-device "is gfx950" cache.
+// mutable state besides the per-device "is gfx950" cache (and, in
+// decode_attn.hip, the per-device address of the allocation-free entry
+// point's array).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <string.h>
@@ -241,6 +243,29 @@ int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const vo
                                                sel->mode, sel->idx, sel->k, sel->segments,
                                                sel->n_seg, sel->max_seg, sel->n_split, scale, out,
                                                lse, ws, st));
+}
+
+int sparse_decode_attn_noalloc(fsa_dtype dt, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* page_table,
+                               const int32_t* seq_lens, const fsa_decode_shape* s,
+                               const fsa_kv_select* sel, float scale, void* out, float* lse,
+                               hipStream_t st) {
+  DecodeDims d;
+  int rc = check_decode_shape(s, &d);
+  if (rc) return rc;
+  if (dt != FSA_BF16) return FSA_ERR_DTYPE;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return FSA_ERR_NULL;
+  if ((rc = check_kv_select(sel, d))) return rc;
+  if (!isfinite(scale)) return FSA_ERR_ARG;
+  if (fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split) > fsa::kNoAllocScratchBytes)
+    return FSA_ERR_WORKSPACE;
+  if ((rc = device_check())) return rc;
+  void* scratch = nullptr;
+  if (fsa::noalloc_scratch(&scratch) != hipSuccess) return FSA_ERR_NO_DEVICE;
+  return launch_status(fsa::launch_decode_attn(q, k_pool, v_pool, page_table, seq_lens, d,
+                                               sel->mode, sel->idx, sel->k, sel->segments,
+                                               sel->n_seg, sel->max_seg, sel->n_split, scale, out,
+                                               lse, scratch, st));
 }
 
 int fsa_build_segments(int mode, int n, int chunk_start, int chunk_len, int local_len,

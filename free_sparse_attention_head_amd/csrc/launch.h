@@ -51,6 +51,11 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
                        hipStream_t st);
 
 // decode_attn.hip
+// bytes of the device array that the allocation-free decode entry point uses
+// for split partials (one per GPU)
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+// device address of this GPU's array (looked up once per device)
+hipError_t noalloc_scratch(void** ptr);
 int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split);
 size_t decode_ws_bytes(const DecodeDims& d, int mode, int k, int n_split);
 hipError_t launch_decode_attn(const void* q, const void* kpool, const void* vpool,

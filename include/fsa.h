@@ -17,7 +17,9 @@
  *     launch failures are reported as FSA_ERR_LAUNCH, device faults surface
  *     at the caller's next synchronisation.
  *   - Calls are re-entrant; consecutive calls on one stream see each other's
- *     results (stream order).  The library keeps no mutable global state.
+ *     results (stream order).  The library keeps no mutable global state,
+ *     apart from a per-device "is gfx950" cache and the per-GPU device array
+ *     that sparse_decode_attn_noalloc alone uses (see there).
  *
  * Prefill shapes: batch B, prompt length S, query heads Hq, KV heads Hkv
  * (Hq % Hkv == 0, G = Hq / Hkv, query head h reads KV head h / G), head dim
@@ -208,6 +210,24 @@ int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const vo
                        const int32_t* page_table, const int32_t* seq_lens,
                        const fsa_decode_shape* s, const fsa_kv_select* sel, float scale,
                        void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st);
+
+/* sparse_decode_attn_noalloc -- sparse_decode_attn without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops and harnesses that forbid allocation.  Arguments, results and
+ * errors are those of sparse_decode_attn; the split partials live instead in
+ * a library-owned device array of FSA_NOALLOC_SCRATCH_BYTES (16 MiB) per
+ * GPU, held from the first call on that GPU until the process ends.  The
+ * call allocates nothing.  It returns FSA_ERR_WORKSPACE when the partials
+ * (fsa_workspace_size(FSA_OP_DECODE_ATTN, ...) bytes) would exceed the array.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (several streams, or several host threads) race and must be ordered
+ * by the caller. */
+#define FSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int sparse_decode_attn_noalloc(fsa_dtype dt, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* page_table,
+                               const int32_t* seq_lens, const fsa_decode_shape* s,
+                               const fsa_kv_select* sel, float scale, void* out, float* lse,
+                               hipStream_t st);
 
 /* ---- helpers --------------------------------------------------------------- */
 

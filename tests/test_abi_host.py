@@ -240,6 +240,21 @@ def test_prefill_scale_must_be_positive():
                                        bad, FAKE, None, None, 0, None) == L.FSA_ERR_ARG
 
 
+def test_noalloc_entry_point_validation():
+    """sparse_decode_attn_noalloc: the checks of sparse_decode_attn, and split
+    partials beyond its 16 MiB array are refused before any device work."""
+    L, lib = _lib()
+    s = _dshape(L, B=2, Hq=32, Hkv=8)
+    call = lambda sel, dt=L.FSA_BF16: lib.sparse_decode_attn_noalloc(
+        dt, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(sel), 0.1, FAKE, None,
+        None)
+    big = L.KvSelect(L.FSA_SEL_ALL, None, 0, None, None, 0, 1024)   # 34 MB of partials
+    assert call(big) == L.FSA_ERR_WORKSPACE
+    assert call(L.KvSelect(L.FSA_SEL_INDEX, None, 16, None, None, 0, 0)) == L.FSA_ERR_NULL
+    assert call(L.KvSelect(L.FSA_SEL_ALL, None, 0, None, None, 0, 2), dt=L.FSA_F32) == L.FSA_ERR_DTYPE
+    assert L.FSA_NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
 def test_binding_rejects_mismatched_tensors():
     """The Python binding checks dtypes and shapes against each other before
     any pointer reaches the library (CPU tensors: every rejection happens
@@ -290,4 +305,6 @@ def test_binding_rejects_mismatched_tensors():
                                            n_seg=sl), "segments")
     rejects(lambda: fsa.topk_indices(qd, pool[..., :64], pt, sl, 16), "head dim")
     rejects(lambda: fsa.topk_indices(qd, pool, pt, sl, 16, idx=torch.zeros((Bd, 8, 8), dtype=torch.int32)),
+            "idx")
+    rejects(lambda: fsa.sparse_decode_attn_noalloc(qd, pool, pool, pt, sl, mode=fsa.SEL_INDEX, idx=idx),
             "idx")
