@@ -134,14 +134,39 @@ def time_attention(fsa, pf, P, reps=20):
             "frac_peak": round(flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
+def shared_set_recall(own, shared, G):
+    """Per query head, the share of its own index set (own [B,Hq,k], -1 =
+    empty) found in its KV head's shared set (shared [B,Hkv,m], ascending
+    valid entries, then -1).  Returns [B,Hq] float."""
+    big = torch.iinfo(torch.int32).max
+    sh = torch.where(shared < 0, torch.full_like(shared, big), shared)
+    sh = sh.repeat_interleave(G, dim=1).contiguous()          # [B, Hq, m]
+    pos = torch.searchsorted(sh, own.contiguous()).clamp(max=sh.shape[2] - 1)
+    hit = (torch.gather(sh, 2, pos) == own) & (own >= 0)
+    return hit.sum(-1).float() / (own >= 0).sum(-1).clamp(min=1).float()
+
+
 def decode_kv_shared(fsa, dc, reps=20):
-    """The per-KV-head Kascade variant on the decode group's inputs, outside
-    the timed steps: pooled top-k per KV head, then the four layers attending
-    at the shared indices (each K/V row read once for the G query heads)."""
+    """GQA-shared index sets on the decode group's inputs, outside the timed
+    steps (Kascade post, "Head-aware is the key to accuracy").  Two shared
+    forms against the per-query-head sets of the timed steps:
+      pooled: one top-k per KV head of the max over its query heads' scores
+              (k entries, G times fewer K/V reads);
+      union:  the union of the G per-head sets (every head keeps its own
+              top-k; each chosen key is read once per KV head).
+    Timings, and the accuracy of each on the anchor layer and the reuse
+    layers: recall of each head's own top-k inside the shared set, the
+    softmax mass kept (exp(lse_set - lse_dense), mean over heads and
+    sequences), and the output's largest difference from the per-head
+    result."""
     Dd = DECODE
     L = dc["layers"]
+    G = Dd["Hq"] // Dd["Hkv"]
     idx = torch.empty((Dd["B"], Dd["Hkv"], Dd["k"]), dtype=torch.int32, device="cuda")
     kth = torch.empty((Dd["B"], Dd["Hkv"]), dtype=torch.float32, device="cuda")
+    uni = torch.empty((Dd["B"], Dd["Hkv"], G * Dd["k"]), dtype=torch.int32, device="cuda")
+    ucnt = torch.empty((Dd["B"], Dd["Hkv"]), dtype=torch.int32, device="cuda")
+    own = dc["idx"]
     tm = Timer()
     for _ in range(2 + reps):
         tm.run("topk", lambda: fsa.topk_indices_kv(L[0]["q"], L[0]["k"], dc["page_table"],
@@ -151,14 +176,56 @@ def decode_kv_shared(fsa, dc, reps=20):
             tm.run("dec", lambda li=li: fsa.sparse_decode_attn(
                 L[li]["q"], L[li]["k"], L[li]["v"], dc["page_table"], dc["seq_lens"],
                 mode=fsa.SEL_INDEX_KV, idx=idx, out=dc["out"][li], want_lse=False))
+        tm.run("union", lambda: fsa.topk_union_kv(own, Dd["Hkv"], out=uni, cnt=ucnt))
+        tm.run("dec_union", lambda: fsa.sparse_decode_attn(
+            L[1]["q"], L[1]["k"], L[1]["v"], dc["page_table"], dc["seq_lens"],
+            mode=fsa.SEL_INDEX_KV, idx=uni, out=dc["out"][1], want_lse=False))
     torch.cuda.synchronize()
     topk_ms = tm.ms("topk", skip=2)[0]
     dec_ms = tm.ms("dec", skip=2 * Dd["layers"])[0]
+    union_ms = tm.ms("union", skip=2)[0]
+    dec_union_ms = tm.ms("dec_union", skip=2)[0]
     layer_bytes = Dd["B"] * Dd["Hkv"] * Dd["k"] * kv_row_bytes(Dd["D"])
+    union_bytes = int(ucnt.sum().item()) * kv_row_bytes(Dd["D"])
+    own_bytes = Dd["B"] * Dd["Hq"] * Dd["k"] * kv_row_bytes(Dd["D"])
+    # accuracy: the anchor layer itself (its per-head sets are its exact
+    # top-k), the reuse layers 1-3 of the workload (fresh queries), and the
+    # same reuse layers with queries correlated to the anchor's (0.9 q_0 +
+    # sqrt(0.19) z, the correlation the workload gives the keys)
+    recall = shared_set_recall(own, idx, G)
+
+    def accuracy(q, layer):
+        args = (q, L[layer]["k"], L[layer]["v"], dc["page_table"], dc["seq_lens"])
+        _, lse_d = fsa.sparse_decode_attn(*args, mode=fsa.SEL_ALL)
+        o_h, lse_h = fsa.sparse_decode_attn(*args, mode=fsa.SEL_INDEX, idx=own)
+        o_p, lse_p = fsa.sparse_decode_attn(*args, mode=fsa.SEL_INDEX_KV, idx=idx)
+        o_u, lse_u = fsa.sparse_decode_attn(*args, mode=fsa.SEL_INDEX_KV, idx=uni)
+        r = {"mass_kept_" + key: round(torch.exp(lse - lse_d).mean().item(), 4)
+             for key, lse in (("per_head", lse_h), ("pooled", lse_p), ("union", lse_u))}
+        r["out_maxdiff_pooled"] = round((o_p.float() - o_h.float()).abs().max().item(), 4)
+        r["out_maxdiff_union"] = round((o_u.float() - o_h.float()).abs().max().item(), 4)
+        return r
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    acc = {"anchor_layer": accuracy(L[0]["q"], 0)}
+    for li in range(1, Dd["layers"]):
+        acc[f"layer{li}"] = accuracy(L[li]["q"], li)
+        z = torch.randn(L[0]["q"].shape, generator=gen, device="cuda")
+        qc = (0.9 * L[0]["q"].float() + math.sqrt(0.19) * z).to(torch.bfloat16)
+        acc[f"layer{li}_correlated_queries"] = accuracy(qc, li)
     return {"topk_kv_ms": round(topk_ms, 4), "decode_kv_ms": round(dec_ms, 4),
             "decode_kv_GBps": round(layer_bytes / (dec_ms * 1e-3) / 1e9, 1),
             "group_ms": round(topk_ms + Dd["layers"] * dec_ms, 4),
-            "bytes_per_layer": layer_bytes}
+            "bytes_per_layer": layer_bytes,
+            "pooled_recall_of_own_topk": {"mean": round(recall.mean().item(), 4),
+                                          "min": round(recall.min().item(), 4)},
+            "union_ms": round(union_ms, 4), "union_decode_ms": round(dec_union_ms, 4),
+            "union_bytes_per_layer": union_bytes,
+            "union_decode_GBps": round(union_bytes / (dec_union_ms * 1e-3) / 1e9, 1),
+            "union_size_over_Gk": round(ucnt.float().mean().item() / (G * Dd["k"]), 4),
+            "per_head_bytes_per_layer": own_bytes,
+            "accuracy": acc}
 
 
 def prefill_sweep(fsa, workloads, pf):

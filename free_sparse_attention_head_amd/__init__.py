@@ -21,7 +21,7 @@ import torch
 from . import _lib as L
 
 __all__ = ["block_stats", "select_blocks", "sparse_prefill_attn", "topk_indices",
-           "topk_indices_kv", "sparse_decode_attn", "sparse_decode_attn_noalloc", "build_segments", "workspace_size", "FsaError",
+           "topk_indices_kv", "topk_union_kv", "sparse_decode_attn", "sparse_decode_attn_noalloc", "build_segments", "workspace_size", "FsaError",
            "SEL_ALL", "SEL_INDEX", "SEL_SEGMENT", "SEL_INDEX_KV", "SEG_GLOBAL", "SEG_FOCUS",
            "SEG_LOCAL", "SEG_STREAMING"]
 
@@ -276,6 +276,29 @@ def topk_indices_kv(q, k_pool, page_table, seq_lens, k, max_seq_len=None, idx=No
     sparse_decode_attn with mode=SEL_INDEX_KV."""
     return _topk("topk_indices_kv", k_pool.shape[1], q, k_pool, page_table, seq_lens, k,
                  max_seq_len, idx, kth, ws)
+
+
+def topk_union_kv(idx, Hkv, out=None, cnt=None):
+    """Union of each KV head's G query-head index sets (idx [B,Hq,k] int32,
+    as topk_indices returns it).  Returns out [B,Hkv,G*k] (distinct entries
+    ascending, then -1) and cnt [B,Hkv]; feed out to sparse_decode_attn with
+    mode=SEL_INDEX_KV."""
+    lib = L.load()
+    _need(idx, "idx", torch.int32, ndim=3)
+    B, Hq, k = idx.shape
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"{Hq} query heads do not divide into {Hkv} KV heads")
+    G = Hq // Hkv
+    if out is None:
+        out = torch.empty((B, Hkv, G * k), dtype=torch.int32, device=idx.device)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=idx.device)
+    _need(out, "out", torch.int32, (B, Hkv, G * k))
+    _need(cnt, "cnt", torch.int32, (B, Hkv))
+    _same_device(idx, out, cnt)
+    L.check("topk_union_kv", lib.topk_union_kv(_ptr(idx), B, Hq, Hkv, k, _ptr(out), _ptr(cnt),
+                                               _stream(idx.device)))
+    return out, cnt
 
 
 def _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments, n_seg, n_split,

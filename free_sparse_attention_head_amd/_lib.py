@@ -59,6 +59,8 @@ SIGNATURES = {
     "topk_indices_kv": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                 ctypes.POINTER(DecodeShape), c_int, c_void_p, c_void_p, c_void_p,
                                 c_size_t, c_void_p]),
+    "topk_union_kv": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                              c_void_p]),
     "sparse_decode_attn": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    ctypes.POINTER(DecodeShape), ctypes.POINTER(KvSelect),
                                    c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

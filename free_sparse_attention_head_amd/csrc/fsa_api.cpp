@@ -225,6 +225,18 @@ int topk_indices_kv(fsa_dtype dt, const void* q, const void* k_pool, const int32
   return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, true, idx, kth, ws, ws_bytes, st);
 }
 
+int topk_union_kv(const int32_t* idx, int B, int Hq, int Hkv, int k, int32_t* out,
+                  int32_t* cnt, hipStream_t st) {
+  if (!idx || !out) return FSA_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FSA_ERR_SHAPE;
+  if (k < 1) return FSA_ERR_ARG;
+  if ((long long)(Hq / Hkv) * k > fsa::kUnionMax) return FSA_ERR_ARG;
+  if ((long long)B * Hq * k > (1LL << 31) - 1) return FSA_ERR_SHAPE;
+  int rc = device_check();
+  if (rc) return rc;
+  return launch_status(fsa::launch_union_sets(idx, B, Hq, Hkv, k, out, cnt, st));
+}
+
 int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* page_table, const int32_t* seq_lens,
                        const fsa_decode_shape* s, const fsa_kv_select* sel, float scale,

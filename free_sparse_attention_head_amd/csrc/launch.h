@@ -50,6 +50,13 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
                        const DecodeDims& d, int k, bool pooled, int32_t* idx, float* kth, void* ws,
                        hipStream_t st);
 
+// union of a KV head's G per-query-head index sets: G * k entries, padded
+// to a power of two, at most kUnionMax
+constexpr int kUnionMax = 16384;
+constexpr int kUnionThreads = 1024;
+hipError_t launch_union_sets(const int32_t* idx, int B, int Hq, int Hkv, int k, int32_t* out,
+                             int32_t* cnt, hipStream_t st);
+
 // decode_attn.hip
 // bytes of the device array that the allocation-free decode entry point uses
 // for split partials (one per GPU)

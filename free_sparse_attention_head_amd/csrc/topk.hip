@@ -33,6 +33,7 @@
 //      final pass in index order keeps key > K*, plus the first keys equal to
 //      K*, compacting positions with workgroup scans so that the output is
 //      ascending.
+#include <limits.h>
 #include <math.h>
 
 #include "common.h"
@@ -542,6 +543,84 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     eq_before += teq;
   }
   if (kth != nullptr && t == 0) kth[row] = key_to_float(kstar);
+}
+
+// ---- union of a KV head's per-query-head index sets -----------------------
+//
+// Kascade post, "Head-aware is the key to accuracy": per-head sets keep each
+// head's own choice; sharing one set among a KV head's G query heads lets
+// them share every K/V read.  The union of the G sets is the shared set that
+// keeps every head's own top-k (each head then attends over a superset of
+// its own choice) and reads each chosen key once per KV head.
+//
+// One workgroup per (sequence, KV head): the G lists (any order; negative
+// slots are empty) go to LDS, padded to a power of two with INT_MAX, a
+// bitonic sort orders them, and a workgroup scan keeps the first of each run
+// of equal entries.  Output: the distinct entries ascending, then -1 to the
+// end of the row (G * k entries).
+__global__ __launch_bounds__(kUnionThreads) void union_sets_kernel(
+    const int32_t* __restrict__ idx, int Hq, int Hkv, int k, int n,
+    int32_t* __restrict__ out, int32_t* __restrict__ cnt) {
+  __shared__ int key[kUnionMax];
+  __shared__ int scan_tmp[17];
+  const int G = Hq / Hkv;
+  const int row = blockIdx.x;  // b * Hkv + g: its G heads' lists are contiguous in idx
+  const int t = threadIdx.x;
+  const int m = G * k;  // entries of the G lists
+  const int32_t* src = idx + (size_t)row * m;
+  for (int e = t; e < n; e += kUnionThreads) {
+    int v = INT_MAX;
+    if (e < m) {
+      const int w = src[e];
+      v = w >= 0 ? w : INT_MAX;
+    }
+    key[e] = v;
+  }
+  __syncthreads();
+  // bitonic sort, ascending: stage sizes 2..n, compare distances size/2..1
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int d = size >> 1; d >= 1; d >>= 1) {
+      for (int e = t; e < n / 2; e += kUnionThreads) {
+        const int a = 2 * d * (e / d) + (e % d), b = a + d;
+        const bool up = (a & size) == 0;  // direction of this bitonic run
+        const int x = key[a], y = key[b];
+        if ((x > y) == up) {
+          key[a] = y;
+          key[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // keep the first of each run of equal valid entries; thread t owns a
+  // contiguous range, so one scan places them in order
+  const int per = (n + kUnionThreads - 1) / kUnionThreads;
+  const int e0 = min(n, t * per), e1 = min(n, e0 + per);
+  int c = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int v = key[e];
+    c += (v != INT_MAX && (e == 0 || key[e - 1] != v)) ? 1 : 0;
+  }
+  int tot;
+  int pos = block_excl_scan(c, scan_tmp, &tot);
+  int32_t* dst = out + (size_t)row * m;
+  for (int e = e0; e < e1; ++e) {
+    const int v = key[e];
+    if (v != INT_MAX && (e == 0 || key[e - 1] != v)) dst[pos++] = v;
+  }
+  for (int e = tot + t; e < m; e += kUnionThreads) dst[e] = -1;
+  if (cnt != nullptr && t == 0) cnt[row] = tot;
+}
+
+hipError_t launch_union_sets(const int32_t* idx, int B, int Hq, int Hkv, int k, int32_t* out,
+                             int32_t* cnt, hipStream_t st) {
+  const int m = (Hq / Hkv) * k;
+  int n = 1;
+  while (n < m) n <<= 1;
+  if (n > kUnionMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(union_sets_kernel, dim3(B * Hkv), dim3(kUnionThreads), 0, st, idx, Hq, Hkv, k,
+                     n, out, cnt);
+  return hipGetLastError();
 }
 
 // Workspace: candidate keys and tile indices (one TT-entry list per tile of

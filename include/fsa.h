@@ -193,6 +193,22 @@ int topk_indices_kv(fsa_dtype dt, const void* q, const void* k_pool, const int32
                     const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
                     float* kth, void* ws, size_t ws_bytes, hipStream_t st);
 
+/* topk_union_kv -- one shared index set per KV head: the union of its G
+ * query heads' sets.  Kascade post, "Head-aware is the key to accuracy":
+ * per-head sets keep each head's own choice, and sharing one set lets a KV
+ * head's query heads share every K/V read.  The union keeps every head's own
+ * top-k (each head attends over a superset of it, FSA_SEL_INDEX_KV with
+ * k' = G * k) and reads each chosen key once per KV head.
+ *   idx (device) int32 [B, Hq, k]: per-query-head sets as topk_indices
+ *       writes them (any order is accepted; negative entries are empty)
+ *   out (device) int32 [B, Hkv, G * k]: the distinct entries ascending, then
+ *       -1 to the end of each row
+ *   cnt (device, nullable) int32 [B, Hkv]: distinct entries per row
+ * G = Hq / Hkv; G * k rounded up to a power of two must not exceed 16384
+ * (else FSA_ERR_ARG). */
+int topk_union_kv(const int32_t* idx, int B, int Hq, int Hkv, int k, int32_t* out,
+                  int32_t* cnt, hipStream_t st);
+
 /* sparse_decode_attn -- split-KV decode attention over a paged cache.
  * Kascade post, "What Kascade got right" (reuse layers attend only at the
  * anchor's indices); Declarative Attention post, "Declarative attention

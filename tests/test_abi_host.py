@@ -308,3 +308,14 @@ def test_binding_rejects_mismatched_tensors():
             "idx")
     rejects(lambda: fsa.sparse_decode_attn_noalloc(qd, pool, pool, pt, sl, mode=fsa.SEL_INDEX, idx=idx),
             "idx")
+
+
+def test_topk_union_kv_validation():
+    L, lib = _lib()
+    call = lambda B, Hq, Hkv, k, idx=FAKE, out=FAKE: lib.topk_union_kv(idx, B, Hq, Hkv, k, out, None, None)
+    assert call(2, 8, 2, 16, idx=None) == L.FSA_ERR_NULL
+    assert call(2, 8, 2, 16, out=None) == L.FSA_ERR_NULL
+    assert call(2, 8, 3, 16) == L.FSA_ERR_SHAPE
+    assert call(0, 8, 2, 16) == L.FSA_ERR_SHAPE
+    assert call(2, 8, 2, 0) == L.FSA_ERR_ARG
+    assert call(2, 16, 1, 1025) == L.FSA_ERR_ARG     # 16 x 1025 entries: beyond the sort

@@ -439,3 +439,115 @@ def test_segment_decode_mixed_batch(name):
             o, l = oracle.segment_attention(q1[b, h], K, V, ranges[b], scale)
             assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16, (b, h)
             assert abs(lse[b, h].item() - l) <= 1e-2
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_topk_union_kv_parity(name):
+    """The union of each KV head's per-query-head top-k sets equals the
+    oracle's union of the same sets exactly (ragged sequences leave -1 slots,
+    which are dropped), and decode over the union matches the oracle's
+    attention of every query head at that set."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L0, L1 = gpu["layers"]
+    idx, _ = fsa.topk_indices(L0["q"], L0["k"], gpu["page_table"], gpu["seq_lens"], k, max_seq_len=N)
+    uni, cnt = fsa.topk_union_kv(idx, Hkv)
+    out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], gpu["page_table"], gpu["seq_lens"],
+                                      mode=fsa.SEL_INDEX_KV, idx=uni, max_seq_len=N)
+    idx, uni, cnt, out, lse = (t.cpu() for t in (idx, uni, cnt, out, lse))
+    G = Hq // Hkv
+    assert uni.shape == (B, Hkv, G * k)
+    q1 = workloads.to_f64(d["layers"][1]["q"])
+    scale = 1 / math.sqrt(D)
+    sizes = []
+    for b in range(B):
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if oracle.kv_head(h, Hq, Hkv) == g]
+            ref = oracle.union_sets([idx[b, h].numpy() for h in heads])
+            c = int(cnt[b, g])
+            assert c == ref.size
+            assert (uni[b, g, :c].numpy() == ref).all() and (uni[b, g, c:] == -1).all()
+            sizes.append(c / (G * k))
+            K, V = seq_kv(d, 1, b, g)
+            for h in (heads[0], heads[-1]):
+                o, l = oracle.index_attention(q1[b, h], K, V, ref, scale)
+                assert np.abs(out[b, h].double().numpy() - o).max() <= TOL_BF16
+                assert abs(lse[b, h].item() - l) <= 1e-2
+    print(f"[{name}] union size / (G k) mean {np.mean(sizes):.3f}")
+
+
+def test_topk_union_kv_unsorted_duplicates_and_empty_slots():
+    """Any order, repeated entries within and across heads, and negative
+    slots anywhere: the union is the sorted distinct non-negative entries."""
+    import free_sparse_attention_head_amd as fsa
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, k = 3, 8, 2, 700       # G k = 2800: padded to 4096 in the sort
+    idx = rng.integers(-3, 5000, size=(B, Hq, k)).astype(np.int32)
+    idx[0, 1, :] = idx[0, 0, ::-1]      # one head repeats another's set reversed
+    idx[1, 4:8, :] = -1                 # a KV head with every slot empty
+    idx[2, :, :350] = 77                # heavy duplication
+    uni, cnt = fsa.topk_union_kv(torch.from_numpy(idx).cuda(), Hkv)
+    uni, cnt = uni.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            ref = oracle.union_sets([idx[b, h] for h in range(Hq) if oracle.kv_head(h, Hq, Hkv) == g])
+            assert cnt[b, g] == ref.size
+            assert (uni[b, g, :ref.size] == ref).all() and (uni[b, g, ref.size:] == -1).all()
+    assert cnt[1, 1] == 0
+
+
+def test_topk_union_kv_largest_sort():
+    """G k = 16384 exactly (8 heads x 2048): the largest sort the kernel runs."""
+    import free_sparse_attention_head_amd as fsa
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, k = 2, 8, 1, 2048
+    idx = np.sort(rng.integers(0, 40000, size=(B, Hq, k)), axis=2).astype(np.int32)
+    uni, cnt = fsa.topk_union_kv(torch.from_numpy(idx).cuda(), Hkv)
+    uni, cnt = uni.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        ref = oracle.union_sets(list(idx[b]))
+        assert cnt[b, 0] == ref.size and (uni[b, 0, :ref.size] == ref).all()
+        assert (uni[b, 0, ref.size:] == -1).all()
+
+
+def test_shared_set_accuracy_harness_matches_oracle():
+    """The measurements behind the bench's per-head vs shared-set comparison:
+    recall of each head's own top-k inside the pooled set (bench's
+    shared_set_recall) against oracle.set_recall, and the softmax mass a set
+    keeps, exp(lse_set - lse_dense) from two decode launches, against
+    oracle.index_mass for per-head, pooled and union sets."""
+    import bench
+    import free_sparse_attention_head_amd as fsa
+    name = "gqa4_d128"
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L0, L1 = gpu["layers"]
+    pt, sls = gpu["page_table"], gpu["seq_lens"]
+    own, _ = fsa.topk_indices(L0["q"], L0["k"], pt, sls, k, max_seq_len=N)
+    pooled, _ = fsa.topk_indices_kv(L0["q"], L0["k"], pt, sls, k, max_seq_len=N)
+    uni, _ = fsa.topk_union_kv(own, Hkv)
+    G = Hq // Hkv
+    rec = bench.shared_set_recall(own, pooled, G).cpu().numpy()
+    args = (L1["q"], L1["k"], L1["v"], pt, sls)
+    _, lse_d = fsa.sparse_decode_attn(*args, mode=fsa.SEL_ALL, max_seq_len=N)
+    kept = {}
+    for key, mode, ix in (("own", fsa.SEL_INDEX, own), ("pooled", fsa.SEL_INDEX_KV, pooled),
+                          ("union", fsa.SEL_INDEX_KV, uni)):
+        _, lse = fsa.sparse_decode_attn(*args, mode=mode, idx=ix, max_seq_len=N)
+        kept[key] = torch.exp(lse - lse_d).cpu().numpy()
+    own, pooled, uni = own.cpu().numpy(), pooled.cpu().numpy(), uni.cpu().numpy()
+    q1 = workloads.to_f64(d["layers"][1]["q"])
+    scale = 1 / math.sqrt(D)
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            g = oracle.kv_head(h, Hq, Hkv)
+            if (own[b, h] >= 0).any():
+                assert abs(rec[b, h] - oracle.set_recall(own[b, h], pooled[b, g])) <= 1e-6
+            K, _ = seq_kv(d, 1, b, g)
+            for key, ix in (("own", own[b, h]), ("pooled", pooled[b, g]), ("union", uni[b, g])):
+                ref = oracle.index_mass(q1[b, h], K, ix, scale)
+                worst = max(worst, abs(kept[key][b, h] - ref))
+    print(f"[shared-set harness] mass kept max-abs difference GPU vs oracle {worst:.2e}")
+    assert worst <= 2e-2
