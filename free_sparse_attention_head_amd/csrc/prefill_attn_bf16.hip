@@ -205,8 +205,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     const size_t base = ((size_t)j * BLK + (c % NCH) * KC) * kv_stride * sizeof(uint16_t);
     const char* src = reinterpret_cast<const char*>(src0) + base;
 #pragma unroll
-    for (int m = 0; m < Tr::IPW; ++m)
-      copy16_to_lds(src + ofs[m], tile + (wave * Tr::IPW + m) * 1024);
+    for (int m = 0; m < Tr::IPW; ++m) {
+      uint32_t o = ofs[m];
+      asm volatile("" : "+v"(o));
+      copy16_to_lds(src + o, tile + (wave * Tr::IPW + m) * 1024);
+    }
   };
   auto issue_k = [&](int c, int j, unsigned char* kt) { issue_tile(c, j, Kb, kofs, kt); };
   auto issue_v = [&](int c, int j, unsigned char* vt) { issue_tile(c, j, Vb, vofs, vt); };

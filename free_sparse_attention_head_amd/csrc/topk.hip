@@ -11,18 +11,19 @@
 //   2. topk_score_kernel: streams K once from HBM through the page table; the
 //      G query heads of a KV head share every 256-byte key row (16 lanes x
 //      16 bytes, v_dot2_f32_bf16 + DPP butterfly).  A workgroup scores one
-//      tile of a row and keeps the tile's fp32 scores, and a histogram of the
-//      top 11 bits of their order-preserving keys, in LDS.  At the end it
-//      reads the row's histogram as it stands and takes as bound the bin of
-//      the k-th largest key counted there (0 while fewer than k are counted).
-//      Counts only grow, so any reading counts a subset of the row: its k-th
-//      largest key is never above the row's, and the bound never exceeds the
-//      bin b1 of the row's k-th largest key.  The tile then keeps only its
-//      candidates, keys in bins >= bound, written (order key, index) in index
-//      order as one list per tile, and adds its counts of bins >= bound to
-//      the row's histogram, which is therefore exact from b1 up, the only
-//      part the select reads.  Tiles run in order along the row, so later
-//      tiles see tighter bounds and write few candidates.
+//      tile of a row.  Before its first scores it reads the row's histogram
+//      of the top 11 bits of the order-preserving keys as it stands (64
+//      coarse buckets of 32 bins first, then the 32 bins of one bucket) and
+//      takes as bound the bin of the k-th largest key counted there (0 while
+//      fewer than k are counted).  Counts only grow, and a bin never counts
+//      more keys than the row holds in it, so any reading counts a subset of
+//      the row: the bound never exceeds the bin b1 of the row's k-th largest
+//      key.  The tile keeps its fp32 scores in LDS and histograms only keys
+//      in bins >= bound; at its end it writes those keys, its candidates, as
+//      (order key, index) in index order as one list per tile, and adds their
+//      counts to the row's histogram (both levels), which is therefore exact
+//      from b1 up, the only part the select reads.  Tiles run in order along
+//      the row, so later tiles see tighter bounds and keep few candidates.
 //   3. topk_select_kernel: one 1024-thread workgroup per score row, reading
 //      the row's candidate lists as one stream in index order.  Digit 1 comes
 //      from the row histogram.  When few keys lie in or above the k-th key's
@@ -42,6 +43,7 @@
 namespace fsa {
 
 constexpr int kBins1 = 2048;      // digit 1: key bits 31..21
+constexpr int kCoarse = 64;       // coarse buckets of digit 1 (32 bins each)
 constexpr int kSelThreads = 1024;
 constexpr int kTileScores = 8192;  // scores of a score workgroup's tile, staged in LDS (32 KB)
 constexpr int kMaxSelTiles = kTopkMaxSeqLen / (kTileScores / 8);  // tiles of a row, at most
@@ -78,10 +80,9 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   static_assert(TT % STEP == 0, "tile of whole steps");
   // page ids of the tile plus the two steps that the last loads run past it
   constexpr int TPAGES = (TT + 2 * STEP) / 16;
-  // digit-1 counts of bins 2w and 2w+1 share word w (a tile holds < 65536
-  // keys); the last word takes the adds of lanes with nothing to count
-  constexpr int HW = GR * kBins1 / 2, TRASH = HW;
-  __shared__ uint32_t lh[HW + 1];
+  // digit-1 counts of bins 2w and 2w+1 share word w (a tile holds < 65536 keys)
+  constexpr int HW = GR * kBins1 / 2;
+  __shared__ uint32_t lh[HW];
   __shared__ __align__(16) float ssc[GR * TT + 4];  // + a spare quad for idle lanes
   __shared__ int pg[TPAGES];
   __shared__ int scan_tmp[17];
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   const int t1 = min(n, t0 + TT);
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int slot = wave * RG + l / LPR, dl = l % LPR;
-  for (int x = tid; x <= TRASH; x += 256) lh[x] = 0u;
+  for (int x = tid; x < HW; x += 256) lh[x] = 0u;
   // the tile's page ids, read once and coalesced: row loads then depend on an
   // LDS read instead of a second global load (bad ids become -1: skipped)
   const int32_t* ptb = pt + (size_t)b * max_pages;
@@ -110,6 +111,41 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
 #pragma unroll
   for (int x = 0; x < G; ++x)
     qv[x] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + g * G + x) * D + dl * 8);
+  const size_t row0 = POOL ? (size_t)b * Hkv + g : (size_t)b * Hq + (size_t)g * G;
+  const int rows_total = B * (POOL ? Hkv : Hq);
+  uint32_t* coarse = hist + (size_t)rows_total * kBins1;  // [rows, kCoarse] after the bins
+  constexpr int BPC = kBins1 / kCoarse;                   // bins per coarse bucket
+  static_assert(kCoarse == 64 && BPC <= 64, "one coarse bucket per lane");
+  __shared__ uint32_t sbound[GR];
+  // Candidate bounds, read before the tile is scored: per row, the bin of the
+  // k-th largest key counted in the row's histogram as it stands (0 while
+  // fewer than k keys are counted).  Wave w takes rows w, w + 4, ...: lane l
+  // reads coarse bucket 63 - l (descending), a wave scan finds the bucket of
+  // the k-th key, then lanes 0..BPC-1 read that bucket's bins, descending.
+  for (int x = wave; x < GR; x += 4) {
+    const uint32_t cb = __hip_atomic_load(coarse + (row0 + x) * kCoarse + (kCoarse - 1 - l),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int inc = wave_incl_scan((int)cb);
+    const uint64_t hit = __ballot(inc >= k);
+    uint32_t bound = 0u;
+    if (hit != 0ull) {
+      const int lb = __ffsll((unsigned long long)hit) - 1;  // first lane reaching k
+      const int above = __shfl(inc - (int)cb, lb, 64);      // keys in higher buckets
+      const int bucket = kCoarse - 1 - lb;
+      uint32_t fc = 0u;
+      if (l < BPC)
+        fc = __hip_atomic_load(hist + (row0 + x) * kBins1 + bucket * BPC + (BPC - 1 - l),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int finc = above + wave_incl_scan((int)fc);
+      const uint64_t fhit = __ballot(l < BPC && finc >= k);
+      // The two levels are read at different times, so the bins may not add
+      // up to the bucket's count; a bin reaching k, or else the bucket's
+      // lowest bin, is then still at or below b1.
+      const int lf = fhit != 0ull ? __ffsll((unsigned long long)fhit) - 1 : BPC - 1;
+      bound = (uint32_t)(bucket * BPC + (BPC - 1 - lf));
+    }
+    if (l == 0) sbound[x] = bound;
+  }
   __syncthreads();
 
   // A lane group's RB rows are consecutive tokens inside one 16-token page.
@@ -164,11 +200,13 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
       }
       const bool ok = (c < GR * NQ) & (tq < t1);
       *reinterpret_cast<floatx4*>(&ssc[ok ? sx * TT + (tq - t0) : GR * TT]) = v;
+      const uint32_t bnd = sbound[sx < GR ? sx : 0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t bin = (uint32_t)sx * kBins1 + (order_key(v[e]) >> 21);
-        const bool oke = ok & (tq + e < t1);
-        atomicAdd(&lh[oke ? bin >> 1 : TRASH], (bin & 1) ? 0x10000u : 1u);
+        const uint32_t kb = order_key(v[e]) >> 21;
+        const uint32_t bin = (uint32_t)sx * kBins1 + kb;
+        // keys below the bound are never candidates: they are not counted
+        if (ok & (tq + e < t1) & (kb >= bnd)) atomicAdd(&lh[bin >> 1], (bin & 1) ? 0x10000u : 1u);
       }
     }
   };
@@ -191,85 +229,92 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   }
   if (base < t1) score_rows(base, ka);
   __syncthreads();
-  const size_t row0 = POOL ? (size_t)b * Hkv + g : (size_t)b * Hq + (size_t)g * G;
-  constexpr int BPT = kBins1 / 256;  // histogram bins per thread
-  constexpr int PER = TT / 256;      // tile tokens per thread
-  // the compaction below reads each thread's tokens as 16-byte quads
-  static_assert(PER >= 4 && PER % 4 == 0, "tile of whole 16-byte quads per thread");
-  __shared__ uint32_t sbound[GR];
   const int nt = t1 - t0;
-  // Candidate bounds: per row, the bin of the k-th largest key counted in
-  // the row's histogram as it stands (0 while fewer than k keys are
-  // counted).  Thread t reads bins [top, top + BPT), the threads in
-  // descending bin order; all rows' reads are issued together.
-  const int top = kBins1 - BPT * (tid + 1);
-  uint32_t hc[GR][BPT];
+  // The tile's counts into the rows' histograms: the LDS counts hold only
+  // keys at or above each row's bound, and the select reads exact counts only
+  // from the k-th key's bin up, which is at or above every tile's bound.
+  // Thread u takes one coarse bucket of one row: its bins, then its total.
+  for (int u = tid; u < GR * kCoarse; u += 256) {
+    const int x = u / kCoarse, cbk = u % kCoarse;
+    uint32_t tot = 0u;
 #pragma unroll
-  for (int x = 0; x < GR; ++x)
+    for (int w = 0; w < BPC / 2; ++w) {
+      const int bin = cbk * BPC + 2 * w;
+      const uint32_t cc = lh[x * (kBins1 / 2) + bin / 2];
+      uint32_t* hr = hist + (row0 + x) * kBins1 + bin;
+      if (cc & 0xffffu) atomicAdd(hr, cc & 0xffffu);
+      if (cc >> 16) atomicAdd(hr + 1, cc >> 16);
+      tot += (cc & 0xffffu) + (cc >> 16);
+    }
+    if (tot) atomicAdd(coarse + (row0 + x) * kCoarse + cbk, tot);
+  }
+  // Each row's candidates of this tile, compacted in index order.
+  if constexpr (GR >= 4) {
+    // a wave per row, no workgroup barrier: lane l reads quads l, l + 64, ...
+    // (consecutive 16-byte LDS reads), one wave scan per 64 quads
+#pragma unroll 1
+    for (int x = wave; x < GR; x += 4) {
+      const uint32_t bound = sbound[x];
+      const size_t cbase = (row0 + x) * (size_t)cstride + t0;
+      int done = 0;
 #pragma unroll
-    for (int e = 0; e < BPT; ++e)
-      hc[x][e] = __hip_atomic_load(hist + (row0 + x) * kBins1 + top + e, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-  if (tid < GR) sbound[tid] = 0u;
+      for (int it = 0; it < TT / 256; ++it) {
+        const int j = 4 * (it * 64 + l);
+        const floatx4 v = *reinterpret_cast<const floatx4*>(&ssc[x * TT + j]);
+        uint32_t key[4];
+        int nc = 0;
 #pragma unroll
-  for (int x = 0; x < GR; ++x) {
-    int c = 0;
+        for (int u = 0; u < 4; ++u) {
+          key[u] = order_key(v[u]);
+          nc += (j + u < nt && (key[u] >> 21) >= bound) ? 1 : 0;
+        }
+        const int inc = wave_incl_scan(nc);
+        int pos = done + inc - nc;
 #pragma unroll
-    for (int e = 0; e < BPT; ++e) c += (int)hc[x][e];
-    int tot;
-    const int above = block_excl_scan(c, scan_tmp, &tot);  // keys in higher bins
-    if (above < k && k <= above + c) {
-      int acc = above;
+        for (int u = 0; u < 4; ++u) {
+          if (j + u < nt && (key[u] >> 21) >= bound) {
+            ckey[cbase + pos] = key[u];
+            cidx[cbase + pos] = (uint16_t)(j + u);
+            ++pos;
+          }
+        }
+        done += __shfl(inc, 63, 64);
+      }
+      if (l == 0) ccnt[(row0 + x) * tiles + tile] = (uint32_t)done;
+    }
+  } else {
+    // fewer rows than waves: thread t takes tokens [t*PER, t*PER + PER), a
+    // workgroup scan places them
+    constexpr int PER = TT / 256;
+    static_assert(PER >= 4 && PER % 4 == 0, "tile of whole 16-byte quads per thread");
+    const int j0 = tid * PER;
+#pragma unroll 1
+    for (int x = 0; x < GR; ++x) {
+      const uint32_t bound = sbound[x];
+      uint32_t key[PER];
+      int nc = 0;
 #pragma unroll
-      for (int e = BPT - 1; e >= 0; --e) {
-        acc += (int)hc[x][e];
-        if (acc >= k) {
-          sbound[x] = (uint32_t)(top + e);
-          break;
+      for (int e = 0; e < PER; e += 4) {
+        const floatx4 v = *reinterpret_cast<const floatx4*>(&ssc[x * TT + j0 + e]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          key[e + u] = order_key(v[u]);
+          nc += (j0 + e + u < nt && (key[e + u] >> 21) >= bound) ? 1 : 0;
         }
       }
-    }
-  }
-  __syncthreads();
-  // The tile's counts into the rows' histograms, from each row's bound up:
-  // the select reads exact counts only from the k-th key's bin up, and that
-  // bin is at or above every tile's bound.
-  for (int y = tid; y < HW; y += 256) {
-    const int x = y / (kBins1 / 2), bin = 2 * (y % (kBins1 / 2));
-    const uint32_t cc = lh[y], bound = sbound[x];
-    uint32_t* hr = hist + (row0 + x) * kBins1 + bin;
-    if ((cc & 0xffffu) && (uint32_t)bin >= bound) atomicAdd(hr, cc & 0xffffu);
-    if ((cc >> 16) && (uint32_t)(bin + 1) >= bound) atomicAdd(hr + 1, cc >> 16);
-  }
-  // Each row's candidates of this tile, compacted in index order: thread t
-  // takes tokens [t*PER, t*PER + PER), a workgroup scan places them.
-  const int j0 = tid * PER;
-#pragma unroll 1
-  for (int x = 0; x < GR; ++x) {
-    const uint32_t bound = sbound[x];
-    uint32_t key[PER];
-    int nc = 0;
+      int ntot;
+      int pos = block_excl_scan(nc, scan_tmp, &ntot);
+      const size_t cbase = (row0 + x) * (size_t)cstride + t0;
 #pragma unroll
-    for (int e = 0; e < PER; e += 4) {
-      const floatx4 v = *reinterpret_cast<const floatx4*>(&ssc[x * TT + j0 + e]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        key[e + u] = order_key(v[u]);
-        nc += (j0 + e + u < nt && (key[e + u] >> 21) >= bound) ? 1 : 0;
+      for (int e = 0; e < PER; ++e) {
+        if (j0 + e < nt && (key[e] >> 21) >= bound) {
+          ckey[cbase + pos] = key[e];
+          cidx[cbase + pos] = (uint16_t)(j0 + e);
+          ++pos;
+        }
       }
+      if (tid == 0) ccnt[(row0 + x) * tiles + tile] = (uint32_t)ntot;
     }
-    int ntot;
-    int pos = block_excl_scan(nc, scan_tmp, &ntot);
-    const size_t cbase = (row0 + x) * (size_t)cstride + t0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      if (j0 + e < nt && (key[e] >> 21) >= bound) {
-        ckey[cbase + pos] = key[e];
-        cidx[cbase + pos] = (uint16_t)(j0 + e);
-        ++pos;
-      }
-    }
-    if (tid == 0) ccnt[(row0 + x) * tiles + tile] = (uint32_t)ntot;
   }
 }
 
@@ -640,7 +685,7 @@ static TopkLayout topk_layout(const DecodeDims& d, bool pooled) {
   L.idx_off = up((size_t)L.rows * L.cstride * sizeof(uint32_t));
   L.cnt_off = L.idx_off + up((size_t)L.rows * L.cstride * sizeof(uint16_t));
   L.hist_off = L.cnt_off + up((size_t)L.rows * L.tiles * sizeof(uint32_t));
-  L.bytes = L.hist_off + (size_t)L.rows * kBins1 * sizeof(uint32_t);
+  L.bytes = L.hist_off + (size_t)L.rows * (kBins1 + kCoarse) * sizeof(uint32_t);
   return L;
 }
 
@@ -660,7 +705,7 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
   uint16_t* cidx = reinterpret_cast<uint16_t*>(w + L.idx_off);
   uint32_t* ccnt = reinterpret_cast<uint32_t*>(w + L.cnt_off);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + L.hist_off);
-  const size_t nh = (size_t)L.rows * kBins1;
+  const size_t nh = (size_t)L.rows * (kBins1 + kCoarse);  // bins, then coarse buckets
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + 255) / 256 < 4096 ? (nh + 255) / 256 : 4096)),
                      dim3(256), 0, st, hist, nh, 0u);
   hipError_t e = hipGetLastError();
