@@ -518,10 +518,40 @@ def prefill_flops(pf):
     return 4.0 * P["T"] * P["T"] * P["D"] * executed, executed
 
 
-def cpu_baseline(pf, budget_s=15.0):
-    """fp64 oracle timed on a bounded sample of the prefill workload: whole
-    query blocks of head 0 at the benchmark's mask, from the last block
-    backwards, until about budget_s seconds of compute."""
+def _threads():
+    """(BLAS threads numpy's matmuls use, cores this process may run on)."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([x.get("num_threads", 1) for x in threadpool_info()
+                    if x.get("user_api") == "blas"] + [1])
+    except Exception:
+        blas = 1
+    return blas, len(os.sched_getaffinity(0))
+
+
+def _host_seq(pool, page_table_row, n, g):
+    """One sequence's pages of KV head g, copied to the host whole and widened
+    to float64 (untimed), with its page-table entries remapped to that copy."""
+    import workloads
+    ids = page_table_row[: (n + 15) // 16].long()
+    uniq, inv = torch.unique(ids, sorted=True, return_inverse=True)
+    return workloads.to_f64(pool[uniq, g:g + 1]), inv.cpu().numpy()
+
+
+def cpu_baseline(pf, dc, sg, budget_s=12.0):
+    """The fp64 oracle timed on bounded samples of the same workloads, on the
+    host's cores (compute only: device-to-host copies and fp64 widening are
+    outside the timed regions).
+      prefill: whole query blocks of head 0 at the benchmark's mask, from the
+               last block backwards, for about budget_s seconds (TFLOP/s on
+               executed blocks);
+      top-k:   anchor scores and exact top-k of a few query heads over the
+               128K decode context (GB/s of keys scanned, bf16 size);
+      index decode: attention of a few query heads at their 2048 indices,
+               through the paged gather (GB/s of admitted K+V, bf16 size);
+      global segment decode: a few query heads over a 1M-token sequence
+               (GB/s of admitted K+V, bf16 size).
+    numpy matmuls use the BLAS threads; sorts and top-k run on one thread."""
     import oracle
     import workloads
     P = PREFILL
@@ -548,15 +578,59 @@ def cpu_baseline(pf, budget_s=15.0):
         if t_cpu >= budget_s:
             break
     flops = 4.0 * T * T * P["D"] * done_blocks
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    cores = min(threads, len(os.sched_getaffinity(0)))
-    return {"value": flops / t_cpu / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    blas, affinity = _threads()
+    legs = {}
+    # decode legs (128K Kascade group, 1M global segment)
+    Dd, Sg = DECODE, SEGMENT
+    row = 2 * Dd["D"] * 2                       # one K + one V row, bf16 bytes
+    L = dc["layers"]
+    sc = 1 / math.sqrt(Dd["D"])
+    t_topk = t_idx = 0.0
+    heads = [(0, 0), (5, 17), (31, 31)]
+    idx = dc["idx"].cpu().numpy()
+    for b, hh in heads:
+        gg = oracle.kv_head(hh, Dd["Hq"], Dd["Hkv"])
+        qh = workloads.to_f64(L[0]["q"][b, hh])
+        subk, pt = _host_seq(L[0]["k"], dc["page_table"][b], Dd["N"], gg)
+        subv, _ = _host_seq(L[0]["v"], dc["page_table"][b], Dd["N"], gg)
+        t0 = time.perf_counter()
+        K = oracle.gather_pages(subk, pt, Dd["N"], 0)
+        oracle.anchor_topk(qh, K, Dd["k"])
+        t_topk += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        V = oracle.gather_pages(subv, pt, Dd["N"], 0)
+        oracle.index_attention(qh, K, V, idx[b, hh], sc)
+        t_idx += time.perf_counter() - t0
+        del K, V, subk, subv
+    n_h = len(heads)
+    legs["topk"] = {"value": round(n_h * Dd["N"] * Dd["D"] * 2 / t_topk / 1e9, 3), "unit": "GB/s",
+                    "sample": f"{n_h} query heads x {Dd['N']} keys, k={Dd['k']} ({t_topk:.1f} s)"}
+    legs["index_decode"] = {"value": round(n_h * Dd["k"] * row / t_idx / 1e9, 4), "unit": "GB/s",
+                            "sample": f"{n_h} query heads x {Dd['k']} indices with their sequence's "
+                                      f"paged gather ({t_idx:.1f} s)"}
+    G = sg["layers"][0]
+    t_seg = 0.0
+    seg_heads = [(0, 0), (3, 29)]
+    for b, hh in seg_heads:
+        gg = oracle.kv_head(hh, Sg["Hq"], Sg["Hkv"])
+        qh = workloads.to_f64(G["q"][b, hh])
+        subk, pt = _host_seq(G["k"], sg["page_table"][b], Sg["N"], gg)
+        subv, _ = _host_seq(G["v"], sg["page_table"][b], Sg["N"], gg)
+        t0 = time.perf_counter()
+        K = oracle.gather_pages(subk, pt, Sg["N"], 0)
+        V = oracle.gather_pages(subv, pt, Sg["N"], 0)
+        oracle.segment_attention(qh, K, V, [(0, Sg["N"])], sc)
+        t_seg += time.perf_counter() - t0
+        del K, V, subk, subv
+    legs["global_segment_decode"] = {
+        "value": round(len(seg_heads) * Sg["N"] * row / t_seg / 1e9, 4), "unit": "GB/s",
+        "sample": f"{len(seg_heads)} query heads over {Sg['N']} tokens ({t_seg:.1f} s)"}
+    return {"value": flops / t_cpu / 1e12, "unit": "TFLOP/s", "cores": min(blas, affinity),
+            "blas_threads": blas, "affinity_cores": affinity, "kind": "oracle",
             "sample": f"fp64 masked attention, head 0, last {rows} of {nB} query blocks "
-                      f"({done_blocks} executed blocks, {t_cpu:.1f} s)"}
+                      f"({done_blocks} executed blocks, {t_cpu:.1f} s); numpy matmuls on the "
+                      f"BLAS threads, sorts and top-k on one thread",
+            "legs": legs}
 
 
 def profiled_traffic(key, source):
@@ -756,7 +830,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu oracle baseline")
-        cpu = cpu_baseline(pf)
+        cpu = cpu_baseline(pf, dc, sg)
 
     res = {
         "metric": "sparse prefill TFLOP/s & decode KV GB/s at 128K ctx, % roofline, 1 MI355X",

@@ -17,6 +17,8 @@ FSA_SEL_ALL, FSA_SEL_INDEX, FSA_SEL_SEGMENT, FSA_SEL_INDEX_KV = 0, 1, 2, 3
 FSA_OP_SELECT_BLOCKS, FSA_OP_PREFILL_ATTN, FSA_OP_TOPK, FSA_OP_DECODE_ATTN = 1, 2, 3, 4
 FSA_SEG_GLOBAL, FSA_SEG_FOCUS, FSA_SEG_LOCAL, FSA_SEG_STREAMING = 0, 1, 2, 3
 FSA_NOALLOC_SCRATCH_BYTES = 16 << 20
+FSA_DBG_BLOCK_INDEX, FSA_DBG_TOKEN_INDEX, FSA_DBG_PAGE_ID, FSA_DBG_SEGMENT = 1, 2, 4, 8
+FSA_DBG_UNAVAILABLE = 0x80000000
 
 c_int, c_float, c_double, c_size_t, c_void_p = (ctypes.c_int, ctypes.c_float, ctypes.c_double,
                                                  ctypes.c_size_t, ctypes.c_void_p)
@@ -74,6 +76,7 @@ SIGNATURES = {
     "fsa_build_segments_nb": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_int32_p, ctypes.POINTER(c_int)]),
     "fsa_status_string": (ctypes.c_char_p, [c_int]),
+    "fsa_debug_flags": (c_int, [ctypes.POINTER(ctypes.c_uint32), c_int]),
     "fsa_device_check": (c_int, []),
 }
 

@@ -1,10 +1,14 @@
 """Build libfsa.so (the C-ABI HIP library) in-tree for gfx950.
 
-    python -m free_sparse_attention_head_amd.build      # or build() from Python
+    python -m free_sparse_attention_head_amd.build                 # libfsa.so
+    python -m free_sparse_attention_head_amd.build --debug-bounds  # libfsa_debug.so
+    python -m free_sparse_attention_head_amd.build --all           # both
 
 Every HIP translation unit is compiled with hipcc for --offload-arch=gfx950 in
 parallel, then linked into free_sparse_attention_head_amd/libfsa.so.  Packed
-fp32 VALU instructions are disabled for device code.
+fp32 VALU instructions are disabled for device code.  The debug-bounds build
+(-DFSA_DEBUG_BOUNDS) records the bad inputs the kernels skip, readable with
+fsa_debug_flags (include/fsa.h); it is otherwise the same library.
 """
 
 import concurrent.futures as cf
@@ -20,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfsa.so")
+DEBUG_LIB = os.path.join(PKG, "libfsa_debug.so")
 ARCH = "gfx950"
 
 
@@ -35,11 +40,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + COMMON + ["-c", src, "-o", obj]
+def _compile(src, build_dir, extra):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [_hipcc()] + COMMON + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [_hipcc(), "-x", "hip"] + COMMON + ["-c", src, "-o", obj]
+        cmd = [_hipcc(), "-x", "hip"] + COMMON + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(x for x in r.stderr.splitlines() if noise not in x)
@@ -48,23 +53,30 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose=False):
-    """Compile every source and link libfsa.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose=False, debug_bounds=False):
+    """Compile every source and link libfsa.so (libfsa_debug.so with
+    debug_bounds); returns the library path."""
+    build_dir = BUILD_DIR + ("_debug" if debug_bounds else "")
+    lib = DEBUG_LIB if debug_bounds else LIB
+    extra = ["-DFSA_DEBUG_BOUNDS"] if debug_bounds else []
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "fsa_api.cpp")]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(lambda x: _compile(x, build_dir, extra), srcs))
     for obj, err in results:
         if verbose and err.strip():
             print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--all" in sys.argv or "--debug-bounds" not in sys.argv:
+        print(build(verbose=True))
+    if "--all" in sys.argv or "--debug-bounds" in sys.argv:
+        print(build(verbose=True, debug_bounds=True))

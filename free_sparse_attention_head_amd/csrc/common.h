@@ -7,6 +7,38 @@
 
 namespace fsa {
 
+// Debug builds (-DFSA_DEBUG_BOUNDS) record inputs that release builds skip
+// silently: each translation unit that includes this header owns one device
+// word of flag bits (FSA_DBG_* in fsa.h), raised with a device-scope atomic
+// OR where a bad list entry, index or page id is met, and read back on the
+// host through debug_flags_of_tu().  Release builds compile the checks out.
+#ifdef FSA_DEBUG_BOUNDS
+static __device__ uint32_t g_debug_flags;
+#define FSA_DEBUG_RAISE(cond, bit)                                       \
+  do {                                                                   \
+    if (cond) __hip_atomic_fetch_or(&::fsa::g_debug_flags, (uint32_t)(bit), \
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
+  } while (0)
+#else
+#define FSA_DEBUG_RAISE(cond, bit) \
+  do {                             \
+  } while (0)
+#endif
+
+// host: this translation unit's flags (0 in a release build), cleared if asked
+static inline hipError_t debug_flags_of_tu(uint32_t* flags, bool clear) {
+#ifdef FSA_DEBUG_BOUNDS
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_debug_flags), sizeof(uint32_t));
+  if (e != hipSuccess || !clear) return e;
+  const uint32_t zero = 0u;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &zero, sizeof(uint32_t));
+#else
+  (void)clear;
+  *flags = 0u;
+  return hipSuccess;
+#endif
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));

@@ -44,7 +44,7 @@ constexpr int kRowBatch = 1024;  // positions resolved to pool rows at a time
 // launch from the longest possible list, but a segment list may admit far
 // fewer tokens; surplus splits then take no positions and write empty
 // partials, which the combine skips.
-constexpr int kMinSplitPositions = 256;
+constexpr int kMinSplitPositions = 64;
 
 template <int D, int NH, int MODE>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
@@ -85,13 +85,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     // are compacted in order with their exclusive prefix of lengths
     static_assert(kMaxSeg == 64, "one segment per lane of a wave");
     if (wave == 0) {
+      // the count and every segment slot are read together (one round trip)
       int ns = nseg[b];
+      int a = 0, e = 0;
+      if (l < min(max_seg, kMaxSeg)) {
+        a = seg[((size_t)b * max_seg + l) * 2];
+        e = seg[((size_t)b * max_seg + l) * 2 + 1];
+      }
+      FSA_DEBUG_RAISE(l == 0 && (ns < 0 || ns > max_seg), FSA_DBG_SEGMENT);
       ns = ns < 0 ? 0 : (ns > max_seg ? max_seg : ns);
       ns = ns > kMaxSeg ? kMaxSeg : ns;
-      int a = 0, len = 0;
+#ifdef FSA_DEBUG_BOUNDS
+      // ranges must be sorted and disjoint: each starts at or after the
+      // previous one's end (lanes are consecutive segments)
+      const int prev_end = __shfl_up(e, 1, 64);
+      FSA_DEBUG_RAISE(l > 0 && l < ns && a < prev_end, FSA_DBG_SEGMENT);
+#endif
+      int len = 0;
       if (l < ns) {
-        a = max(seg[((size_t)b * max_seg + l) * 2], 0);
-        len = max(min(seg[((size_t)b * max_seg + l) * 2 + 1], n) - a, 0);
+        a = max(a, 0);
+        len = max(min(e, n) - a, 0);
+      } else {
+        a = 0;
       }
       const uint64_t valid = __ballot(len > 0);
       const int rank = __popcll(valid & ((1ull << l) - 1ull));
@@ -143,6 +158,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   auto row_of = [&](int tok) -> uint32_t {
     const int page = ptb[min(max(tok, 0), max(n - 1, 0)) >> 4];
     const bool ok = (tok >= 0) & (tok < n) & (page >= 0) & (page < num_pages);
+    // -1 marks an empty slot (top-k of a short sequence, union padding)
+    FSA_DEBUG_RAISE(tok < -1 || tok >= n, FSA_DBG_TOKEN_INDEX);
+    FSA_DEBUG_RAISE(tok >= 0 && tok < n && (page < 0 || page >= num_pages), FSA_DBG_PAGE_ID);
     const uint32_t row = ((uint32_t)page * (uint32_t)Hkv + (uint32_t)g) * 16u + (uint32_t)(tok & 15);
     // a select, not a branch, so that the next lookup's read can issue first
     return __builtin_unpredictable(ok) ? row : kNoRow;
@@ -334,7 +352,7 @@ int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split) {
   // per split
   const int target = listed ? 1024 : 2048;
   int ns = (target + items - 1) / items;
-  const int cap = (len + 255) / 256;
+  const int cap = (len + kMinSplitPositions - 1) / kMinSplitPositions;
   if (ns > cap) ns = cap;
   return ns < 1 ? 1 : ns;
 }
@@ -438,6 +456,10 @@ hipError_t noalloc_scratch(void** ptr) {
   if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
   *ptr = g_scratch_ptr[dev];
   return hipSuccess;
+}
+
+hipError_t debug_flags_decode(uint32_t* flags, bool clear) {
+  return debug_flags_of_tu(flags, clear);
 }
 
 }  // namespace fsa

@@ -102,6 +102,26 @@ int check_kv_select(const fsa_kv_select* sel, const DecodeDims& d) {
 
 extern "C" {
 
+int fsa_debug_flags(uint32_t* flags, int clear) {
+  if (!flags) return FSA_ERR_NULL;
+  int rc = device_check();
+  if (rc) return rc;
+  uint32_t all = 0u;
+  hipError_t (*const readers[])(uint32_t*, bool) = {
+      fsa::debug_flags_prefill_f32, fsa::debug_flags_prefill_bf16, fsa::debug_flags_topk,
+      fsa::debug_flags_decode};
+  for (auto rd : readers) {
+    uint32_t f = 0u;
+    if (rd(&f, clear != 0) != hipSuccess) return FSA_ERR_LAUNCH;
+    all |= f;
+  }
+#ifndef FSA_DEBUG_BOUNDS
+  all |= FSA_DBG_UNAVAILABLE;
+#endif
+  *flags = all;
+  return FSA_OK;
+}
+
 const char* fsa_status_string(int status) {
   switch (status) {
     case FSA_OK: return "ok";
@@ -120,6 +140,9 @@ int fsa_device_check(void) { return device_check(); }
 
 size_t fsa_workspace_size(int op, const void* shape, const void* params) {
   if (shape == nullptr) return 0;
+  if (op != FSA_OP_SELECT_BLOCKS && op != FSA_OP_PREFILL_ATTN && op != FSA_OP_TOPK &&
+      op != FSA_OP_DECODE_ATTN)
+    return 0;  // the shape is not read: its type depends on the op
   if (op == FSA_OP_SELECT_BLOCKS || op == FSA_OP_PREFILL_ATTN) {
     PrefillDims d;
     if (check_prefill_shape(static_cast<const fsa_prefill_shape*>(shape), &d) != FSA_OK) return 0;

@@ -40,6 +40,13 @@ hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
                                     const int32_t* bcnt, float scale, void* out, float* lse,
                                     hipStream_t st);
 
+// flag bits (FSA_DBG_*) each translation unit with input checks has raised
+// since its last clear; all 0 unless built with FSA_DEBUG_BOUNDS
+hipError_t debug_flags_prefill_f32(uint32_t* flags, bool clear);
+hipError_t debug_flags_prefill_bf16(uint32_t* flags, bool clear);
+hipError_t debug_flags_topk(uint32_t* flags, bool clear);
+hipError_t debug_flags_decode(uint32_t* flags, bool clear);
+
 // topk.hip
 constexpr int kTopkMaxSeqLen = 1 << 23;  // tokens per sequence that top-k supports
 // decode splits per (sequence, head item), at most (n_split argument and combine)

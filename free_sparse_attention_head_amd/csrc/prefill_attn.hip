@@ -136,6 +136,7 @@ __global__ __launch_bounds__(BLK * 2, D == 128 ? 1 : 2) void prefill_attn_kernel
     int j = -1;
     if (e < cnt) j = bidx ? bidx[(size_t)row * nB + e] : e;
     const int ok = (j >= 0 && j <= i) ? 1 : 0;
+    FSA_DEBUG_RAISE(e < cnt && !ok, FSA_DBG_BLOCK_INDEX);
     int tot;
     const int pos = block_excl_scan(ok, scan_tmp, &tot);
     if (ok) Ls[nvalid + pos] = j;
@@ -286,6 +287,10 @@ hipError_t launch_prefill_attn(bool f32, const void* q, const void* k, const voi
   FSA_PA(64, 64) FSA_PA(64, 128) FSA_PA(128, 64) FSA_PA(128, 128)
 #undef FSA_PA
   return hipErrorInvalidValue;
+}
+
+hipError_t debug_flags_prefill_f32(uint32_t* flags, bool clear) {
+  return debug_flags_of_tu(flags, clear);
 }
 
 }  // namespace fsa

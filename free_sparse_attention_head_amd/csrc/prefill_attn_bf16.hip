@@ -165,6 +165,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     int j = -1;
     if (e < cnt) j = bidx ? bidx[(size_t)row * nB + e] : e;
     const int ok = (j >= 0 && j <= i) ? 1 : 0;
+    FSA_DEBUG_RAISE(e < cnt && !ok, FSA_DBG_BLOCK_INDEX);
     int tot;
     const int pos = block_excl_scan(ok, scan_tmp, &tot);
     if (ok) Ls[nvalid + pos] = (uint16_t)j;
@@ -494,6 +495,10 @@ hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
   if (d.D == 128) return launch_for_block<128>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
   if (d.D == 64) return launch_for_block<64>(q, k, v, d, bidx, bcnt, scale, out, lse, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t debug_flags_prefill_bf16(uint32_t* flags, bool clear) {
+  return debug_flags_of_tu(flags, clear);
 }
 
 }  // namespace fsa

@@ -105,6 +105,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   for (int x = tid; x < TPAGES; x += 256) {
     const int tok = t0 + x * 16;
     int p = tok < t1 ? ptb[tok >> 4] : -1;
+    FSA_DEBUG_RAISE(tok < t1 && (p < 0 || p >= num_pages), FSA_DBG_PAGE_ID);
     pg[x] = (p >= 0 && p < num_pages) ? p : -1;
   }
   uint4 qv[G];
@@ -735,6 +736,10 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
                      cidx, ccnt, hist, sl, rows_per_b, d.max_seq_len, L.tt, L.tiles, L.cstride, k,
                      idx, kth);
   return hipGetLastError();
+}
+
+hipError_t debug_flags_topk(uint32_t* flags, bool clear) {
+  return debug_flags_of_tu(flags, clear);
 }
 
 }  // namespace fsa

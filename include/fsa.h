@@ -55,7 +55,11 @@ enum {
   FSA_ERR_ARG = -7        /* another argument is out of range                    */
 };
 
-typedef enum { FSA_BF16 = 0, FSA_F32 = 1 } fsa_dtype;
+/* Element type of a call's tensors.  A plain 32-bit integer (not an enum
+ * type), so that any value a caller passes is well defined to inspect:
+ * values other than these two are rejected with FSA_ERR_DTYPE. */
+typedef int32_t fsa_dtype;
+enum { FSA_BF16 = 0, FSA_F32 = 1 };
 
 typedef struct {
   int32_t B, S, Hq, Hkv, D, T;
@@ -96,7 +100,7 @@ enum { FSA_SEL_ALL = 0, FSA_SEL_INDEX = 1, FSA_SEL_SEGMENT = 2, FSA_SEL_INDEX_KV
  *                    sequence must be sorted and disjoint, and are clipped
  *                    to [0, seq_lens[b]); shared by all heads.
  * n_split: split-KV factor per (sequence, head), 0 <= n_split <= 4096; 0
- * picks one.  A split takes at least 256 list positions, so splits beyond
+ * picks one.  A split takes at least 64 list positions, so splits beyond
  * what a short list needs stay empty (their partials carry no weight). */
 typedef struct {
   int32_t mode;
@@ -279,6 +283,31 @@ int fsa_build_segments(int mode, int n, int chunk_start, int chunk_len, int loca
  * Returns FSA_ERR_ARG for min_nb < 0 and as fsa_build_segments otherwise. */
 int fsa_build_segments_nb(int mode, int n, int chunk_start, int chunk_len, int local_len,
                           int n_sink, int page, int min_nb, int32_t* out, int* n_seg);
+
+/* fsa_debug_flags -- inputs that the kernels skip, recorded by a debug build.
+ * Release builds skip bad inputs silently (see each call); a library built
+ * with FSA_DEBUG_BOUNDS (python -m free_sparse_attention_head_amd.build
+ * --debug-bounds, libfsa_debug.so) also raises, on the device, one flag bit
+ * per kind of bad input it met:
+ *   FSA_DBG_BLOCK_INDEX  a prefill block-list entry outside [0, i]
+ *   FSA_DBG_TOKEN_INDEX  a decode index entry below -1 or at or past seq_len
+ *                        (-1 marks an empty slot and is not flagged)
+ *   FSA_DBG_PAGE_ID      a page-table entry outside [0, num_pages) for a
+ *                        token inside the sequence (decode and top-k)
+ *   FSA_DBG_SEGMENT      an n_seg outside [0, max_seg], or segment ranges
+ *                        that are not sorted and disjoint
+ * flags (host) receives the bits raised since the last clear, on every GPU
+ * call of this process; clear != 0 resets them.  The read synchronises with
+ * the null stream: synchronise other streams first.  A release build sets
+ * only FSA_DBG_UNAVAILABLE. */
+enum {
+  FSA_DBG_BLOCK_INDEX = 1,
+  FSA_DBG_TOKEN_INDEX = 2,
+  FSA_DBG_PAGE_ID = 4,
+  FSA_DBG_SEGMENT = 8,
+  FSA_DBG_UNAVAILABLE = (int)0x80000000u
+};
+int fsa_debug_flags(uint32_t* flags, int clear);
 
 /* Static text for a status code. */
 const char* fsa_status_string(int status);
