@@ -7,9 +7,10 @@ One step runs every row of the hot path once over resident synthetic inputs:
     select_blocks (two-branch selector tuned to the target density) ->
     sparse_prefill_attn;
   Kascade decode group, 128K context (B=32, 32 query / 8 KV heads, D=128,
-    bf16 KV in shuffled 16-token pages, 4 layers): topk_indices (k=2048) at
-    the anchor layer, then sparse_decode_attn at those indices for the anchor
-    and the three reuse layers;
+    bf16 KV in shuffled 16-token pages, 4 layers): topk_indices_scored
+    (k=2048) at the anchor layer, the anchor's own attention at those indices
+    from the kept keys' scores (V read only), then sparse_decode_attn at the
+    same indices for the three reuse layers;
   segment decode, 1M context (B=4, same heads, shuffled pages): global, focus
     (2048-token chunk + 1024 local tail), local (1024) and streaming
     (4 sinks + 1024 window) masks, and one mixed batch whose sequences draw
@@ -409,6 +410,7 @@ def make_decode(fsa, workloads, seed=1003):
     d = workloads.decode_inputs(D["B"], D["N"], D["Hq"], D["Hkv"], D["D"], layers=D["layers"],
                                 seed=seed, device="cuda")
     d["idx"] = torch.empty((D["B"], D["Hq"], D["k"]), dtype=torch.int32, device="cuda")
+    d["scores"] = torch.empty((D["B"], D["Hq"], D["k"]), dtype=torch.float32, device="cuda")
     d["kth"] = torch.empty((D["B"], D["Hq"]), dtype=torch.float32, device="cuda")
     d["out"] = [torch.empty((D["B"], D["Hq"], D["D"]), dtype=torch.bfloat16, device="cuda")
                 for _ in range(D["layers"])]
@@ -485,14 +487,20 @@ def step_prefill(fsa, pf, tm):
 
 
 def step_decode(fsa, dc, tm):
-    """Kascade group: anchor top-k, then index decode for anchor + reuse layers."""
+    """Kascade group: anchor top-k (with the kept keys' scores), the anchor's
+    attention at its top-k from those scores (V read only), then index decode
+    for the reuse layers."""
     Dd = DECODE
     L = dc["layers"]
-    tm.run("topk_indices", lambda: fsa.topk_indices(L[0]["q"], L[0]["k"], dc["page_table"],
-                                                    dc["seq_lens"], Dd["k"], idx=dc["idx"],
-                                                    kth=dc["kth"], ws=dc.get("topk_ws")))
-    for li in range(Dd["layers"]):
-        tm.run("decode_index" if li else "decode_index_anchor", lambda li=li: fsa.sparse_decode_attn(
+    tm.run("topk_indices", lambda: fsa.topk_indices_scored(
+        L[0]["q"], L[0]["k"], dc["page_table"], dc["seq_lens"], Dd["k"], idx=dc["idx"],
+        scores=dc["scores"], kth=dc["kth"], ws=dc.get("topk_ws")))
+    tm.run("decode_index_anchor", lambda: fsa.sparse_decode_attn(
+        L[0]["q"], L[0]["k"], L[0]["v"], dc["page_table"], dc["seq_lens"],
+        mode=fsa.SEL_INDEX_SCORED, idx=dc["idx"], scores=dc["scores"], out=dc["out"][0],
+        want_lse=False, ws=dc.get("dec_ws")))
+    for li in range(1, Dd["layers"]):
+        tm.run("decode_index", lambda li=li: fsa.sparse_decode_attn(
             L[li]["q"], L[li]["k"], L[li]["v"], dc["page_table"], dc["seq_lens"],
             mode=fsa.SEL_INDEX, idx=dc["idx"], out=dc["out"][li], want_lse=False,
             ws=dc.get("dec_ws")))
@@ -870,6 +878,9 @@ def main():
         "decode": {"topk_ms": round(topk_ms, 4),
                    "topk_scan_GBps": round(scan_bytes / (topk_ms * 1e-3) / 1e9, 1),
                    "anchor_decode_ms": round(k_ms["decode_index_anchor"][0], 4),
+                   "anchor_decode_GBps": round(idx_bytes / 2 / (k_ms["decode_index_anchor"][0] * 1e-3)
+                                               / 1e9, 1),
+                   "anchor_ms": round(topk_ms + k_ms["decode_index_anchor"][0], 4),
                    "reuse_decode_ms": round(reuse_ms, 4), "reuse_GBps": round(reuse_gbps, 1),
                    "group_ms": round(group_ms, 4),
                    "group_GBps": round(group_bytes / (group_ms * 1e-3) / 1e9, 1)},

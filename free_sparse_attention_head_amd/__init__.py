@@ -21,13 +21,13 @@ import torch
 from . import _lib as L
 
 __all__ = ["block_stats", "select_blocks", "sparse_prefill_attn", "topk_indices",
-           "topk_indices_kv", "topk_union_kv", "sparse_decode_attn", "sparse_decode_attn_noalloc", "build_segments", "workspace_size", "FsaError",
-           "SEL_ALL", "SEL_INDEX", "SEL_SEGMENT", "SEL_INDEX_KV", "SEG_GLOBAL", "SEG_FOCUS",
+           "topk_indices_kv", "topk_indices_scored", "topk_union_kv", "sparse_decode_attn", "sparse_decode_attn_noalloc", "build_segments", "workspace_size", "FsaError",
+           "SEL_ALL", "SEL_INDEX", "SEL_SEGMENT", "SEL_INDEX_KV", "SEL_INDEX_SCORED", "SEG_GLOBAL", "SEG_FOCUS",
            "SEG_LOCAL", "SEG_STREAMING"]
 
 FsaError = L.FsaError
-SEL_ALL, SEL_INDEX, SEL_SEGMENT, SEL_INDEX_KV = (L.FSA_SEL_ALL, L.FSA_SEL_INDEX, L.FSA_SEL_SEGMENT,
-                                             L.FSA_SEL_INDEX_KV)
+SEL_ALL, SEL_INDEX, SEL_SEGMENT, SEL_INDEX_KV, SEL_INDEX_SCORED = (
+    L.FSA_SEL_ALL, L.FSA_SEL_INDEX, L.FSA_SEL_SEGMENT, L.FSA_SEL_INDEX_KV, L.FSA_SEL_INDEX_SCORED)
 SEG_GLOBAL, SEG_FOCUS, SEG_LOCAL, SEG_STREAMING = (L.FSA_SEG_GLOBAL, L.FSA_SEG_FOCUS,
                                                    L.FSA_SEG_LOCAL, L.FSA_SEG_STREAMING)
 
@@ -269,6 +269,33 @@ def topk_indices(q, k_pool, page_table, seq_lens, k, max_seq_len=None, idx=None,
                  idx, kth, ws)
 
 
+def topk_indices_scored(q, k_pool, page_table, seq_lens, k, max_seq_len=None, idx=None,
+                        scores=None, kth=None, ws=None):
+    """topk_indices plus each kept key's raw fp32 score.  Returns idx
+    [B,Hq,k], scores [B,Hq,k] and kth [B,Hq]; idx and scores feed
+    sparse_decode_attn with mode=SEL_INDEX_SCORED, which then reads only V."""
+    lib = L.load()
+    shape = _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
+    B, Hq = q.shape[0], q.shape[1]
+    if idx is None:
+        idx = torch.empty((B, Hq, k), dtype=torch.int32, device=q.device)
+    if scores is None:
+        scores = torch.empty((B, Hq, k), dtype=torch.float32, device=q.device)
+    if kth is None:
+        kth = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(idx, "idx", torch.int32, (B, Hq, k))
+    _need(scores, "scores", torch.float32, (B, Hq, k))
+    _need(kth, "kth", torch.float32, (B, Hq))
+    _same_device(q, k_pool, page_table, seq_lens, idx, scores, kth, ws)
+    wsb = workspace_size("topk", shape, int(k))
+    ws, wsn = _ws(wsb, q.device, ws)
+    L.check("topk_indices_scored", lib.topk_indices_scored(
+        _dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(page_table), _ptr(seq_lens),
+        ctypes.byref(shape), int(k), _ptr(idx), _ptr(scores), _ptr(kth), _ptr(ws), wsn,
+        _stream(q.device)))
+    return idx, scores, kth
+
+
 def topk_indices_kv(q, k_pool, page_table, seq_lens, k, max_seq_len=None, idx=None, kth=None,
                     ws=None):
     """Exact top-k per KV head of the max over its query heads' scores.
@@ -302,17 +329,19 @@ def topk_union_kv(idx, Hkv, out=None, cnt=None):
 
 
 def _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments, n_seg, n_split,
-                 max_seq_len, want_lse, out, lse):
+                 max_seq_len, want_lse, out, lse, scores=None):
     """Checks of a decode call's tensors; returns (KvSelect, out, lse)."""
     _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
     B, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     _need(v_pool, "v_pool", torch.bfloat16, k_pool.shape)
-    if mode in (SEL_INDEX, SEL_INDEX_KV):
+    if mode in (SEL_INDEX, SEL_INDEX_KV, SEL_INDEX_SCORED):
         _need(idx, "idx", torch.int32, ndim=3)
-        heads = Hq if mode == SEL_INDEX else Hkv
+        heads = Hkv if mode == SEL_INDEX_KV else Hq
         if idx.shape[0] != B or idx.shape[1] != heads:
             raise ValueError(f"idx must be [{B}, {heads}, k], got {tuple(idx.shape)}")
+        if mode == SEL_INDEX_SCORED:
+            _need(scores, "scores", torch.float32, idx.shape)
     elif mode == SEL_SEGMENT:
         _need(segments, "segments", torch.int32, ndim=3)
         if segments.shape[0] != B or segments.shape[2] != 2:
@@ -329,11 +358,13 @@ def _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments, n
         lse = None
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq))
-    _same_device(q, k_pool, v_pool, page_table, seq_lens, idx, segments, n_seg, out, lse)
-    sel = L.KvSelect(int(mode), None, 0, None, None, 0, int(n_split))
-    if mode in (SEL_INDEX, SEL_INDEX_KV):
+    _same_device(q, k_pool, v_pool, page_table, seq_lens, idx, segments, n_seg, out, lse, scores)
+    sel = L.KvSelect(int(mode), None, 0, None, None, 0, int(n_split), None)
+    if mode in (SEL_INDEX, SEL_INDEX_KV, SEL_INDEX_SCORED):
         sel.idx = _ptr(idx).value
         sel.k = idx.shape[2]
+        if mode == SEL_INDEX_SCORED:
+            sel.scores = _ptr(scores).value
     elif mode == SEL_SEGMENT:
         sel.segments = _ptr(segments).value
         sel.n_seg = _ptr(n_seg).value
@@ -343,13 +374,14 @@ def _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments, n
 
 def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, idx=None,
                        segments=None, n_seg=None, scale=None, n_split=0, max_seq_len=None,
-                       want_lse=True, out=None, lse=None, ws=None):
+                       want_lse=True, out=None, lse=None, ws=None, scores=None):
     """Split-KV paged decode attention.  mode SEL_ALL / SEL_INDEX (idx [B,Hq,k]) /
-    SEL_INDEX_KV (idx [B,Hkv,k]) / SEL_SEGMENT (segments [B,max_seg,2], n_seg [B]).
+    SEL_INDEX_KV (idx [B,Hkv,k]) / SEL_INDEX_SCORED (idx and scores [B,Hq,k],
+    V read only) / SEL_SEGMENT (segments [B,max_seg,2], n_seg [B]).
     Returns (out bf16 [B,Hq,D], lse fp32 [B,Hq] or None)."""
     lib = L.load()
     sel, out, lse = _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments,
-                                 n_seg, n_split, max_seq_len, want_lse, out, lse)
+                                 n_seg, n_split, max_seq_len, want_lse, out, lse, scores)
     shape = _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
     D = q.shape[2]
     if scale is None:
@@ -365,14 +397,15 @@ def sparse_decode_attn(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, id
 
 def sparse_decode_attn_noalloc(q, k_pool, v_pool, page_table, seq_lens, mode=SEL_ALL, idx=None,
                                segments=None, n_seg=None, scale=None, n_split=0,
-                               max_seq_len=None, want_lse=True, out=None, lse=None):
+                               max_seq_len=None, want_lse=True, out=None, lse=None,
+                               scores=None):
     """sparse_decode_attn without a workspace: the library keeps the split
     partials in its own device array (FSA_NOALLOC_SCRATCH_BYTES per GPU).
     Calls that overlap on one GPU race.  Pass out (and lse) to allocate
     nothing here either."""
     lib = L.load()
     sel, out, lse = _decode_args(q, k_pool, v_pool, page_table, seq_lens, mode, idx, segments,
-                                 n_seg, n_split, max_seq_len, want_lse, out, lse)
+                                 n_seg, n_split, max_seq_len, want_lse, out, lse, scores)
     shape = _decode_shape(q, k_pool, page_table, max_seq_len, seq_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[2])

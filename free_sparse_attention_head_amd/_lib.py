@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG, "libfsa.so")
 FSA_OK, FSA_ERR_NULL, FSA_ERR_SHAPE, FSA_ERR_DTYPE = 0, -1, -2, -3
 FSA_ERR_WORKSPACE, FSA_ERR_NO_DEVICE, FSA_ERR_LAUNCH, FSA_ERR_ARG = -4, -5, -6, -7
 FSA_BF16, FSA_F32 = 0, 1
-FSA_SEL_ALL, FSA_SEL_INDEX, FSA_SEL_SEGMENT, FSA_SEL_INDEX_KV = 0, 1, 2, 3
+FSA_SEL_ALL, FSA_SEL_INDEX, FSA_SEL_SEGMENT, FSA_SEL_INDEX_KV, FSA_SEL_INDEX_SCORED = 0, 1, 2, 3, 4
 FSA_OP_SELECT_BLOCKS, FSA_OP_PREFILL_ATTN, FSA_OP_TOPK, FSA_OP_DECODE_ATTN = 1, 2, 3, 4
 FSA_SEG_GLOBAL, FSA_SEG_FOCUS, FSA_SEG_LOCAL, FSA_SEG_STREAMING = 0, 1, 2, 3
 FSA_NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -42,7 +42,7 @@ class DecodeShape(ctypes.Structure):
 class KvSelect(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("idx", c_void_p), ("k", ctypes.c_int32),
                 ("segments", c_void_p), ("n_seg", c_void_p), ("max_seg", ctypes.c_int32),
-                ("n_split", ctypes.c_int32)]
+                ("n_split", ctypes.c_int32), ("scores", c_void_p)]
 
 
 # name -> (restype, argtypes)
@@ -58,6 +58,9 @@ SIGNATURES = {
     "topk_indices": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                              ctypes.POINTER(DecodeShape), c_int, c_void_p, c_void_p, c_void_p,
                              c_size_t, c_void_p]),
+    "topk_indices_scored": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    ctypes.POINTER(DecodeShape), c_int, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]),
     "topk_indices_kv": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                 ctypes.POINTER(DecodeShape), c_int, c_void_p, c_void_p, c_void_p,
                                 c_size_t, c_void_p]),

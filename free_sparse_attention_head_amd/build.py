@@ -1,8 +1,8 @@
 """Build libfsa.so (the C-ABI HIP library) in-tree for gfx950.
 
-    python -m free_sparse_attention_head_amd.build                 # libfsa.so
+    python -m free_sparse_attention_head_amd.build                 # both libraries
+    python -m free_sparse_attention_head_amd.build --release-only  # libfsa.so
     python -m free_sparse_attention_head_amd.build --debug-bounds  # libfsa_debug.so
-    python -m free_sparse_attention_head_amd.build --all           # both
 
 Every HIP translation unit is compiled with hipcc for --offload-arch=gfx950 in
 parallel, then linked into free_sparse_attention_head_amd/libfsa.so.  Packed
@@ -76,7 +76,7 @@ def build(verbose=False, debug_bounds=False):
 
 
 if __name__ == "__main__":
-    if "--all" in sys.argv or "--debug-bounds" not in sys.argv:
+    if "--debug-bounds" not in sys.argv:
         print(build(verbose=True))
-    if "--all" in sys.argv or "--debug-bounds" in sys.argv:
+    if "--release-only" not in sys.argv:
         print(build(verbose=True, debug_bounds=True))

@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ sl, int Hq, int Hkv, int max_pages, int num_pages,
-    int max_seq_len, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ seg,
+    int max_seq_len, const int32_t* __restrict__ idx, const float* __restrict__ scores, int k,
+    const int32_t* __restrict__ seg,
     const int32_t* __restrict__ nseg, int max_seg, int n_split, float scale_log2,
     float* __restrict__ part, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int LPR = D / 8;            // lanes per key row
@@ -64,15 +65,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ int seg_lo[kMaxSeg], seg_pre[kMaxSeg + 1];
   __shared__ int s_nseg;
   __shared__ uint32_t rows_lds[kRowBatch];  // pool row of each position of the batch
+  constexpr bool SCORED = MODE == FSA_SEL_INDEX_SCORED;
+  // scored mode: the raw score of each position of the batch (keys not read)
+  __shared__ float sc_lds[SCORED ? kRowBatch : 1];
 
   const int G = Hq / Hkv;
   const int s = blockIdx.x % n_split;
   const int item = blockIdx.x / n_split;  // b * (heads per item layout) + hh
-  const int per_b = (MODE == FSA_SEL_INDEX) ? Hq : Hkv;
+  constexpr bool PER_HEAD = MODE == FSA_SEL_INDEX || MODE == FSA_SEL_INDEX_SCORED;
+  const int per_b = PER_HEAD ? Hq : Hkv;
   const int hh = item % per_b, b = item / per_b;
-  const int g = (MODE == FSA_SEL_INDEX) ? hh / G : hh;
-  const int h0 = (MODE == FSA_SEL_INDEX) ? hh : hh * G;  // first query head of the item
-  constexpr bool LISTED = MODE == FSA_SEL_INDEX || MODE == FSA_SEL_INDEX_KV;
+  const int g = PER_HEAD ? hh / G : hh;
+  const int h0 = PER_HEAD ? hh : hh * G;  // first query head of the item
+  constexpr bool LISTED = MODE == FSA_SEL_INDEX || MODE == FSA_SEL_INDEX_KV || SCORED;
   const int n = min(max(sl[b], 0), max_seq_len);
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
@@ -193,6 +198,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kRowBatch / kDecThreads; ++u) rows_lds[u * kDecThreads + tid] = rw[u];
+    if constexpr (SCORED) {
+      const float* scr = scores + ((size_t)b * per_b + hh) * k;
+#pragma unroll
+      for (int u = 0; u < kRowBatch / kDecThreads; ++u) {
+        const int x = u * kDecThreads + tid;
+        sc_lds[x] = x < b1 - b0 ? scr[b0 + x] : 0.f;
+      }
+    }
     __syncthreads();
     for (int base = b0; base < b1; base += NSLOT * RB) {
       uint4 kr[RB], vr[RB];
@@ -203,7 +216,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         const uint32_t row = pos < b1 ? rows_lds[pos - b0] : kNoRow;
         ok[r] = row != kNoRow;
         if (ok[r]) {
-          kr[r] = *reinterpret_cast<const uint4*>(kpool + (size_t)row * D + dl * 8);
+          if constexpr (!SCORED)
+            kr[r] = *reinterpret_cast<const uint4*>(kpool + (size_t)row * D + dl * 8);
           vr[r] = *reinterpret_cast<const uint4*>(vpool + (size_t)row * D + dl * 8);
         } else {
           kr[r] = make_uint4(0, 0, 0, 0);
@@ -216,7 +230,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-          float d = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
+          float d;
+          if constexpr (SCORED) {
+            const int pos = base + slot * RB + r;
+            d = sc_lds[min(pos - b0, kRowBatch - 1)];
+          } else {
+            d = group_sum<LPR>(dot8_bf16(qv[x], kr[r], 0.f));
+          }
           sc[r] = ok[r] ? d * scale_log2 : -INFINITY;
           mx = fmaxf(mx, sc[r]);
         }
@@ -344,8 +364,9 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
 
 int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split) {
   if (n_split > 0) return n_split;
-  const int items = mode == FSA_SEL_INDEX ? d.B * d.Hq : d.B * d.Hkv;
-  const bool listed = mode == FSA_SEL_INDEX || mode == FSA_SEL_INDEX_KV;
+  const bool per_head = mode == FSA_SEL_INDEX || mode == FSA_SEL_INDEX_SCORED;
+  const int items = per_head ? d.B * d.Hq : d.B * d.Hkv;
+  const bool listed = per_head || mode == FSA_SEL_INDEX_KV;
   const int len = listed ? k : d.max_seq_len;
   // aim for >= 2048 workgroups (1024 for listed positions: a single split then
   // writes the output itself, with no combine launch) and >= 256 positions
@@ -365,7 +386,7 @@ size_t decode_ws_bytes(const DecodeDims& d, int mode, int k, int n_split) {
 template <int D>
 static hipError_t launch_dec_d(const void* q, const void* kp, const void* vp, const int32_t* pt,
                                const int32_t* sl, const DecodeDims& d, int mode,
-                               const int32_t* idx, int k, const int32_t* seg,
+                               const int32_t* idx, const float* scores, int k, const int32_t* seg,
                                const int32_t* nseg, int max_seg, int ns, float sl2,
                                void* out, float* lse, float* part, hipStream_t st) {
   const uint16_t* Q = static_cast<const uint16_t*>(q);
@@ -375,13 +396,18 @@ static hipError_t launch_dec_d(const void* q, const void* kp, const void* vp, co
   if (mode == FSA_SEL_INDEX) {
     hipLaunchKernelGGL((decode_split_kernel<D, 1, FSA_SEL_INDEX>), dim3(d.B * d.Hq * ns),
                        dim3(kDecThreads), 0, st, Q, Kp, Vp, pt, sl, d.Hq, d.Hkv, d.max_pages,
-                       d.num_pages, d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part,
-                       static_cast<uint16_t*>(out), lse);
+                       d.num_pages, d.max_seq_len, idx, scores, k, seg, nseg, max_seg, ns, sl2,
+                       part, static_cast<uint16_t*>(out), lse);
+  } else if (mode == FSA_SEL_INDEX_SCORED) {
+    hipLaunchKernelGGL((decode_split_kernel<D, 1, FSA_SEL_INDEX_SCORED>), dim3(d.B * d.Hq * ns),
+                       dim3(kDecThreads), 0, st, Q, Kp, Vp, pt, sl, d.Hq, d.Hkv, d.max_pages,
+                       d.num_pages, d.max_seq_len, idx, scores, k, seg, nseg, max_seg, ns, sl2,
+                       part, static_cast<uint16_t*>(out), lse);
   } else {
 #define FSA_DEC(GG, MM)                                                                        \
   hipLaunchKernelGGL((decode_split_kernel<D, GG, MM>), dim3(d.B * d.Hkv * ns), dim3(kDecThreads), \
                      0, st, Q, Kp, Vp, pt, sl, d.Hq, d.Hkv, d.max_pages, d.num_pages,           \
-                     d.max_seq_len, idx, k, seg, nseg, max_seg, ns, sl2, part,                \
+                     d.max_seq_len, idx, scores, k, seg, nseg, max_seg, ns, sl2, part,        \
                      static_cast<uint16_t*>(out), lse)
 #define FSA_DEC_G(GG)                         \
   if (G == GG) {                              \
@@ -405,18 +431,18 @@ static hipError_t launch_dec_d(const void* q, const void* kp, const void* vp, co
 
 hipError_t launch_decode_attn(const void* q, const void* kpool, const void* vpool,
                               const int32_t* pt, const int32_t* sl, const DecodeDims& d,
-                              int mode, const int32_t* idx, int k, const int32_t* seg,
-                              const int32_t* nseg, int max_seg, int n_split, float scale,
-                              void* out, float* lse, void* ws, hipStream_t st) {
+                              int mode, const int32_t* idx, const float* scores, int k,
+                              const int32_t* seg, const int32_t* nseg, int max_seg, int n_split,
+                              float scale, void* out, float* lse, void* ws, hipStream_t st) {
   const int ns = decode_pick_split(d, mode, k, n_split);
   float* part = static_cast<float*>(ws);
   const float sl2 = scale * kLog2e;
   if (d.D == 128)
-    return launch_dec_d<128>(q, kpool, vpool, pt, sl, d, mode, idx, k, seg, nseg, max_seg, ns,
-                             sl2, out, lse, part, st);
+    return launch_dec_d<128>(q, kpool, vpool, pt, sl, d, mode, idx, scores, k, seg, nseg,
+                             max_seg, ns, sl2, out, lse, part, st);
   if (d.D == 64)
-    return launch_dec_d<64>(q, kpool, vpool, pt, sl, d, mode, idx, k, seg, nseg, max_seg, ns,
-                            sl2, out, lse, part, st);
+    return launch_dec_d<64>(q, kpool, vpool, pt, sl, d, mode, idx, scores, k, seg, nseg,
+                            max_seg, ns, sl2, out, lse, part, st);
   return hipErrorInvalidValue;
 }
 

@@ -88,6 +88,10 @@ int check_kv_select(const fsa_kv_select* sel, const DecodeDims& d) {
       if (sel->idx == nullptr) return FSA_ERR_NULL;
       if (sel->k < 1) return FSA_ERR_ARG;
       return FSA_OK;
+    case FSA_SEL_INDEX_SCORED:
+      if (sel->idx == nullptr || sel->scores == nullptr) return FSA_ERR_NULL;
+      if (sel->k < 1) return FSA_ERR_ARG;
+      return FSA_OK;
     case FSA_SEL_SEGMENT:
       if (sel->segments == nullptr || sel->n_seg == nullptr) return FSA_ERR_NULL;
       if (sel->max_seg < 1 || sel->max_seg > kMaxSegments) return FSA_ERR_ARG;
@@ -159,9 +163,11 @@ size_t fsa_workspace_size(int op, const void* shape, const void* params) {
     const fsa_kv_select* sel = static_cast<const fsa_kv_select*>(params);
     if (sel == nullptr || sel->n_split < 0 || sel->n_split > kMaxSplit) return 0;
     if (sel->mode != FSA_SEL_ALL && sel->mode != FSA_SEL_INDEX && sel->mode != FSA_SEL_SEGMENT &&
-        sel->mode != FSA_SEL_INDEX_KV)
+        sel->mode != FSA_SEL_INDEX_KV && sel->mode != FSA_SEL_INDEX_SCORED)
       return 0;
-    if ((sel->mode == FSA_SEL_INDEX || sel->mode == FSA_SEL_INDEX_KV) && sel->k < 1) return 0;
+    if ((sel->mode == FSA_SEL_INDEX || sel->mode == FSA_SEL_INDEX_KV ||
+         sel->mode == FSA_SEL_INDEX_SCORED) && sel->k < 1)
+      return 0;
     return fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split);
   }
   return 0;
@@ -220,8 +226,8 @@ int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* 
 
 static int topk_common(fsa_dtype dt, const void* q, const void* k_pool,
                        const int32_t* page_table, const int32_t* seq_lens,
-                       const fsa_decode_shape* s, int k, bool pooled, int32_t* idx, float* kth,
-                       void* ws, size_t ws_bytes, hipStream_t st) {
+                       const fsa_decode_shape* s, int k, bool pooled, int32_t* idx,
+                       float* scores, float* kth, void* ws, size_t ws_bytes, hipStream_t st) {
   DecodeDims d;
   int rc = check_decode_shape(s, &d);
   if (rc) return rc;
@@ -233,19 +239,30 @@ static int topk_common(fsa_dtype dt, const void* q, const void* k_pool,
   if (ws_bytes < fsa::topk_ws_bytes(d, k)) return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;
   return launch_status(
-      fsa::launch_topk(q, k_pool, page_table, seq_lens, d, k, pooled, idx, kth, ws, st));
+      fsa::launch_topk(q, k_pool, page_table, seq_lens, d, k, pooled, idx, scores, kth, ws, st));
 }
 
 int topk_indices(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
                  const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
                  float* kth, void* ws, size_t ws_bytes, hipStream_t st) {
-  return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, false, idx, kth, ws, ws_bytes, st);
+  return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, false, idx, nullptr, kth, ws,
+                     ws_bytes, st);
+}
+
+int topk_indices_scored(fsa_dtype dt, const void* q, const void* k_pool,
+                        const int32_t* page_table, const int32_t* seq_lens,
+                        const fsa_decode_shape* s, int k, int32_t* idx, float* scores,
+                        float* kth, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!scores) return FSA_ERR_NULL;
+  return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, false, idx, scores, kth, ws,
+                     ws_bytes, st);
 }
 
 int topk_indices_kv(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
                     const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
                     float* kth, void* ws, size_t ws_bytes, hipStream_t st) {
-  return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, true, idx, kth, ws, ws_bytes, st);
+  return topk_common(dt, q, k_pool, page_table, seq_lens, s, k, true, idx, nullptr, kth, ws,
+                     ws_bytes, st);
 }
 
 int topk_union_kv(const int32_t* idx, int B, int Hq, int Hkv, int k, int32_t* out,
@@ -268,16 +285,19 @@ int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const vo
   int rc = check_decode_shape(s, &d);
   if (rc) return rc;
   if (dt != FSA_BF16) return FSA_ERR_DTYPE;
-  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return FSA_ERR_NULL;
   if ((rc = check_kv_select(sel, d))) return rc;
+  // keys are not read when their scores come with the indices
+  if (!q || (!k_pool && sel->mode != FSA_SEL_INDEX_SCORED) || !v_pool || !page_table ||
+      !seq_lens || !out)
+    return FSA_ERR_NULL;
   if (!isfinite(scale)) return FSA_ERR_ARG;
   if (!ws) return FSA_ERR_NULL;
   if (ws_bytes < fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split)) return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;
   return launch_status(fsa::launch_decode_attn(q, k_pool, v_pool, page_table, seq_lens, d,
-                                               sel->mode, sel->idx, sel->k, sel->segments,
-                                               sel->n_seg, sel->max_seg, sel->n_split, scale, out,
-                                               lse, ws, st));
+                                               sel->mode, sel->idx, sel->scores, sel->k,
+                                               sel->segments, sel->n_seg, sel->max_seg,
+                                               sel->n_split, scale, out, lse, ws, st));
 }
 
 int sparse_decode_attn_noalloc(fsa_dtype dt, const void* q, const void* k_pool,
@@ -289,8 +309,10 @@ int sparse_decode_attn_noalloc(fsa_dtype dt, const void* q, const void* k_pool,
   int rc = check_decode_shape(s, &d);
   if (rc) return rc;
   if (dt != FSA_BF16) return FSA_ERR_DTYPE;
-  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return FSA_ERR_NULL;
   if ((rc = check_kv_select(sel, d))) return rc;
+  if (!q || (!k_pool && sel->mode != FSA_SEL_INDEX_SCORED) || !v_pool || !page_table ||
+      !seq_lens || !out)
+    return FSA_ERR_NULL;
   if (!isfinite(scale)) return FSA_ERR_ARG;
   if (fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split) > fsa::kNoAllocScratchBytes)
     return FSA_ERR_WORKSPACE;
@@ -298,9 +320,9 @@ int sparse_decode_attn_noalloc(fsa_dtype dt, const void* q, const void* k_pool,
   void* scratch = nullptr;
   if (fsa::noalloc_scratch(&scratch) != hipSuccess) return FSA_ERR_NO_DEVICE;
   return launch_status(fsa::launch_decode_attn(q, k_pool, v_pool, page_table, seq_lens, d,
-                                               sel->mode, sel->idx, sel->k, sel->segments,
-                                               sel->n_seg, sel->max_seg, sel->n_split, scale, out,
-                                               lse, scratch, st));
+                                               sel->mode, sel->idx, sel->scores, sel->k,
+                                               sel->segments, sel->n_seg, sel->max_seg,
+                                               sel->n_split, scale, out, lse, scratch, st));
 }
 
 int fsa_build_segments(int mode, int n, int chunk_start, int chunk_len, int local_len,

@@ -53,9 +53,10 @@ constexpr int kTopkMaxSeqLen = 1 << 23;  // tokens per sequence that top-k suppo
 constexpr int kMaxSplit = 4096;
 size_t topk_ws_bytes(const DecodeDims& d, int k);
 // pooled: one index set per KV head from the max over its query heads' scores
+// scores (nullable): the raw score of each kept key, beside idx
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
-                       const DecodeDims& d, int k, bool pooled, int32_t* idx, float* kth, void* ws,
-                       hipStream_t st);
+                       const DecodeDims& d, int k, bool pooled, int32_t* idx, float* scores,
+                       float* kth, void* ws, hipStream_t st);
 
 // union of a KV head's G per-query-head index sets: G * k entries, padded
 // to a power of two, at most kUnionMax
@@ -74,7 +75,8 @@ int decode_pick_split(const DecodeDims& d, int mode, int k, int n_split);
 size_t decode_ws_bytes(const DecodeDims& d, int mode, int k, int n_split);
 hipError_t launch_decode_attn(const void* q, const void* kpool, const void* vpool,
                               const int32_t* pt, const int32_t* sl, const DecodeDims& d,
-                              int mode, const int32_t* idx, int k, const int32_t* seg,
+                              int mode, const int32_t* idx, const float* scores, int k,
+                              const int32_t* seg,
                               const int32_t* nseg, int max_seg, int n_split, float scale,
                               void* out, float* lse, void* ws, hipStream_t st);
 

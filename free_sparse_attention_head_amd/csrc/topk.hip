@@ -117,7 +117,27 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   uint32_t* coarse = hist + (size_t)rows_total * kBins1;  // [rows, kCoarse] after the bins
   constexpr int BPC = kBins1 / kCoarse;                   // bins per coarse bucket
   static_assert(kCoarse == 64 && BPC <= 64, "one coarse bucket per lane");
+  // A lane group's RB rows are consecutive tokens inside one 16-token page.
+  // Every wave issues all of its row loads on every step, with no branch
+  // around them (rows of a missing page, or past the tile, are read from page
+  // 0; their scores are replaced by 0 or never kept): the compiler then knows
+  // how many loads are younger than each row buffer and waits for that
+  // buffer alone.
+  auto page_of = [&](int base) { return pg[(base + slot * RB - t0) >> 4]; };
+  auto load_rows = [&](int base, uint4 (&kr)[RB]) {
+    const int tok0 = base + slot * RB;
+    const int page = max(page_of(base), 0);
+    const size_t prow = ((size_t)page * Hkv + g) * 16 + (tok0 & 15);
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+      kr[r] = *reinterpret_cast<const uint4*>(kpool + (prow + r) * D + dl * 8);
+  };
   __shared__ uint32_t sbound[GR];
+  __syncthreads();  // the tile's page ids are in LDS
+  // two row buffers: the next step's rows are in flight while this step is
+  // scored; the first step's rows are requested before the bounds are read
+  uint4 ka[RB], kb[RB];
+  load_rows(t0, ka);
   // Candidate bounds, read before the tile is scored: per row, the bin of the
   // k-th largest key counted in the row's histogram as it stands (0 while
   // fewer than k keys are counted).  Wave w takes rows w, w + 4, ...: lane l
@@ -149,21 +169,6 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   }
   __syncthreads();
 
-  // A lane group's RB rows are consecutive tokens inside one 16-token page.
-  // Every wave issues all of its row loads on every step, with no branch
-  // around them (rows of a missing page, or past the tile, are read from page
-  // 0; their scores are replaced by 0 or never kept): the compiler then knows
-  // how many loads are younger than each row buffer and waits for that
-  // buffer alone.
-  auto page_of = [&](int base) { return pg[(base + slot * RB - t0) >> 4]; };
-  auto load_rows = [&](int base, uint4 (&kr)[RB]) {
-    const int tok0 = base + slot * RB;
-    const int page = max(page_of(base), 0);
-    const size_t row0 = ((size_t)page * Hkv + g) * 16 + (tok0 & 15);
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-      kr[r] = *reinterpret_cast<const uint4*>(kpool + (row0 + r) * D + dl * 8);
-  };
   // After the group sums every lane of a row group holds all GR*RB scores of
   // its RB consecutive tokens, as GR*NQ quads of four consecutive tokens of
   // one score row.  Quad c = j*LPR + dl is kept by lane dl of the group with
@@ -211,9 +216,6 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
       }
     }
   };
-  // two row buffers: the next step's rows are in flight while this step is scored
-  uint4 ka[RB], kb[RB];
-  load_rows(t0, ka);
   int base = t0;
   for (; base + STEP < t1; base += 2 * STEP) {
     // scheduling barriers keep each step's scoring after the loads of the
@@ -391,7 +393,7 @@ struct CandStream {
 constexpr int kCandCap = 6144;
 __device__ void select_from_candidates(const CandStream& cs, int k, uint32_t b1, int need,
                                        TopkShared& sh, int32_t* __restrict__ out,
-                                       float* __restrict__ kth) {
+                                       float* __restrict__ sco, float* __restrict__ kth) {
   __shared__ uint32_t ck[kCandCap];
   __shared__ int ci[kCandCap];
   const int t = threadIdx.x;
@@ -455,11 +457,17 @@ __device__ void select_from_candidates(const CandStream& cs, int k, uint32_t b1,
   for (int e = e0; e < e1; ++e) {
     const uint32_t key = ck[e];
     if (key > ks) {
-      if (pos < k) out[pos] = ci[e];
+      if (pos < k) {
+        out[pos] = ci[e];
+        if (sco != nullptr) sco[pos] = key_to_float(key);
+      }
       ++pos;
     } else if (key == ks) {
       if (eq_rank < need) {
-        if (pos < k) out[pos] = ci[e];
+        if (pos < k) {
+          out[pos] = ci[e];
+          if (sco != nullptr) sco[pos] = key_to_float(key);
+        }
         ++pos;
       }
       ++eq_rank;
@@ -474,14 +482,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const uint32_t* __restrict__ ckey, const uint16_t* __restrict__ cidx,
     const uint32_t* __restrict__ ccnt, const uint32_t* __restrict__ hist,
     const int32_t* __restrict__ sl, int rows_per_b, int max_seq_len, int tt, int tiles,
-    int cstride, int k, int32_t* __restrict__ idx, float* __restrict__ kth) {
+    int cstride, int k, int32_t* __restrict__ idx, float* __restrict__ scores,
+    float* __restrict__ kth) {
   __shared__ TopkShared sh;
   __shared__ int seg[kMaxSelTiles + 1];
   const int row = blockIdx.x, b = row / rows_per_b;
   const int n = min(max(sl[b], 0), max_seq_len);
   const int t = threadIdx.x;
   int32_t* out = idx + (size_t)row * k;
-  if (n < k) {
+  float* sco = scores != nullptr ? scores + (size_t)row * k : nullptr;
+  if (n < k && sco == nullptr) {
     for (int x = t; x < k; x += kSelThreads) out[x] = x < n ? x : -1;
     if (kth != nullptr && t == 0) kth[row] = -INFINITY;
     return;
@@ -510,6 +520,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   __syncthreads();
   const CandStream cs{ckey + (size_t)row * cstride, cidx + (size_t)row * cstride, seg, nt, tt,
                       seg[nt]};
+  if (n < k) {
+    // every key is kept (no reading of the histogram ever counted k keys, so
+    // every tile's bound was 0): the stream holds token x at position x
+    for (int x = t; x < k; x += kSelThreads) {
+      int hint = 0, tok = -1;
+      uint32_t key = 0u;
+      if (x < n) cs.at(x, hint, key, tok);
+      out[x] = x < n ? tok : -1;
+      sco[x] = x < n ? key_to_float(key) : -INFINITY;
+    }
+    if (kth != nullptr && t == 0) kth[row] = -INFINITY;
+    return;
+  }
   // digit 1 from the row histogram (exact from the k-th key's bin up)
   for (int x = t; x < kBins1; x += kSelThreads) sh.hist[x] = hist[(size_t)row * kBins1 + x];
   __syncthreads();
@@ -519,7 +542,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int cand = above + (int)sh.hist[d];
   __syncthreads();
   if (cand <= kCandCap) {
-    select_from_candidates(cs, k, (uint32_t)d, kk, sh, out, kth ? kth + row : nullptr);
+    select_from_candidates(cs, k, (uint32_t)d, kk, sh, out, sco, kth ? kth + row : nullptr);
     return;
   }
   // general path: refine digits 2 and 3 by re-reading the candidate stream
@@ -574,11 +597,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     for (int e = 0; e < 4; ++e) {
       if (!valid[e]) continue;
       if (key[e] > kstar) {
-        if (pos < k) out[pos] = tok[e];
+        if (pos < k) {
+          out[pos] = tok[e];
+          if (sco != nullptr) sco[pos] = key_to_float(key[e]);
+        }
         ++pos;
       } else if (key[e] == kstar) {
         if (eq_rank < need_eq) {
-          if (pos < k) out[pos] = tok[e];
+          if (pos < k) {
+            out[pos] = tok[e];
+            if (sco != nullptr) sco[pos] = key_to_float(key[e]);
+          }
           ++pos;
         }
         ++eq_rank;
@@ -697,8 +726,8 @@ size_t topk_ws_bytes(const DecodeDims& d, int k) {
 }
 
 hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, const int32_t* sl,
-                       const DecodeDims& d, int k, bool pooled, int32_t* idx, float* kth, void* ws,
-                       hipStream_t st) {
+                       const DecodeDims& d, int k, bool pooled, int32_t* idx, float* scores,
+                       float* kth, void* ws, hipStream_t st) {
   const int rows_per_b = pooled ? d.Hkv : d.Hq;  // score rows (and index sets) per sequence
   const TopkLayout L = topk_layout(d, pooled);
   char* w = static_cast<char*>(ws);
@@ -734,7 +763,7 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * rows_per_b), dim3(kSelThreads), 0, st, ckey,
                      cidx, ccnt, hist, sl, rows_per_b, d.max_seq_len, L.tt, L.tiles, L.cstride, k,
-                     idx, kth);
+                     idx, scores, kth);
   return hipGetLastError();
 }
 

@@ -85,7 +85,13 @@ typedef struct {
   int32_t max_seq_len; /* upper bound of seq_lens[b], <= 16*max_pages   */
 } fsa_decode_shape;
 
-enum { FSA_SEL_ALL = 0, FSA_SEL_INDEX = 1, FSA_SEL_SEGMENT = 2, FSA_SEL_INDEX_KV = 3 };
+enum {
+  FSA_SEL_ALL = 0,
+  FSA_SEL_INDEX = 1,
+  FSA_SEL_SEGMENT = 2,
+  FSA_SEL_INDEX_KV = 3,
+  FSA_SEL_INDEX_SCORED = 4
+};
 
 /* Which cached tokens a decode query reads (host struct).
  *   FSA_SEL_ALL:     tokens [0, seq_lens[b]).
@@ -95,6 +101,12 @@ enum { FSA_SEL_ALL = 0, FSA_SEL_INDEX = 1, FSA_SEL_SEGMENT = 2, FSA_SEL_INDEX_KV
  *                    shared by its G query heads (each K/V row is read once
  *                    for the group); entries outside [0, seq_lens[b]) are
  *                    skipped.
+ *   FSA_SEL_INDEX_SCORED: idx as FSA_SEL_INDEX plus scores (device) fp32
+ *                    [B, Hq, k], the raw q . k of each listed key (as
+ *                    topk_indices_scored writes them); the keys are not read
+ *                    (k_pool may be NULL), only V at the indices.  The
+ *                    anchor layer of a Kascade group attends this way at its
+ *                    own top-k without reading K twice.
  *   FSA_SEL_SEGMENT: segments (device) int32 [B, max_seg, 2] token ranges
  *                    [start, end), n_seg (device) int32 [B]; ranges of one
  *                    sequence must be sorted and disjoint, and are clipped
@@ -110,6 +122,7 @@ typedef struct {
   const int32_t* n_seg;
   int32_t max_seg;
   int32_t n_split;
+  const float* scores; /* FSA_SEL_INDEX_SCORED only */
 } fsa_kv_select;
 
 /* ---- entry points -------------------------------------------------------- */
@@ -182,6 +195,18 @@ int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* 
 int topk_indices(fsa_dtype dt, const void* q, const void* k_pool, const int32_t* page_table,
                  const int32_t* seq_lens, const fsa_decode_shape* s, int k, int32_t* idx,
                  float* kth, void* ws, size_t ws_bytes, hipStream_t st);
+
+/* topk_indices_scored -- topk_indices that also returns each kept key's
+ * score: scores (device) fp32 [B, Hq, k], scores[b,h,x] = the raw fp32
+ * q . k of token idx[b,h,x] as the scan computed it (-inf for the -1 slots
+ * of a sequence shorter than k).  Kascade post, "What Kascade got right": the
+ * anchor layer scores every key to pick its top-k, so its own attention at
+ * those keys needs only their values (FSA_SEL_INDEX_SCORED).  Other
+ * arguments and errors as topk_indices; scores must not be NULL. */
+int topk_indices_scored(fsa_dtype dt, const void* q, const void* k_pool,
+                        const int32_t* page_table, const int32_t* seq_lens,
+                        const fsa_decode_shape* s, int k, int32_t* idx, float* scores,
+                        float* kth, void* ws, size_t ws_bytes, hipStream_t st);
 
 /* topk_indices_kv -- exact top-k per KV head over a pooled score, the
  * GQA-shared counterpart of topk_indices.  Kascade post, "Head-aware is the

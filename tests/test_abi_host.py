@@ -319,3 +319,24 @@ def test_topk_union_kv_validation():
     assert call(0, 8, 2, 16) == L.FSA_ERR_SHAPE
     assert call(2, 8, 2, 0) == L.FSA_ERR_ARG
     assert call(2, 16, 1, 1025) == L.FSA_ERR_ARG     # 16 x 1025 entries: beyond the sort
+
+
+def test_scored_mode_validation():
+    """FSA_SEL_INDEX_SCORED needs idx and scores; the key pool may be NULL
+    there (keys are not read) but nowhere else."""
+    L, lib = _lib()
+    s = _dshape(L)
+    call = lambda sel, kp=FAKE: lib.sparse_decode_attn(
+        L.FSA_BF16, FAKE, kp, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(sel), 0.1, FAKE,
+        None, FAKE, 1 << 30, None)
+    sel = L.KvSelect(L.FSA_SEL_INDEX_SCORED, FAKE.value, 16, None, None, 0, 0, None)
+    assert call(sel) == L.FSA_ERR_NULL                       # no scores
+    sel = L.KvSelect(L.FSA_SEL_INDEX_SCORED, FAKE.value, 16, None, None, 0, 0, FAKE.value)
+    assert call(sel, kp=None) == L.FSA_ERR_NO_DEVICE         # valid: reaches the device check
+    sel = L.KvSelect(L.FSA_SEL_INDEX, FAKE.value, 16, None, None, 0, 0, FAKE.value)
+    assert call(sel, kp=None) == L.FSA_ERR_NULL              # other modes read the keys
+    assert lib.fsa_workspace_size(L.FSA_OP_DECODE_ATTN, ctypes.byref(s), ctypes.byref(
+        L.KvSelect(L.FSA_SEL_INDEX_SCORED, None, 16, None, None, 0, 2, None))) == 2 * 8 * 2 * 130 * 4
+    k = 16
+    assert lib.topk_indices_scored(L.FSA_BF16, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), k, FAKE,
+                                   None, None, FAKE, 1 << 30, None) == L.FSA_ERR_NULL

@@ -551,3 +551,47 @@ def test_shared_set_accuracy_harness_matches_oracle():
                 worst = max(worst, abs(kept[key][b, h] - ref))
     print(f"[shared-set harness] mass kept max-abs difference GPU vs oracle {worst:.2e}")
     assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_topk_scores_and_scored_anchor_decode(name):
+    """topk_indices_scored returns the same index sets as topk_indices and, for
+    each kept key, its score (against the oracle's anchor scores; -inf in
+    the empty slots of a short sequence); the anchor layer's attention at
+    its own top-k from those scores, reading V only, equals index decode of
+    the same layer bit for bit (the scores are the decode kernel's own dot
+    products) and the oracle's attention at those indices."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, sl, k = SHAPES[name]
+    d, gpu = inputs(name)
+    L0 = gpu["layers"][0]
+    pt, sls = gpu["page_table"], gpu["seq_lens"]
+    idx_ref, kth_ref = fsa.topk_indices(L0["q"], L0["k"], pt, sls, k, max_seq_len=N)
+    idx, sco, kth = fsa.topk_indices_scored(L0["q"], L0["k"], pt, sls, k, max_seq_len=N)
+    assert torch.equal(idx, idx_ref) and torch.equal(kth, kth_ref)
+    args = (L0["q"], L0["k"], L0["v"], pt, sls)
+    o_i, l_i = fsa.sparse_decode_attn(*args, mode=fsa.SEL_INDEX, idx=idx, max_seq_len=N)
+    for ns in (0, 3):
+        o_s, l_s = fsa.sparse_decode_attn(*args, mode=fsa.SEL_INDEX_SCORED, idx=idx, scores=sco,
+                                          n_split=ns, max_seq_len=N)
+        if ns == 0:
+            assert torch.equal(o_s, o_i) and torch.equal(l_s, l_i)
+    # keys are not read in scored mode: a pool of zeros in their place changes nothing
+    o_z, l_z = fsa.sparse_decode_attn(L0["q"], torch.zeros_like(L0["k"]), L0["v"], pt, sls,
+                                      mode=fsa.SEL_INDEX_SCORED, idx=idx, scores=sco, max_seq_len=N)
+    assert torch.equal(o_z, o_i) and torch.equal(l_z, l_i)
+    idx, sco, o_i, l_i = idx.cpu().numpy(), sco.cpu().numpy(), o_i.cpu(), l_i.cpu()
+    q = workloads.to_f64(d["layers"][0]["q"])
+    scale = 1 / math.sqrt(D)
+    for b in range(B):
+        n = sl[b]
+        for h in range(Hq):
+            K, V = seq_kv(d, 0, b, oracle.kv_head(h, Hq, Hkv))
+            s = oracle.anchor_scores(q[b, h], K)
+            valid = idx[b, h] >= 0
+            assert np.abs(sco[b, h][valid] - s[idx[b, h][valid]]).max() <= 1e-3
+            assert np.isneginf(sco[b, h][~valid]).all()
+            assert valid.sum() == min(n, k)
+            o, l = oracle.index_attention(q[b, h], K, V, idx[b, h], scale)
+            assert np.abs(o_i[b, h].double().numpy() - o).max() <= TOL_BF16
+            assert abs(l_i[b, h].item() - l) <= 1e-2
