@@ -485,7 +485,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     int cstride, int k, int32_t* __restrict__ idx, float* __restrict__ scores,
     float* __restrict__ kth) {
   __shared__ TopkShared sh;
-  __shared__ int seg[kMaxSelTiles + 1];
+  // tile offsets of the candidate stream: tiles + 1 entries, sized at launch
+  // (a static array for the longest supported row would take 32 KB of LDS
+  // and halve the workgroups a CU holds)
+  extern __shared__ int seg[];
   const int row = blockIdx.x, b = row / rows_per_b;
   const int n = min(max(sl[b], 0), max_seq_len);
   const int t = threadIdx.x;
@@ -761,7 +764,8 @@ hipError_t launch_topk(const void* q, const void* kpool, const int32_t* pt, cons
 #undef FSA_TS
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * rows_per_b), dim3(kSelThreads), 0, st, ckey,
+  hipLaunchKernelGGL(topk_select_kernel, dim3(d.B * rows_per_b), dim3(kSelThreads),
+                     (L.tiles + 1) * sizeof(int), st, ckey,
                      cidx, ccnt, hist, sl, rows_per_b, d.max_seq_len, L.tt, L.tiles, L.cstride, k,
                      idx, scores, kth);
   return hipGetLastError();
