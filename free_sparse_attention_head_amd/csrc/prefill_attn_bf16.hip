@@ -7,7 +7,7 @@
 // One workgroup per (batch, query head, query block i): T/32 waves of 32
 // query rows.  The workgroup walks the row's causal key blocks in 64-key
 // chunks through two LDS buffers:
-//   * K and V chunks are copied HBM -> LDS with global_load_lds_dwordx4
+//   * K and V chunks are copied HBM -> LDS with buffer_load_dwordx4 ... lds
 //     (each wave instruction lands 64 lanes x 16 B contiguously): no staging
 //     registers, no LDS store instructions, no transposes.  The next chunk's
 //     copies are issued before the current chunk is computed;
@@ -71,6 +71,13 @@ __device__ __forceinline__ int v_swz(int row) {
 template <typename T>
 __device__ __forceinline__ FSA_LDS T* lds_ptr(const void* p) {
   return (FSA_LDS T*)(const_cast<void*>(p));
+}
+
+// 16 bytes a lane, HBM -> LDS, through a buffer descriptor (MUBUF form).  A
+// non-template function: the host pass then still instantiates the kernels.
+__device__ __forceinline__ void copy16_to_lds_buf(__amdgpu_buffer_rsrc_t rs, const void* l, uint32_t voff,
+                                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr<void>(l), 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ void copy16_to_lds(const void* g, const void* l) {
@@ -188,32 +195,44 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   for (int kk = 0; kk < D / 16; ++kk) qf[kk] = kfrag(stage + lq * ROWB, kk);
   __syncthreads();
 
-  // HBM -> LDS copy of chunk c into tile buffer kt: a wave-uniform source
-  // base plus fixed per-lane byte offsets (row, swizzled slot) and a
-  // wave-uniform LDS base per instruction
-  uint32_t kofs[Tr::IPW], vofs[Tr::IPW];
-#pragma unroll
-  for (int m = 0; m < Tr::IPW; ++m) {
-    const int r = (wave * Tr::IPW + m) * Tr::RPI + l / SLOTS;
+  // HBM -> LDS copy of chunk c into tile buffer kt.  Instruction m of a wave
+  // lands rows (wave*IPW + m)*RPI + l/SLOTS of the chunk: the row step of m
+  // is a wave-uniform byte offset (the instruction's SGPR offset), and the
+  // per-lane part (row l/SLOTS, swizzled slot) is one register for V and one
+  // for K, whose slot swizzle changes with m by a constant XOR of the slot
+  // bits (a row starts on a multiple of the key stride, itself a multiple
+  // of the row size, so the slot bits of the offset are free).
+  static_assert((Tr::IPW * Tr::RPI) % SLOTS == 0, "copy rows per wave");
+  const uint32_t stride_b = (uint32_t)(kv_stride * sizeof(uint16_t));  // token to token
+  uint32_t kofs0, vofs0;
+  {
+    const int r = wave * Tr::IPW * Tr::RPI + l / SLOTS;
     const int sl = l % SLOTS;
-    kofs[m] = (uint32_t)((r * kv_stride + (sl ^ k_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
-    vofs[m] = (uint32_t)((r * kv_stride + (sl ^ v_swz<SLOTS>(r)) * 8) * sizeof(uint16_t));
+    kofs0 = (uint32_t)r * stride_b + (uint32_t)((sl ^ k_swz<SLOTS>(r)) * 16);
+    vofs0 = (uint32_t)r * stride_b + (uint32_t)((sl ^ v_swz<SLOTS>(r)) * 16);
   }
+  // The copies are MUBUF loads to LDS through a buffer descriptor of the
+  // chunk (base in SGPRs, range = the chunk's rows).  Unlike the FLAT form,
+  // the compiler's wait-count model then keeps exact LDS counts for the
+  // fragment reads issued while these copies are in flight.
+  const uint32_t chunk_bytes = (uint32_t)KC * stride_b;
   // (j = key block of chunk c, read from the list one step ahead)
-  auto issue_tile = [&](int c, int j, const uint16_t* src0, const uint32_t (&ofs)[Tr::IPW],
-                        unsigned char* tile) {
+  auto issue_tile = [&](int c, int j, const uint16_t* src0, bool is_k, unsigned char* tile) {
     j = __builtin_amdgcn_readfirstlane(j);
-    const size_t base = ((size_t)j * BLK + (c % NCH) * KC) * kv_stride * sizeof(uint16_t);
+    const size_t base = ((size_t)j * BLK + (c % NCH) * KC) * stride_b;
     const char* src = reinterpret_cast<const char*>(src0) + base;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, (int)chunk_bytes, 0x00020000);
 #pragma unroll
     for (int m = 0; m < Tr::IPW; ++m) {
-      uint32_t o = ofs[m];
-      asm volatile("" : "+v"(o));
-      copy16_to_lds(src + o, tile + (wave * Tr::IPW + m) * 1024);
+      // K: the slot swizzle of row r is r % SLOTS, and r moves by m*RPI
+      const uint32_t kx = (uint32_t)(((m * Tr::RPI) & (SLOTS - 1)) * 16);
+      copy16_to_lds_buf(rs, tile + (wave * Tr::IPW + m) * 1024, is_k ? (kofs0 ^ kx) : vofs0,
+                        (uint32_t)(m * Tr::RPI) * stride_b);
     }
   };
-  auto issue_k = [&](int c, int j, unsigned char* kt) { issue_tile(c, j, Kb, kofs, kt); };
-  auto issue_v = [&](int c, int j, unsigned char* vt) { issue_tile(c, j, Vb, vofs, vt); };
+  auto issue_k = [&](int c, int j, unsigned char* kt) { issue_tile(c, j, Kb, true, kt); };
+  auto issue_v = [&](int c, int j, unsigned char* vt) { issue_tile(c, j, Vb, false, vt); };
 
   // Pipeline barrier: this wave's tile copies have landed and its LDS reads
   // have retired; the s_barrier then publishes every wave's copies and frees
@@ -229,6 +248,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  float l_part[2] = {0.f, 0.f};  // row-sum partials of the chunks since the last rescale
 
   // per-lane LDS offsets of the fragment reads
   const int li = l & 15, q16 = (l >> 4) & 1;  // transposing-read lane coordinates
@@ -265,7 +285,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
       const float m_new = grow ? mx : m_run;
       const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
       m_run = m_new;
-      l_run *= alpha;
+      l_run = (l_run + l_part[0] + l_part[1]) * alpha;
+      l_part[0] = l_part[1] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -275,8 +296,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   };
 
   // One sixteenth of the softmax of a chunk: P elements 2q and 2q+1 of the
-  // lane's 32 (bf16, packed into pp[q]) and their share of the row sum.
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  // lane's 32 (bf16, packed into pp[q]) and their share of the row sum.  The
+  // row sum adds the fp32 values in two partial sums with plain adds:
+  // v_dot2 does not issue while an MFMA is in flight, plain VALU does.
   auto p_slice = [&](const floatx16 (&s)[NKT], float mc, uint32_t (&pp)[NP], int q) {
     const int e0 = 2 * q;  // element index kc*8 + e of P
     const float x0 = s[e0 >> 4][e0 & 15], x1 = s[(e0 + 1) >> 4][(e0 + 1) & 15];
@@ -286,35 +308,40 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     pb[0] = (__bf16)p0;
     pb[1] = (__bf16)p1;
     pp[q] = __builtin_bit_cast(uint32_t, pb);
-    // row sum of the bf16-rounded P that the PV step multiplies
-    l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_run, false);
+    l_part[q & 1] += p0 + p1;
   };
 
   // S^T = K Q^T of the next chunk from K tile kS into sn (NKT 32x32 tiles:
   // keys 0-31, 32-63), interleaved with the softmax of the current chunk (sc,
   // mc -> pp): after each S MFMA 8 / NKK P slices.  K fragments of step kk+1
   // are read before the MFMAs of step kk.  Either half may be absent.
+  // K fragments are read KRD k-steps ahead through a ring; the first KRD
+  // steps' fragments are read by the caller (before the prelude).
+  constexpr int KRD = 2;
+  auto k_first = [&](const unsigned char* kS, bf16x8 (&ring)[KRD][NKT]) {
+    const unsigned char* kr0 = kS + lq * ROWB;
+#pragma unroll
+    for (int kk = 0; kk < KRD; ++kk)
+#pragma unroll
+      for (int tl = 0; tl < NKT; ++tl) ring[kk][tl] = kfrag(kr0 + tl * 32 * ROWB, kk);
+  };
   auto s_and_p = [&](auto has_s, auto has_p, const unsigned char* kS, floatx16 (&sn)[NKT],
-                     const floatx16 (&sc)[NKT], float mc, uint32_t (&pp)[NP]) {
+                     const floatx16 (&sc)[NKT], float mc, uint32_t (&pp)[NP],
+                     bf16x8 (&ring)[KRD][NKT]) {
     constexpr bool DO_S = decltype(has_s)::value, DO_P = decltype(has_p)::value;
     constexpr int SPM = 8 / NKK;  // P slices after each S MFMA (NKT * 8 slices in all)
     static_assert(SPM * NKK == 8, "head dimension");
     const unsigned char* kr0 = kS + lq * ROWB;
     const floatx16 zero = {};
-    bf16x8 a[NKT];
-    if constexpr (DO_S) {
-#pragma unroll
-      for (int tl = 0; tl < NKT; ++tl) a[tl] = kfrag(kr0 + tl * 32 * ROWB, 0);
-    }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      bf16x8 nx[NKT];
+      bf16x8 a[NKT];
 #pragma unroll
-      for (int tl = 0; tl < NKT; ++tl) nx[tl] = a[tl];
+      for (int tl = 0; tl < NKT; ++tl) a[tl] = ring[kk % KRD][tl];
       if constexpr (DO_S) {
-        if (kk + 1 < NKK) {
+        if (kk + KRD < NKK) {
 #pragma unroll
-          for (int tl = 0; tl < NKT; ++tl) nx[tl] = kfrag(kr0 + tl * 32 * ROWB, kk + 1);
+          for (int tl = 0; tl < NKT; ++tl) ring[kk % KRD][tl] = kfrag(kr0 + tl * 32 * ROWB, kk + KRD);
         }
       }
 #pragma unroll
@@ -325,8 +352,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
 #pragma unroll
           for (int q = 0; q < SPM; ++q) p_slice(sc, mc, pp, (NKT * kk + tl) * SPM + q);
       }
-#pragma unroll
-      for (int tl = 0; tl < NKT; ++tl) a[tl] = nx[tl];
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -387,6 +412,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     jq0 = jq1;
     jq1 = jq2;
     jq2 = block_of(c + 3);
+    bf16x8 ring[KRD][NKT];
+    if constexpr (decltype(has_next)::value) k_first(kS, ring);
     const float mc = prelude(c, jc, sc);
     uint32_t pp[NP];
     // Two waves share each SIMD.  While one is in its S + softmax phase
@@ -394,7 +421,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     // the other's PV phase, back-to-back MFMAs, keeps the matrix core busy
     // meanwhile.
     __builtin_amdgcn_s_setprio(1);
-    s_and_p(has_next, std::true_type{}, kS, sn, sc, mc, pp);
+    s_and_p(has_next, std::true_type{}, kS, sn, sc, mc, pp, ring);
     __builtin_amdgcn_s_setprio(0);
     pv(pp, vP);
   };
@@ -409,7 +436,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     issue_v(0, jq0, vb0);
     if (n > 1) issue_k(1, jq1, kb1);
     tile_barrier();
-    s_and_p(std::true_type{}, std::false_type{}, kb0, sA, sB, 0.f, pp0);
+    {
+      bf16x8 ring[KRD][NKT];
+      k_first(kb0, ring);
+      s_and_p(std::true_type{}, std::false_type{}, kb0, sA, sB, 0.f, pp0, ring);
+    }
     int c = 0;
     for (; c + 2 < n; c += 2) {
       step(std::true_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
@@ -427,6 +458,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // wave has passed its barrier, so the staging regions are free again: the
   // wave writes its rows there (lane: 4 values of row lq at d0) and stores
   // them back as whole rows.
+  l_run += l_part[0] + l_part[1];
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int t = i * BLK + qrow;
