@@ -253,12 +253,20 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   }
   // Each row's candidates of this tile, compacted in index order.
   if constexpr (GR >= 4) {
-    // a wave per row, no workgroup barrier: lane l reads quads l, l + 64, ...
-    // (consecutive 16-byte LDS reads), one wave scan per 64 quads
+    // A wave per row: lane l reads quads l, l + 64, ... (consecutive 16-byte
+    // LDS reads), one wave scan per 64 quads.  The candidates are compacted
+    // in LDS first (keys in place over the row's scores: a candidate's place
+    // never passes the quads still to be read; token offsets over the row's
+    // histogram words, flushed above), then copied out with coalesced
+    // stores; a lane's own candidates are consecutive, so stores straight
+    // from the scan would touch every fourth element.
+    static_assert(GR * TT <= 2 * HW, "token offsets fit over the histogram words");
+    __syncthreads();  // every row's histogram words are flushed
 #pragma unroll 1
     for (int x = wave; x < GR; x += 4) {
       const uint32_t bound = sbound[x];
-      const size_t cbase = (row0 + x) * (size_t)cstride + t0;
+      uint32_t* kst = reinterpret_cast<uint32_t*>(&ssc[x * TT]);
+      uint16_t* ist = reinterpret_cast<uint16_t*>(lh) + x * TT;
       int done = 0;
 #pragma unroll
       for (int it = 0; it < TT / 256; ++it) {
@@ -276,12 +284,17 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (j + u < nt && (key[u] >> 21) >= bound) {
-            ckey[cbase + pos] = key[u];
-            cidx[cbase + pos] = (uint16_t)(j + u);
+            kst[pos] = key[u];
+            ist[pos] = (uint16_t)(j + u);
             ++pos;
           }
         }
         done += __shfl(inc, 63, 64);
+      }
+      const size_t cbase = (row0 + x) * (size_t)cstride + t0;
+      for (int e = l; e < done; e += 64) {
+        ckey[cbase + e] = kst[e];
+        cidx[cbase + e] = ist[e];
       }
       if (l == 0) ccnt[(row0 + x) * tiles + tile] = (uint32_t)done;
     }
