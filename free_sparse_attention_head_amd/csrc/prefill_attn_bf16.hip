@@ -80,6 +80,8 @@ __device__ __forceinline__ void copy16_to_lds_buf(__amdgpu_buffer_rsrc_t rs, con
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr<void>(l), 16, voff, soff, 0, 0);
 }
 
+// 16 bytes a lane, HBM -> LDS (FLAT form): the Q rows of the prologue, which
+// are waited for in full before the chunk loop starts.
 __device__ __forceinline__ void copy16_to_lds(const void* g, const void* l) {
   __builtin_amdgcn_global_load_lds(g, lds_ptr<void>(l), 16, 0, 0);
 }
@@ -313,10 +315,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
 
   // S^T = K Q^T of the next chunk from K tile kS into sn (NKT 32x32 tiles:
   // keys 0-31, 32-63), interleaved with the softmax of the current chunk (sc,
-  // mc -> pp): after each S MFMA 8 / NKK P slices.  K fragments of step kk+1
-  // are read before the MFMAs of step kk.  Either half may be absent.
-  // K fragments are read KRD k-steps ahead through a ring; the first KRD
-  // steps' fragments are read by the caller (before the prelude).
+  // mc -> pp): after each S MFMA 8 / NKK P slices.  Either half may be
+  // absent.  K fragments are read KRD k-steps ahead through a ring; the
+  // first KRD steps' fragments are read by the caller, before the prelude.
   constexpr int KRD = 2;
   auto k_first = [&](const unsigned char* kS, bf16x8 (&ring)[KRD][NKT]) {
     const unsigned char* kr0 = kS + lq * ROWB;
