@@ -337,9 +337,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 a[NKT];
-#pragma unroll
-      for (int tl = 0; tl < NKT; ++tl) a[tl] = ring[kk % KRD][tl];
       if constexpr (DO_S) {
+#pragma unroll
+        for (int tl = 0; tl < NKT; ++tl) a[tl] = ring[kk % KRD][tl];
         if (kk + KRD < NKK) {
 #pragma unroll
           for (int tl = 0; tl < NKT; ++tl) ring[kk % KRD][tl] = kfrag(kr0 + tl * 32 * ROWB, kk + KRD);
