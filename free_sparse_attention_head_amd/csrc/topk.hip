@@ -385,7 +385,8 @@ struct CandStream {
     k = key[o];
     tok = lo * tt + (int)idx[o];
   }
-  // this thread's four consecutive elements from p0 (invalid past the end)
+  // this thread's four consecutive elements from p0 (invalid past the end).
+  // They nearly always lie in one tile's list: one search then finds all four.
   __device__ void quad(int p0, uint32_t (&k)[4], int (&tok)[4], bool (&valid)[4]) const {
     int hint = 0;
 #pragma unroll
@@ -393,8 +394,25 @@ struct CandStream {
       valid[e] = p0 + e < m;
       k[e] = 0u;
       tok[e] = -1;
-      if (valid[e]) at(p0 + e, hint, k[e], tok[e]);
     }
+    if (!valid[0]) return;
+    uint32_t k0;
+    int t0;
+    at(p0, hint, k0, t0);
+    if (p0 + 3 < m && p0 + 3 < seg[hint + 1]) {
+      const int o = hint * tt + (p0 - seg[hint]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k[e] = key[o + e];
+        tok[e] = hint * tt + (int)idx[o + e];
+      }
+      return;
+    }
+    k[0] = k0;
+    tok[0] = t0;
+#pragma unroll
+    for (int e = 1; e < 4; ++e)
+      if (valid[e]) at(p0 + e, hint, k[e], tok[e]);
   }
 };
 
