@@ -32,8 +32,9 @@
 //      candidates sharing the prefix by re-reading the stream.  This yields
 //      the exact k-th key K* and how many keys equal to K* are taken.  A
 //      final pass in index order keeps key > K*, plus the first keys equal to
-//      K*, compacting positions with workgroup scans so that the output is
-//      ascending.
+//      K*, ranking positions with wave ballots and one workgroup scan per
+//      pass so that the output is ascending.  Each load instruction of a
+//      pass reads 64 consecutive list entries.
 #include <limits.h>
 #include <math.h>
 
@@ -385,34 +386,37 @@ struct CandStream {
     k = key[o];
     tok = lo * tt + (int)idx[o];
   }
-  // this thread's four consecutive elements from p0 (invalid past the end).
-  // They nearly always lie in one tile's list: one search then finds all four.
-  __device__ void quad(int p0, uint32_t (&k)[4], int (&tok)[4], bool (&valid)[4]) const {
-    int hint = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      valid[e] = p0 + e < m;
-      k[e] = 0u;
-      tok[e] = -1;
-    }
-    if (!valid[0]) return;
-    uint32_t k0;
-    int t0;
-    at(p0, hint, k0, t0);
-    if (p0 + 3 < m && p0 + 3 < seg[hint + 1]) {
-      const int o = hint * tt + (p0 - seg[hint]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k[e] = key[o + e];
-        tok[e] = hint * tt + (int)idx[o + e];
+  // elements p0, p0 + 64, ..., p0 + 64 (N - 1) (invalid past the end): one
+  // tile search for the first, then a walk over the tile ends that the rest
+  // cross (lists may be empty), so that all 2N loads are in flight together.
+  // The 64 lanes of a wave take 64 consecutive positions, so each load
+  // instruction reads consecutive list entries.
+  template <int N>
+  __device__ void strided(int p0, uint32_t (&k)[N], int (&tok)[N], bool (&valid)[N]) const {
+    int tile = 0;
+    if (p0 < m) {
+      int lo = 0, hi = nt - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg[mid] <= p0) lo = mid; else hi = mid - 1;
       }
-      return;
+      tile = lo;
     }
-    k[0] = k0;
-    tok[0] = t0;
+    int start = seg[tile], next = seg[tile + 1];
 #pragma unroll
-    for (int e = 1; e < 4; ++e)
-      if (valid[e]) at(p0 + e, hint, k[e], tok[e]);
+    for (int e = 0; e < N; ++e) {
+      const int p = p0 + 64 * e;
+      valid[e] = p < m;
+      // p < m = seg[nt], so the walk stops at a tile <= nt - 1
+      while (valid[e] && p >= next) {
+        ++tile;
+        start = next;
+        next = seg[tile + 1];
+      }
+      const int o = tile * tt + (p - start);
+      k[e] = valid[e] ? key[o] : 0u;
+      tok[e] = valid[e] ? tile * tt + (int)idx[o] : -1;
+    }
   }
 };
 
@@ -422,32 +426,40 @@ struct CandStream {
 // then run on LDS only.  `need` = how many keys of bin b1 still have to be
 // taken.
 constexpr int kCandCap = 6144;
+constexpr int kSelPer = 8;  // stream elements a thread takes per pass
 __device__ void select_from_candidates(const CandStream& cs, int k, uint32_t b1, int need,
                                        TopkShared& sh, int32_t* __restrict__ out,
                                        float* __restrict__ sco, float* __restrict__ kth) {
   __shared__ uint32_t ck[kCandCap];
   __shared__ int ci[kCandCap];
   const int t = threadIdx.x;
+  // A pass covers kSelPer * kSelThreads stream positions: wave w the
+  // kSelPer * 64 from base + w * kSelPer * 64, lane l every 64th of them
+  // from l.  Ranks inside the wave come from ballots (element e of every
+  // lane precedes element e + 1 of any), the waves' offsets from one scan.
+  const int lane = t & 63, wave = t >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
   int ncand = 0;
-  for (int base = 0; base < cs.m; base += 4 * kSelThreads) {
-    uint32_t key[4];
-    int tok[4];
-    bool f[4];
-    cs.quad(base + 4 * t, key, tok, f);
-    int c = 0;
+  for (int base = 0; base < cs.m; base += kSelPer * kSelThreads) {
+    uint32_t key[kSelPer];
+    int tok[kSelPer];
+    bool f[kSelPer];
+    cs.strided(base + wave * kSelPer * 64 + lane, key, tok, f);
+    int rank[kSelPer], wtot = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kSelPer; ++e) {
       f[e] = f[e] && (key[e] >> 21) >= b1;
-      c += f[e] ? 1 : 0;
+      const uint64_t mk = __ballot(f[e]);
+      rank[e] = wtot + __popcll(mk & below);
+      wtot += __popcll(mk);
     }
     int tot;
-    int pos = ncand + block_excl_scan(c, sh.scan, &tot);
+    const int wo = __shfl(block_excl_scan(lane == 0 ? wtot : 0, sh.scan, &tot), 0, 64);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < kSelPer; ++e)
       if (f[e]) {
-        ck[pos] = key[e];
-        ci[pos] = tok[e];
-        ++pos;
+        ck[ncand + wo + rank[e]] = key[e];
+        ci[ncand + wo + rank[e]] = tok[e];
       }
     ncand += tot;
   }
@@ -508,8 +520,12 @@ __device__ void select_from_candidates(const CandStream& cs, int k, uint32_t b1,
 }
 
 // One workgroup per score row; rows_per_b rows (query heads, or KV heads when
-// pooled) per sequence.
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+// pooled) per sequence.  A row's select is a chain of latencies, so rows in
+// flight set the pace: two 1024-thread workgroups share a CU only while a
+// wave holds at most 64 VGPRs and about 72 SGPRs (with 78 SGPRs, or 71
+// VGPRs, a CU ran one), hence the register caps (surplus SGPRs go to VGPR
+// lanes).
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_num_sgpr(72), amdgpu_num_vgpr(64))) void topk_select_kernel(
     const uint32_t* __restrict__ ckey, const uint16_t* __restrict__ cidx,
     const uint32_t* __restrict__ ccnt, const uint32_t* __restrict__ hist,
     const int32_t* __restrict__ sl, int rows_per_b, int max_seq_len, int tt, int tiles,
@@ -521,8 +537,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   // and halve the workgroups a CU holds)
   extern __shared__ int seg[];
   const int row = blockIdx.x, b = row / rows_per_b;
-  const int n = min(max(sl[b], 0), max_seq_len);
   const int t = threadIdx.x;
+  // The sequence length, the tiles' list lengths and the row histogram are
+  // read together (one round trip); lengths of tiles past the sequence's end
+  // are dropped once its length is known.
+  constexpr int TPT = kMaxSelTiles / kSelThreads;  // tiles per thread, consecutive
+  constexpr int HPT = kBins1 / kSelThreads;        // histogram bins per thread
+  static_assert(kMaxSelTiles % kSelThreads == 0 && kBins1 % kSelThreads == 0, "per-thread shares");
+  const int n_in = sl[b];
+  int c[TPT];
+#pragma unroll
+  for (int e = 0; e < TPT; ++e) {
+    const int i = t * TPT + e;
+    c[e] = i < tiles ? (int)ccnt[(size_t)row * tiles + i] : 0;
+  }
+  uint32_t hv[HPT];
+#pragma unroll
+  for (int x = 0; x < HPT; ++x) hv[x] = hist[(size_t)row * kBins1 + x * kSelThreads + t];
+  const int n = min(max(n_in, 0), max_seq_len);
   int32_t* out = idx + (size_t)row * k;
   float* sco = scores != nullptr ? scores + (size_t)row * k : nullptr;
   if (n < k && sco == nullptr) {
@@ -533,12 +565,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   // the candidate stream: exclusive prefix of the tiles' list lengths
   const int nt = (n + tt - 1) / tt;
   {
-    constexpr int TPT = kMaxSelTiles / kSelThreads;  // tiles per thread, consecutive
-    int c[TPT], sum = 0;
+    int sum = 0;
 #pragma unroll
     for (int e = 0; e < TPT; ++e) {
-      const int i = t * TPT + e;
-      c[e] = i < nt ? (int)ccnt[(size_t)row * tiles + i] : 0;
+      c[e] = t * TPT + e < nt ? c[e] : 0;
       sum += c[e];
     }
     int tot;
@@ -568,7 +598,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     return;
   }
   // digit 1 from the row histogram (exact from the k-th key's bin up)
-  for (int x = t; x < kBins1; x += kSelThreads) sh.hist[x] = hist[(size_t)row * kBins1 + x];
+#pragma unroll
+  for (int x = 0; x < HPT; ++x) sh.hist[x * kSelThreads + t] = hv[x];
   __syncthreads();
   int kk = k, d, above;
   find_digit(sh, kBins1, kk, d, above);
@@ -587,13 +618,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     for (int x = t; x < nbins[pass]; x += kSelThreads) sh.hist[x] = 0u;
     __syncthreads();
     const uint32_t dmask = (uint32_t)nbins[pass] - 1u;
-    for (int p0 = 4 * t; p0 < cs.m; p0 += 4 * kSelThreads) {
-      uint32_t key[4];
-      int tok[4];
-      bool valid[4];
-      cs.quad(p0, key, tok, valid);
+    for (int base = 0; base < cs.m; base += kSelPer * kSelThreads) {
+      uint32_t key[kSelPer];
+      int tok[kSelPer];
+      bool valid[kSelPer];
+      cs.strided(base + (t >> 6) * kSelPer * 64 + (t & 63), key, tok, valid);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < kSelPer; ++e)
         if (valid[e] && (key[e] & pmask) == prefix)
           atomicAdd(&sh.hist[(key[e] >> shifts[pass]) & dmask], 1u);
     }
@@ -605,51 +636,45 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   const uint32_t kstar = prefix;
   const int need_eq = kk;
-  // output pass in index order: keep key > K*, and the first need_eq keys == K*
-  int eq_before = 0, out_before = 0;
-  for (int base = 0; base < cs.m; base += 4 * kSelThreads) {
-    uint32_t key[4];
-    int tok[4];
-    bool valid[4];
-    cs.quad(base + 4 * t, key, tok, valid);
-    int neq = 0, ngt = 0;
+  // output pass in index order: keep key > K*, and the first need_eq keys
+  // == K*.  An element's output place is the greater keys before it plus
+  // min(equal keys before it, need_eq); positions are laid out as in the
+  // fast path's pass, ranks from ballots and one scan per pass.
+  const int lane = t & 63, wave = t >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int gt_before = 0, eq_before = 0;
+  for (int base = 0; base < cs.m; base += kSelPer * kSelThreads) {
+    uint32_t key[kSelPer];
+    int tok[kSelPer];
+    bool valid[kSelPer];
+    cs.strided(base + wave * kSelPer * 64 + lane, key, tok, valid);
+    int gr[kSelPer], er[kSelPer], wgt = 0, weq = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      neq += (valid[e] && key[e] == kstar) ? 1 : 0;
-      ngt += (valid[e] && key[e] > kstar) ? 1 : 0;
+    for (int e = 0; e < kSelPer; ++e) {
+      const uint64_t mg = __ballot(valid[e] && key[e] > kstar);
+      const uint64_t me = __ballot(valid[e] && key[e] == kstar);
+      gr[e] = wgt + __popcll(mg & below);
+      er[e] = weq + __popcll(me & below);
+      wgt += __popcll(mg);
+      weq += __popcll(me);
     }
-    // one scan carries both counts: equal keys in the high half
+    // one scan carries both counts (at most 16384 each): equal keys high
     int tot;
-    const int ex = block_excl_scan((neq << 16) | ngt, sh.scan, &tot);
-    int eq_rank = eq_before + (ex >> 16);
-    int gt_rank = ex & 0xffff;
-    // output position = keys kept before this thread's first element: all of
-    // out_before, this iteration's greater keys before it, and the equal keys
-    // before it that still fit under need_eq
-    int pos = out_before + gt_rank + min(eq_rank, need_eq) - min(eq_before, need_eq);
+    const int ex = __shfl(block_excl_scan(lane == 0 ? ((weq << 16) | wgt) : 0, sh.scan, &tot), 0, 64);
+    const int g0 = gt_before + (ex & 0xffff), e0 = eq_before + (ex >> 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kSelPer; ++e) {
       if (!valid[e]) continue;
-      if (key[e] > kstar) {
-        if (pos < k) {
-          out[pos] = tok[e];
-          if (sco != nullptr) sco[pos] = key_to_float(key[e]);
-        }
-        ++pos;
-      } else if (key[e] == kstar) {
-        if (eq_rank < need_eq) {
-          if (pos < k) {
-            out[pos] = tok[e];
-            if (sco != nullptr) sco[pos] = key_to_float(key[e]);
-          }
-          ++pos;
-        }
-        ++eq_rank;
+      const int gb = g0 + gr[e], eb = e0 + er[e];
+      const bool keep = key[e] > kstar || (key[e] == kstar && eb < need_eq);
+      const int pos = gb + min(eb, need_eq);
+      if (keep && pos < k) {
+        out[pos] = tok[e];
+        if (sco != nullptr) sco[pos] = key_to_float(key[e]);
       }
     }
-    const int teq = tot >> 16, tgt = tot & 0xffff;
-    out_before += tgt + max(0, min(teq, need_eq - eq_before));
-    eq_before += teq;
+    gt_before += tot & 0xffff;
+    eq_before += tot >> 16;
   }
   if (kth != nullptr && t == 0) kth[row] = key_to_float(kstar);
 }
