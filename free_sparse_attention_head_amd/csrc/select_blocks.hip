@@ -15,9 +15,11 @@
 //      exact top-k of each branch by a radix select in 8-bit digits on
 //      order-preserving keys held in registers (per-wave LDS histogram,
 //      early stop once the k-th key's bin is kept whole; remaining ties go to
-//      the lower block index through a wave scan of the equal-key flags),
+//      the lower block index through a wave scan of the equal-key counts),
 //      union with the forced sink/band blocks, compaction into an ascending
-//      block list with a wave scan, and the bitmask row.
+//      block list with a wave scan, and the bitmask row.  Per-entry flags
+//      are per-lane bit masks, which keeps the wave's registers to 75 VGPRs
+//      and 86 SGPRs at 16 entries a lane (100 SGPRs as per-entry booleans).
 #include <math.h>
 
 #include "common.h"
@@ -152,20 +154,16 @@ __device__ __forceinline__ void wave_lds_fence() {
 // the top (histogram of the entries still matching the digits fixed so far,
 // counted from the largest bin down), stopping early once the k-th key's bin
 // is kept whole; the remaining ties are ranked by index with a wave scan.
+// A lane's valid entries are its first nv; the result is a per-lane bit mask
+// (bit e = entry e kept), so no per-entry flags live in lane-mask registers.
 template <int E>
-__device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], const bool (&valid)[E], int k,
-                                          int n, WaveShared& sh, bool (&sel)[E]) {
+__device__ __forceinline__ uint64_t wave_topk(const uint32_t (&key)[E], int nv, int k, int n,
+                                              WaveShared& sh) {
+  static_assert(E <= 64, "one mask bit per entry");
   const int l = lane_id();
-  if (k >= n) {  // every valid entry
-#pragma unroll
-    for (int e = 0; e < E; ++e) sel[e] = valid[e];
-    return;
-  }
-  if (k <= 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) sel[e] = false;
-    return;
-  }
+  const uint64_t vm = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+  if (k >= n) return vm;  // every valid entry
+  if (k <= 0) return 0ull;
   uint32_t prefix = 0, pmask = 0;
   int kk = k;  // entries still to take among those matching prefix
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -173,7 +171,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], const bool (
     wave_lds_fence();
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (valid[e] && (key[e] & pmask) == prefix)
+      if (e < nv && (key[e] & pmask) == prefix)
         __hip_atomic_fetch_add(&sh.hist[(key[e] >> shift) & 255u], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WAVEFRONT);
     wave_lds_fence();
@@ -206,22 +204,28 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], const bool (
     prefix |= (uint32_t)d << shift;
     pmask |= 255u << shift;
     if (cd == kk) {  // the k-th key's bin is kept whole
+      uint64_t sel = 0ull;
 #pragma unroll
-      for (int e = 0; e < E; ++e) sel[e] = valid[e] && (key[e] & pmask) >= prefix;
-      return;
+      for (int e = 0; e < E; ++e) sel |= (uint64_t)((key[e] & pmask) >= prefix) << e;
+      return sel & vm;
     }
   }
   // prefix is the k-th largest key; kk of its copies are kept, lowest index first
-  int neq = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) neq += (valid[e] && key[e] == prefix) ? 1 : 0;
-  int rank = wave_incl_scan(neq) - neq;
+  uint64_t gt = 0ull, eq = 0ull;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool eq = valid[e] && key[e] == prefix;
-    sel[e] = valid[e] && (key[e] > prefix || (eq && rank < kk));
-    rank += eq ? 1 : 0;
+    gt |= (uint64_t)(key[e] > prefix) << e;
+    eq |= (uint64_t)(key[e] == prefix) << e;
   }
+  gt &= vm;
+  eq &= vm;
+  const int neq = __popcll(eq);
+  const int rank = wave_incl_scan(neq) - neq;  // equal keys in lower lanes
+  // keep this lane's first max(0, kk - rank) equal keys
+  const int take = min(max(kk - rank, 0), neq);
+  uint64_t keep_eq = eq;
+  for (int x = take; x < neq; ++x) keep_eq &= ~(1ull << (63 - __builtin_clzll(keep_eq)));
+  return gt | keep_eq;
 }
 
 __device__ __forceinline__ int k_of(double p, int n) {
@@ -253,32 +257,29 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void select_rows_kernel(
   const float qn = sqrtf(wave_sum(s2));
 
   uint32_t kc[E], kr[E];
-  bool valid[E];
+  const int nv = min(max(n - l * E, 0), E);  // this lane's valid entries
   const float* scr = sc + (size_t)row * nB;
   const float* rr = rad + ((size_t)b * Hkv + g) * nB;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = l * E + e;
-    valid[e] = j < n;
-    const float s = valid[e] ? scr[j] : 0.f;
-    const float r = valid[e] ? fmaf(qn, rr[j], s) : 0.f;
+    const bool valid = e < nv;
+    const float s = valid ? scr[j] : 0.f;
+    const float r = valid ? fmaf(qn, rr[j], s) : 0.f;
     kc[e] = order_key(s);
     kr[e] = order_key(r);
-    if (score_r != nullptr && valid[e]) score_r[(size_t)row * nB + j] = r;
+    if (score_r != nullptr && valid) score_r[(size_t)row * nB + j] = r;
   }
-  bool selc[E], selr[E];
-  wave_topk<E>(kc, valid, k_of(p_c, n), n, sh, selc);
-  wave_topk<E>(kr, valid, k_of(p_r, n), n, sh, selr);
-
-  int cnt = 0;
-  bool m[E];
+  uint64_t m = wave_topk<E>(kc, nv, k_of(p_c, n), n, sh);
+  m |= wave_topk<E>(kr, nv, k_of(p_r, n), n, sh);
+  // forced blocks: j < sink, or j > i - band (the band's blocks)
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = l * E + e;
     const bool forced = (j < sink) || (band > 0 && j > i - band);
-    m[e] = valid[e] && (selc[e] || selr[e] || forced);
-    cnt += m[e] ? 1 : 0;
+    m |= (uint64_t)(e < nv && forced) << e;
   }
+  const int cnt = __popcll(m);
   const int inc = wave_incl_scan(cnt);
   int pos = inc - cnt;
   const int tot = __shfl(inc, 63, 64);
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void select_rows_kernel(
   wave_lds_fence();
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (m[e]) {
+    if ((m >> e) & 1ull) {
       const int j = l * E + e;
       lst[pos++] = j;
       __hip_atomic_fetch_or(&sh.words[j >> 5], 1u << (j & 31), __ATOMIC_RELAXED,
