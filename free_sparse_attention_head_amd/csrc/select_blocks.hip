@@ -8,9 +8,9 @@
 //   1. pool_queries_kernel: qbar[b,h,i,:] = mean of the T query rows of block i
 //      (one workgroup per (b, i): the T x Hq x D slab is contiguous in HBM and
 //      read once with 16-byte loads).
-//   2. centroid_score_kernel: Sc[b,h,i,j] = qbar_i . c_j for j <= i, as 64x64
+//   2. centroid_score_kernel: Sc[b,h,i,j] = qbar_i . c_j for j <= i, as 128x128
 //      fp32 register-blocked tiles of the lower triangle (LDS-staged operands,
-//      4x4 outputs per thread, sequential accumulation over d).
+//      8x8 outputs per thread, sequential accumulation over d).
 //   3. select_rows_kernel: one wave per row (b,h,i): Sr = Sc + ||qbar||*r,
 //      exact top-k of each branch by a radix select in 8-bit digits on
 //      order-preserving keys held in registers (per-wave LDS histogram,
@@ -75,14 +75,19 @@ __global__ __launch_bounds__(256) void pool_queries_kernel(const TI* __restrict_
 }
 
 // ---------------------------------------------------------------- scores
-constexpr int kTile = 64, kDc = 32;
+// 128x128 tiles of the lower triangle, 256 threads, 8x8 outputs a thread
+// (rows ty*4 + {0..3} and 64 + ty*4 + {0..3}, columns likewise from tx): four
+// 16-byte LDS reads feed 64 FMAs, half the LDS traffic per FMA of 4x4
+// outputs a thread, which left the kernel waiting on LDS.  The dot products
+// still accumulate over d in order, one fmaf per term.
+constexpr int kTile = 128, kDc = 32;
 
 __global__ __launch_bounds__(256) void centroid_score_kernel(const float* __restrict__ qbar,
                                                              const float* __restrict__ cen,
                                                              float* __restrict__ sc, int Hq,
                                                              int Hkv, int nB, int D, int tiles) {
-  __shared__ float As[kDc][kTile + 4];
-  __shared__ float Bs[kDc][kTile + 4];
+  __shared__ __align__(16) float As[kDc][kTile + 4];
+  __shared__ __align__(16) float Bs[kDc][kTile + 4];
   const int x = blockIdx.x % tiles, bh = blockIdx.x / tiles;
   const int h = bh % Hq, b = bh / Hq, g = h / (Hq / Hkv);
   // x -> (it, jt) with jt <= it, row-major over the lower triangle
@@ -93,42 +98,80 @@ __global__ __launch_bounds__(256) void centroid_score_kernel(const float* __rest
   const float* A = qbar + ((size_t)b * Hq + h) * nB * D;
   const float* Bm = cen + ((size_t)b * Hkv + g) * nB * D;
   const int t = threadIdx.x, ty = t / 16, tx = t % 16;
-  float acc[4][4];
+  float acc[2][4][2][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[a][r][c][e] = 0.f;
   for (int d0 = 0; d0 < D; d0 += kDc) {
-    // stage 64 rows x 32 d of each operand, transposed to [d][row]
-    for (int e = t; e < kTile * kDc; e += 256) {
-      const int r = e / kDc, dd = e % kDc;
+    // stage 128 rows x 32 d of each operand, transposed to [d][row]: thread
+    // e reads 4 consecutive d of row e/8 (eight threads cover a row's 128 B)
+#pragma unroll
+    for (int u = 0; u < kTile * kDc / 4 / 256; ++u) {
+      const int e = t + 256 * u, r = e / (kDc / 4), d4 = e % (kDc / 4);
       const int ia = it * kTile + r, jb = jt * kTile + r;
-      As[dd][r] = ia < nB ? A[(size_t)ia * D + d0 + dd] : 0.f;
-      Bs[dd][r] = jb < nB ? Bm[(size_t)jb * D + d0 + dd] : 0.f;
+      const float4 va = ia < nB ? *reinterpret_cast<const float4*>(A + (size_t)ia * D + d0 + 4 * d4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 vb = jb < nB ? *reinterpret_cast<const float4*>(Bm + (size_t)jb * D + d0 + 4 * d4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      As[4 * d4 + 0][r] = va.x;
+      As[4 * d4 + 1][r] = va.y;
+      As[4 * d4 + 2][r] = va.z;
+      As[4 * d4 + 3][r] = va.w;
+      Bs[4 * d4 + 0][r] = vb.x;
+      Bs[4 * d4 + 1][r] = vb.y;
+      Bs[4 * d4 + 2][r] = vb.z;
+      Bs[4 * d4 + 3][r] = vb.w;
     }
     __syncthreads();
-#pragma unroll 8
+#pragma unroll 4
     for (int dd = 0; dd < kDc; ++dd) {
-      const float4 av = *reinterpret_cast<const float4*>(&As[dd][ty * 4]);
-      const float4 bv = *reinterpret_cast<const float4*>(&Bs[dd][tx * 4]);
-      const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+      float av[2][4], bv[2][4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&As[dd][64 * h2 + ty * 4]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&Bs[dd][64 * h2 + tx * 4]);
+        av[h2][0] = a4.x, av[h2][1] = a4.y, av[h2][2] = a4.z, av[h2][3] = a4.w;
+        bv[h2][0] = b4.x, bv[h2][1] = b4.y, bv[h2][2] = b4.z, bv[h2][3] = b4.w;
+      }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(ar[a], br[c], acc[a][c]);
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[a][r][c][e] = fmaf(av[a][r], bv[c][e], acc[a][r][c][e]);
     }
     __syncthreads();
   }
   float* out = sc + ((size_t)b * Hq + h) * nB * nB;
+  // a tile left of the diagonal holds only j < i; rows are 16-byte aligned
+  // when nB is a multiple of 4
+  const bool vec = jt < it && (nB & 3) == 0;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = it * kTile + ty * 4 + a;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = jt * kTile + tx * 4 + c;
-      if (i < nB && j <= i) out[(size_t)i * nB + j] = acc[a][c];
+    for (int r = 0; r < 4; ++r) {
+      const int i = it * kTile + 64 * a + ty * 4 + r;
+      if (i >= nB) continue;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int j0 = jt * kTile + 64 * c + tx * 4;
+        if (vec && j0 + 3 < nB) {
+          *reinterpret_cast<float4*>(&out[(size_t)i * nB + j0]) =
+              make_float4(acc[a][r][c][0], acc[a][r][c][1], acc[a][r][c][2], acc[a][r][c][3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < nB && j0 + e <= i) out[(size_t)i * nB + j0 + e] = acc[a][r][c][e];
+        }
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------- selection
