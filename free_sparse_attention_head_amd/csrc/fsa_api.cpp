@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <initializer_list>
 
 #include "fsa.h"
 #include "launch.h"
@@ -37,6 +38,17 @@ int device_check() {
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? FSA_OK : FSA_ERR_LAUNCH; }
+
+// The kernels move data tensors and workspaces in 16-byte vectors and index
+// arrays in 4-byte words; a pointer off that grain is rejected, never read.
+// Null pointers pass here (the null checks come first).
+bool off_grain(std::initializer_list<const void*> ptrs, uintptr_t grain) {
+  for (const void* ptr : ptrs)
+    if (reinterpret_cast<uintptr_t>(ptr) & (grain - 1)) return true;
+  return false;
+}
+bool misaligned16(std::initializer_list<const void*> ptrs) { return off_grain(ptrs, 16); }
+bool misaligned4(std::initializer_list<const void*> ptrs) { return off_grain(ptrs, 4); }
 
 int check_prefill_shape(const fsa_prefill_shape* s, PrefillDims* d) {
   if (s == nullptr) return FSA_ERR_NULL;
@@ -180,6 +192,7 @@ int block_stats(fsa_dtype dt, const void* k, const fsa_prefill_shape* s, float* 
   if (rc) return rc;
   if ((rc = check_dtype_prefill(dt))) return rc;
   if (!k || !centroid || !radius) return FSA_ERR_NULL;
+  if (misaligned16({k, centroid, radius})) return FSA_ERR_ARG;
   if ((rc = device_check())) return rc;
   return launch_status(fsa::launch_block_stats(dt == FSA_F32, k, centroid, radius, d, st));
 }
@@ -196,6 +209,9 @@ int select_blocks(fsa_dtype dt, const void* q, const float* centroid, const floa
   if (isnan(p->p_centroid) || isnan(p->p_rescue)) return FSA_ERR_ARG;
   if (p->band_blocks < 0 || p->sink_blocks < 0) return FSA_ERR_ARG;
   if (!ws) return FSA_ERR_NULL;
+  if (misaligned16({q, centroid, radius, score_c, score_r, ws}) ||
+      misaligned4({mask_bits, block_idx, block_cnt}))
+    return FSA_ERR_ARG;
   if (ws_bytes < fsa::select_ws_bytes(d)) return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;
   return launch_status(fsa::launch_select_blocks(dt == FSA_F32, q, centroid, radius, d,
@@ -219,6 +235,7 @@ int sparse_prefill_attn(fsa_dtype dt, const void* q, const void* k, const void* 
   // the kernels track the running row maximum in unscaled score units, which
   // orders scaled scores the same way only for a positive scale
   if (!isfinite(scale) || !(scale > 0.f)) return FSA_ERR_ARG;
+  if (misaligned16({q, k, v, out}) || misaligned4({block_idx, block_cnt, lse})) return FSA_ERR_ARG;
   if ((rc = device_check())) return rc;
   return launch_status(fsa::launch_prefill_attn(dt == FSA_F32, q, k, v, d, block_idx, block_cnt,
                                                 scale, out, lse, st));
@@ -236,6 +253,8 @@ static int topk_common(fsa_dtype dt, const void* q, const void* k_pool,
   if (k < 1 || k > d.max_seq_len) return FSA_ERR_ARG;
   if (d.max_seq_len > fsa::kTopkMaxSeqLen) return FSA_ERR_SHAPE;
   if (!ws) return FSA_ERR_NULL;
+  if (misaligned16({q, k_pool, ws}) || misaligned4({page_table, seq_lens, idx, scores, kth}))
+    return FSA_ERR_ARG;
   if (ws_bytes < fsa::topk_ws_bytes(d, k)) return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;
   return launch_status(
@@ -268,6 +287,7 @@ int topk_indices_kv(fsa_dtype dt, const void* q, const void* k_pool, const int32
 int topk_union_kv(const int32_t* idx, int B, int Hq, int Hkv, int k, int32_t* out,
                   int32_t* cnt, hipStream_t st) {
   if (!idx || !out) return FSA_ERR_NULL;
+  if (misaligned4({idx, out, cnt})) return FSA_ERR_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FSA_ERR_SHAPE;
   if (k < 1) return FSA_ERR_ARG;
   if ((long long)(Hq / Hkv) * k > fsa::kUnionMax) return FSA_ERR_ARG;
@@ -292,6 +312,9 @@ int sparse_decode_attn(fsa_dtype dt, const void* q, const void* k_pool, const vo
     return FSA_ERR_NULL;
   if (!isfinite(scale)) return FSA_ERR_ARG;
   if (!ws) return FSA_ERR_NULL;
+  if (misaligned16({q, k_pool, v_pool, out, ws}) ||
+      misaligned4({page_table, seq_lens, lse, sel->idx, sel->scores, sel->segments, sel->n_seg}))
+    return FSA_ERR_ARG;
   if (ws_bytes < fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split)) return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;
   return launch_status(fsa::launch_decode_attn(q, k_pool, v_pool, page_table, seq_lens, d,
@@ -314,6 +337,9 @@ int sparse_decode_attn_noalloc(fsa_dtype dt, const void* q, const void* k_pool,
       !seq_lens || !out)
     return FSA_ERR_NULL;
   if (!isfinite(scale)) return FSA_ERR_ARG;
+  if (misaligned16({q, k_pool, v_pool, out}) ||
+      misaligned4({page_table, seq_lens, lse, sel->idx, sel->scores, sel->segments, sel->n_seg}))
+    return FSA_ERR_ARG;
   if (fsa::decode_ws_bytes(d, sel->mode, sel->k, sel->n_split) > fsa::kNoAllocScratchBytes)
     return FSA_ERR_WORKSPACE;
   if ((rc = device_check())) return rc;

@@ -10,6 +10,10 @@
  *     (host) are ordinary host memory read before the call returns.
  *   - Tensors are dense, row-major (C order), with the shapes given below;
  *     bf16 is IEEE bfloat16 stored in 16 bits, fp32 is IEEE binary32.
+ *   - bf16 / fp32 data tensors (queries, keys, values, KV pools, centroids,
+ *     radii, scores of select_blocks, outputs) and workspaces start on a
+ *     16-byte boundary, index / count / length arrays on a 4-byte boundary,
+ *     else FSA_ERR_ARG (the kernels move them in 16- and 4-byte words).
  *   - Every entry point validates its host-side arguments before any launch
  *     and returns FSA_OK (0) or a negative FSA_ERR_* code; nothing aborts,
  *     exits or throws across the ABI.  Kernel work is enqueued

@@ -108,6 +108,52 @@ def test_select_validation_and_workspace():
     assert lib.fsa_workspace_size(99, ctypes.byref(s), None) == 0
 
 
+def test_misaligned_pointers_are_rejected():
+    """Data tensors and workspaces off a 16-byte boundary, and index arrays off
+    a 4-byte one, come back as FSA_ERR_ARG before anything is launched."""
+    L, lib = _lib()
+    OFF16 = ctypes.c_void_p(0x1004)  # 4-byte aligned, not 16
+    OFF4 = ctypes.c_void_p(0x1002)
+    s = _shape(L)
+    assert lib.block_stats(L.FSA_BF16, OFF16, ctypes.byref(s), FAKE, FAKE, None) == L.FSA_ERR_ARG
+    assert lib.block_stats(L.FSA_BF16, FAKE, ctypes.byref(s), FAKE, OFF16, None) == L.FSA_ERR_ARG
+    ws = lib.fsa_workspace_size(L.FSA_OP_SELECT_BLOCKS, ctypes.byref(s), None)
+    p = L.SelectParams(0.25, 0.1, 0, 0)
+    sel_args = dict(q=FAKE, c=FAKE, r=FAKE, m=FAKE, bi=FAKE, bc=FAKE, sc=None, ws=FAKE)
+    for key, val in (("q", OFF16), ("c", OFF16), ("sc", OFF16), ("ws", OFF16), ("bi", OFF4)):
+        a = dict(sel_args, **{key: val})
+        assert lib.select_blocks(L.FSA_F32, a["q"], a["c"], a["r"], ctypes.byref(s),
+                                 ctypes.byref(p), a["m"], a["bi"], a["bc"], a["sc"], None,
+                                 a["ws"], ws, None) == L.FSA_ERR_ARG, key
+    for q, k, v, out in ((OFF16, FAKE, FAKE, FAKE), (FAKE, FAKE, OFF16, FAKE),
+                         (FAKE, FAKE, FAKE, OFF16)):
+        assert lib.sparse_prefill_attn(L.FSA_BF16, q, k, v, ctypes.byref(s), None, None, 0.125,
+                                       out, None, None, 0, None) == L.FSA_ERR_ARG
+    assert lib.sparse_prefill_attn(L.FSA_BF16, FAKE, FAKE, FAKE, ctypes.byref(s), OFF4, FAKE,
+                                   0.125, FAKE, None, None, 0, None) == L.FSA_ERR_ARG
+    ds = _dshape(L)
+    k = ctypes.c_int(16)
+    tws = lib.fsa_workspace_size(L.FSA_OP_TOPK, ctypes.byref(ds), ctypes.byref(k))
+    for q, kp, pt, ws_ in ((OFF16, FAKE, FAKE, FAKE), (FAKE, OFF16, FAKE, FAKE),
+                           (FAKE, FAKE, OFF4, FAKE), (FAKE, FAKE, FAKE, OFF16)):
+        assert lib.topk_indices(L.FSA_BF16, q, kp, pt, FAKE, ctypes.byref(ds), 16, FAKE, None,
+                                ws_, tws, None) == L.FSA_ERR_ARG
+    sel = L.KvSelect(L.FSA_SEL_INDEX, FAKE.value, 16, None, None, 0, 0)
+    for q, kp, vp, out in ((OFF16, FAKE, FAKE, FAKE), (FAKE, FAKE, OFF16, FAKE),
+                           (FAKE, FAKE, FAKE, OFF16)):
+        assert lib.sparse_decode_attn(L.FSA_BF16, q, kp, vp, FAKE, FAKE, ctypes.byref(ds),
+                                      ctypes.byref(sel), 0.1, out, None, FAKE, 1 << 30,
+                                      None) == L.FSA_ERR_ARG
+        assert lib.sparse_decode_attn_noalloc(L.FSA_BF16, q, kp, vp, FAKE, FAKE, ctypes.byref(ds),
+                                              ctypes.byref(sel), 0.1, out, None,
+                                              None) == L.FSA_ERR_ARG
+    bad_idx = L.KvSelect(L.FSA_SEL_INDEX, OFF4.value, 16, None, None, 0, 0)
+    assert lib.sparse_decode_attn(L.FSA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(ds),
+                                  ctypes.byref(bad_idx), 0.1, FAKE, None, FAKE, 1 << 30,
+                                  None) == L.FSA_ERR_ARG
+    assert lib.topk_union_kv(OFF4, 2, 8, 2, 16, FAKE, None, None) == L.FSA_ERR_ARG
+
+
 def _dshape(L, **kw):
     d = dict(B=2, Hq=8, Hkv=2, D=128, page_size=16, num_pages=64, max_pages=32, max_seq_len=512)
     d.update(kw)
