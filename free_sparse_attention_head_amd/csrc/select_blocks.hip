@@ -303,15 +303,38 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void select_rows_kernel(
   const int nv = min(max(n - l * E, 0), E);  // this lane's valid entries
   const float* scr = sc + (size_t)row * nB;
   const float* rr = rad + ((size_t)b * Hkv + g) * nB;
+  // A lane's entries are consecutive: with nB a multiple of 4 its quads start
+  // on 16-byte boundaries, and each quad whose four entries are valid is read
+  // with one 16-byte load of the scores and one of the radii (a lane's 16
+  // single-word loads at a 64-byte lane stride touched 4x the cache lines).
+  const bool quads = E % 4 == 0 && (nB & 3) == 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = l * E + e;
-    const bool valid = e < nv;
-    const float s = valid ? scr[j] : 0.f;
-    const float r = valid ? fmaf(qn, rr[j], s) : 0.f;
-    kc[e] = order_key(s);
-    kr[e] = order_key(r);
-    if (score_r != nullptr && valid) score_r[(size_t)row * nB + j] = r;
+  for (int e4 = 0; e4 < (E + 3) / 4; ++e4) {
+    float sv[4] = {0.f, 0.f, 0.f, 0.f}, rv[4] = {0.f, 0.f, 0.f, 0.f};
+    const int e0 = 4 * e4, j0 = l * E + e0;
+    if (quads && e0 + 4 <= nv) {
+      const float4 s4 = *reinterpret_cast<const float4*>(scr + j0);
+      const float4 r4 = *reinterpret_cast<const float4*>(rr + j0);
+      sv[0] = s4.x, sv[1] = s4.y, sv[2] = s4.z, sv[3] = s4.w;
+      rv[0] = r4.x, rv[1] = r4.y, rv[2] = r4.z, rv[3] = r4.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + u < E && e0 + u < nv) {
+          sv[u] = scr[j0 + u];
+          rv[u] = rr[j0 + u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u;
+      if (e >= E) break;
+      const bool valid = e < nv;
+      const float r = valid ? fmaf(qn, rv[u], sv[u]) : 0.f;
+      kc[e] = order_key(valid ? sv[u] : 0.f);
+      kr[e] = order_key(r);
+      if (score_r != nullptr && valid) score_r[(size_t)row * nB + j0 + u] = r;
+    }
   }
   uint64_t m = wave_topk<E>(kc, nv, k_of(p_c, n), n, sh);
   m |= wave_topk<E>(kr, nv, k_of(p_r, n), n, sh);

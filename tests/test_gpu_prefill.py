@@ -289,11 +289,12 @@ def test_selection_ties(kind):
         _exact_rows(_select_on(q, k, T, pc, pr, band, sink), pc, pr, band, sink, nB)
 
 
-@pytest.mark.parametrize("nB", [100, 300, 700, 2048, 4096])
+@pytest.mark.parametrize("nB", [100, 300, 700, 1001, 2048, 4096])
 def test_selection_long_rows(nB):
     """Row lengths for each selection instantiation not met elsewhere (2, 8,
-    16, 32 and 64 entries per lane): exact top-k of the kernel's own scores on
-    sampled rows, the longest included."""
+    16, 32 and 64 entries per lane; nB = 1001 is no multiple of 4, so its rows
+    are read with single-word loads): exact top-k of the kernel's own scores
+    on sampled rows, the longest included."""
     T, D = 64, 64
     S = nB * T
     print(f"[select long rows] S={S} T={T} nB={nB}", flush=True)
