@@ -128,14 +128,19 @@ __device__ __forceinline__ T wave_max(T v) {
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP lane moves (no
+// LDS round trip per step, as a __shfl_up ladder takes): a Hillis-Steele
+// scan inside each row of 16 lanes (row_shr 1, 2, 4, 8; lanes without a
+// source add 0), then each row's total carried forward: lane 15 into row 1
+// and lane 47 into row 3 (row_bcast:15), lane 31 into rows 2 and 3
+// (row_bcast:31).  Rows a move leaves out keep their value.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (l >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
