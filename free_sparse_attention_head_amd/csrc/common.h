@@ -3,7 +3,10 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace fsa {
 
@@ -114,18 +117,56 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
   return acc;
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// op over the 64 lanes of a wave, the result in every lane: the row_shr /
+// row_bcast ladder of wave_incl_scan (below) with `ident` for lanes that a
+// move gives no source, then lane 63 (which has seen every lane) read into
+// a scalar.  32-bit T only.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T v, T ident, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit lanes");
+  const int id = __builtin_bit_cast(int, ident);
+#define FSA_DPP_STEP(CTRL, ROWS)                                                              \
+  v = op(v, __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), \
+                                                              CTRL, ROWS, 0xf, false)))
+  FSA_DPP_STEP(0x111, 0xf);  // row_shr:1
+  FSA_DPP_STEP(0x112, 0xf);  // row_shr:2
+  FSA_DPP_STEP(0x114, 0xf);  // row_shr:4
+  FSA_DPP_STEP(0x118, 0xf);  // row_shr:8
+  FSA_DPP_STEP(0x142, 0xa);  // row_bcast:15
+  FSA_DPP_STEP(0x143, 0xc);  // row_bcast:31
+#undef FSA_DPP_STEP
+  return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
+__device__ __forceinline__ T wave_sum(T v) {
+  return wave_allreduce(v, T(0), [](T a, T b) { return a + b; });
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_allreduce(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
+}
+
+// x at this lane and at lane l ^ OFF (OFF = 8, 16 or 32), as two values whose
+// order may differ between the two lanes, so callers combine them
+// symmetrically: v_permlane32_swap / v_permlane16_swap exchange half-waves
+// or 16-lane rows, and DPP row_ror:8 rotates a 16-lane row by 8.
+template <int OFF>
+__device__ __forceinline__ void xor_pair(float x, float& a, float& b) {
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    static_assert(OFF == 8, "lane distance 8, 16 or 32");
+    a = x;
+    b = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xf, 0xf, false));
+  }
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave, in DPP lane moves (no

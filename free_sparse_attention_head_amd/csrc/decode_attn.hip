@@ -266,21 +266,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   // ---- merge the row groups of each wave (lanes LPR apart hold the same d
   // values of different row groups), then the waves through LDS, and write
   // the split's unnormalised partial (max, sum, output).
+  // One merge step with the row group OFF lanes away; the pair's order may
+  // differ between the two lanes, and the merge is symmetric in it.
+  auto merge_step = [&](auto off_c, int x) {
+    constexpr int OFF = decltype(off_c)::value;
+    float ma, mb, la, lb;
+    xor_pair<OFF>(m_run[x], ma, mb);
+    xor_pair<OFF>(l_run[x], la, lb);
+    const float M = fmaxf(ma, mb);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float wa = __builtin_amdgcn_exp2f(ma - Mu);
+    const float wb = __builtin_amdgcn_exp2f(mb - Mu);
+    l_run[x] = la * wa + lb * wb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float oa, ob;
+      xor_pair<OFF>(o[x][e], oa, ob);
+      o[x][e] = oa * wa + ob * wb;
+    }
+    m_run[x] = M;
+  };
+  static_assert(LPR == 8 || LPR == 16, "row groups of 8 or 16 lanes");
 #pragma unroll
   for (int x = 0; x < NH; ++x) {
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-      const float mo = __shfl_xor(m_run[x], off, 64);
-      const float lo = __shfl_xor(l_run[x], off, 64);
-      const float M = fmaxf(m_run[x], mo);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      const float ws = __builtin_amdgcn_exp2f(m_run[x] - Mu);
-      const float wo = __builtin_amdgcn_exp2f(mo - Mu);
-      l_run[x] = l_run[x] * ws + lo * wo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[x][e] = o[x][e] * ws + __shfl_xor(o[x][e], off, 64) * wo;
-      m_run[x] = M;
-    }
+    if constexpr (LPR == 8) merge_step(std::integral_constant<int, 8>{}, x);
+    merge_step(std::integral_constant<int, 16>{}, x);
+    merge_step(std::integral_constant<int, 32>{}, x);
     if (l < LPR) {
       if (dl == 0) {
         sm_m[wave][x] = m_run[x];

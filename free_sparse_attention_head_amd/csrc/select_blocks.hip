@@ -240,9 +240,9 @@ __device__ __forceinline__ uint64_t wave_topk(const uint32_t (&key)[E], int nv, 
       above = a;
     }
     const int src = __builtin_ctzll(__ballot(mine));  // exactly one lane (kk <= total)
-    d = __shfl(d, src, 64);
-    above = __shfl(above, src, 64);
-    cd = __shfl(cd, src, 64);
+    d = __builtin_amdgcn_readlane(d, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    cd = __builtin_amdgcn_readlane(cd, src);
     kk -= above;
     prefix |= (uint32_t)d << shift;
     pmask |= 255u << shift;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void select_rows_kernel(
   const int cnt = __popcll(m);
   const int inc = wave_incl_scan(cnt);
   int pos = inc - cnt;
-  const int tot = __shfl(inc, 63, 64);
+  const int tot = __builtin_amdgcn_readlane(inc, 63);
   int32_t* lst = bidx + (size_t)row * nB;
   // mask bits of this lane's entries, gathered into 32-bit words in LDS
   for (int w = l; w < nw; w += 64) sh.words[w] = 0u;

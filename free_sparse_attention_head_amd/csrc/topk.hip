@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
     uint32_t bound = 0u;
     if (hit != 0ull) {
       const int lb = __ffsll((unsigned long long)hit) - 1;  // first lane reaching k
-      const int above = __shfl(inc - (int)cb, lb, 64);      // keys in higher buckets
+      const int above = __builtin_amdgcn_readlane(inc - (int)cb, lb);  // keys in higher buckets
       const int bucket = kCoarse - 1 - lb;
       uint32_t fc = 0u;
       if (l < BPC)
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
             ++pos;
           }
         }
-        done += __shfl(inc, 63, 64);
+        done += __builtin_amdgcn_readlane(inc, 63);
       }
       const size_t cbase = (row0 + x) * (size_t)cstride + t0;
       for (int e = l; e < done; e += 64) {
@@ -454,7 +454,7 @@ __device__ void select_from_candidates(const CandStream& cs, int k, uint32_t b1,
       wtot += __popcll(mk);
     }
     int tot;
-    const int wo = __shfl(block_excl_scan(lane == 0 ? wtot : 0, sh.scan, &tot), 0, 64);
+    const int wo = __builtin_amdgcn_readlane(block_excl_scan(lane == 0 ? wtot : 0, sh.scan, &tot), 0);
 #pragma unroll
     for (int e = 0; e < kSelPer; ++e)
       if (f[e]) {
@@ -660,7 +660,8 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_num_sgpr(72), am
     }
     // one scan carries both counts (at most 16384 each): equal keys high
     int tot;
-    const int ex = __shfl(block_excl_scan(lane == 0 ? ((weq << 16) | wgt) : 0, sh.scan, &tot), 0, 64);
+    const int ex =
+        __builtin_amdgcn_readlane(block_excl_scan(lane == 0 ? ((weq << 16) | wgt) : 0, sh.scan, &tot), 0);
     const int g0 = gt_before + (ex & 0xffff), e0 = eq_before + (ex >> 16);
 #pragma unroll
     for (int e = 0; e < kSelPer; ++e) {
