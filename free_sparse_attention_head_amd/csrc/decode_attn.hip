@@ -25,8 +25,8 @@
 //   * a split takes at least kMinSplitPositions positions, so short segment
 //     lists leave surplus splits empty (max -inf, sum 0);
 //   * combine_kernel merges the splits of one (sequence, head): one wave
-//     reads every split's (max, sum) in parallel, then accumulates only the
-//     non-empty splits' outputs; with a single split the split kernel
+//     reads every split's (max, sum) in parallel, then the splits' outputs
+//     eight at a time, all loads of a batch in flight together; with a single split the split kernel
 //     normalises and writes the output itself.
 #include <math.h>
 
@@ -338,8 +338,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
                                                      uint16_t* __restrict__ out,
                                                      float* __restrict__ lse) {
   // one wave per (b, h): the lanes read the splits' (max, sum) pairs in
-  // parallel, the weights go through LDS, and the output pass reads only the
-  // splits with a non-zero weight (empty splits hold max = -inf)
+  // parallel, the weights go through LDS (an empty split holds max = -inf:
+  // weight 0), and the output pass loads the splits' outputs in batches
   __shared__ float w_s[kMaxSplit];
   const int bh = blockIdx.x, l = threadIdx.x;
   const float* pp = part + (size_t)bh * n_split * (D + 2);
@@ -360,12 +360,24 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float w = w_s[s];
-    if (w == 0.f) continue;  // the same for every lane
-    const float* ps = pp + (size_t)s * (D + 2);
+  // kCombineBatch splits' outputs are loaded together, then added in split
+  // order.  Every split wrote a finite output (an empty one 0, with weight 0),
+  // so adding w * o for a zero weight leaves the sum as skipping it would.
+  constexpr int kCombineBatch = 8;
+  for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+    float v[kCombineBatch][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] += w * ps[2 + l * DPL + e];
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float* ps = pp + (size_t)min(s0 + u, n_split - 1) * (D + 2);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) v[u][e] = ps[2 + l * DPL + e];
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float w = s0 + u < n_split ? w_s[s0 + u] : 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += w * v[u][e];
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
