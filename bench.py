@@ -684,10 +684,12 @@ def attach_workspaces(fsa, pf, dc, sg):
         ssel = fsa._lib.KvSelect(fsa.SEL_ALL, None, 0, None, None, 0, 0)
         wsb = fsa.workspace_size("decode", sshape, ssel)
         sg["ws"] = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-        # small modes: one split per 128 admitted tokens of a sequence, within the workspace
+        # small modes: one split per 256 admitted tokens of a sequence, at least 8
+        # (measured best for focus / local / streaming), within the workspace
         for name, m in sg["modes"].items():
             per_seq = m["admitted"] // Sg["B"]
-            m["n_split"] = max(1, min(wsb // (Sg["B"] * Sg["Hq"] * (Sg["D"] + 2) * 4), per_seq // 128))
+            m["n_split"] = max(1, min(wsb // (Sg["B"] * Sg["Hq"] * (Sg["D"] + 2) * 4),
+                                      max(8, per_seq // 256)))
 
 
 def profile_only(fsa, workloads, args):
