@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   constexpr int TPAGES = (TT + 2 * STEP) / 16;
   // digit-1 counts of bins 2w and 2w+1 share word w (a tile holds < 65536 keys)
   constexpr int HW = GR * kBins1 / 2;
-  __shared__ uint32_t lh[HW];
+  __shared__ __align__(16) uint32_t lh[HW];
   __shared__ __align__(16) float ssc[GR * TT + 4];  // + a spare quad for idle lanes
   __shared__ int pg[TPAGES];
   __shared__ int scan_tmp[17];
@@ -237,17 +237,27 @@ __global__ __launch_bounds__(256) void topk_score_kernel(
   // The tile's counts into the rows' histograms: the LDS counts hold only
   // keys at or above each row's bound, and the select reads exact counts only
   // from the k-th key's bin up, which is at or above every tile's bound.
-  // Thread u takes one coarse bucket of one row: its bins, then its total.
+  // Thread u takes one coarse bucket of one row: its BPC/2 count words, read
+  // with 16-byte LDS loads all at once (one at a time they were a chain of
+  // LDS round trips), then its bins and its total.
+  constexpr int WPU = BPC / 2;  // count words per coarse bucket
+  static_assert(WPU % 4 == 0, "buckets of whole 16-byte words");
   for (int u = tid; u < GR * kCoarse; u += 256) {
     const int x = u / kCoarse, cbk = u % kCoarse;
+    uint4 cw[WPU / 4];
+#pragma unroll
+    for (int w = 0; w < WPU / 4; ++w)
+      cw[w] = reinterpret_cast<const uint4*>(lh)[x * (kBins1 / 8) + cbk * (WPU / 4) + w];
     uint32_t tot = 0u;
 #pragma unroll
-    for (int w = 0; w < BPC / 2; ++w) {
-      const int bin = cbk * BPC + 2 * w;
-      const uint32_t cc = lh[x * (kBins1 / 2) + bin / 2];
-      uint32_t* hr = hist + (row0 + x) * kBins1 + bin;
-      if (cc & 0xffffu) atomicAdd(hr, cc & 0xffffu);
-      if (cc >> 16) atomicAdd(hr + 1, cc >> 16);
+    for (int w = 0; w < WPU; ++w) {
+      const uint32_t cc = (w & 3) == 0 ? cw[w / 4].x : (w & 3) == 1 ? cw[w / 4].y
+                        : (w & 3) == 2 ? cw[w / 4].z : cw[w / 4].w;
+      // bins 2w and 2w+1 are adjacent words of the row's histogram: one
+      // 64-bit add covers both (a bin never counts 2^32 keys: no carry)
+      if (cc)
+        atomicAdd(reinterpret_cast<unsigned long long*>(hist + (row0 + x) * kBins1 + cbk * BPC + 2 * w),
+                  ((unsigned long long)(cc >> 16) << 32) | (cc & 0xffffu));
       tot += (cc & 0xffffu) + (cc >> 16);
     }
     if (tot) atomicAdd(coarse + (row0 + x) * kCoarse + cbk, tot);
