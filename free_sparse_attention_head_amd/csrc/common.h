@@ -186,28 +186,23 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // Exclusive prefix sum over the whole workgroup (blockDim.x a multiple of 64,
-// at most 1024).  `tmp` is shared scratch of >= 17 ints.  Returns the
-// exclusive prefix of v; *total receives the workgroup sum.  Contains
-// barriers: every thread must call it.
+// at most 1024).  `tmp` is shared scratch of >= 16 ints.  Returns the
+// exclusive prefix of v; *total receives the workgroup sum.  Each wave
+// publishes its total; then lanes 0..15 of every wave read the (at most 16)
+// totals, one wave scan ranks them, and a wave takes the inclusive sum of
+// the waves before it from lane w - 1 and the workgroup total from the last
+// wave's lane: no thread walks the totals in a chain.  Contains barriers:
+// every thread must call it.
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int inc = wave_incl_scan(v);
-  if (lane_id() == 63) tmp[w] = inc;
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6, l = lane_id();
+  const int inc = wave_incl_scan(v);
+  if (l == 63) tmp[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < nw; ++i) {
-      int t = tmp[i];
-      tmp[i] = run;
-      run += t;
-    }
-    tmp[16] = run;
-  }
-  __syncthreads();
-  int r = tmp[w] + inc - v;
-  *total = tmp[16];
-  __syncthreads();
-  return r;
+  const int wsum = wave_incl_scan(l < nw ? tmp[l] : 0);  // lanes >= nw add 0
+  const int before = w > 0 ? __builtin_amdgcn_readlane(wsum, w - 1) : 0;
+  *total = __builtin_amdgcn_readlane(wsum, nw - 1);
+  __syncthreads();  // tmp is free for the next call
+  return before + inc - v;
 }
 
 // Map a launch of `padded` workgroups (a multiple of kXcds) onto logical work

@@ -1,0 +1,46 @@
+"""Register budgets that kernels' occupancy depends on (CPU only: compiles
+the device code to assembly and reads the kernel descriptors).
+
+The top-k select kernel runs one 1024-thread workgroup per score row, and its
+time is set by how many rows run per CU: two workgroups share a CU only while
+a wave holds at most 64 VGPRs and about 72 SGPRs (an occupancy probe placed
+one per CU at 78 SGPRs or 71 VGPRs).  The compiler does not enforce the VGPR
+cap the kernel asks for, so this test does."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from free_sparse_attention_head_amd import build as B
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                                reason="hipcc not available")
+
+
+def _descriptors(src, tmp_path):
+    out = tmp_path / (os.path.basename(src) + ".s")
+    cmd = [B._hipcc()] + [x for x in B.COMMON if x != "-fPIC"] + ["--cuda-device-only", "-S", "-o", str(out), src]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    text = out.read_text()
+    kd = {}
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S):
+        body = m.group(2)
+        get = lambda key: int(re.search(r"\.amdhsa_" + key + r" (\d+)", body).group(1))
+        kd[m.group(1)] = {"vgpr": get("next_free_vgpr"), "sgpr": get("next_free_sgpr"),
+                          "lds": get("group_segment_fixed_size"),
+                          "scratch": get("private_segment_fixed_size")}
+    return kd
+
+
+def test_topk_select_kernel_fits_two_workgroups_per_cu(tmp_path):
+    kd = _descriptors(os.path.join(B.CSRC, "topk.hip"), tmp_path)
+    sel = [v for k, v in kd.items() if "topk_select_kernel" in k]
+    assert len(sel) == 1, list(kd)
+    d = sel[0]
+    assert d["vgpr"] <= 64, d
+    assert d["sgpr"] <= 72, d
+    assert d["scratch"] == 0, d
+    assert 2 * d["lds"] <= 160 * 1024, d
