@@ -94,6 +94,37 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Exclusive prefix count of 0/1 flags over the workgroup, for the block-list
+// build that runs once per workgroup: a __shfl_up ladder inside each wave and
+// one thread walking the wave totals.  Its speed does not matter here; the
+// kernel sits at 256 VGPRs, and with the DPP-ladder form of the scan the
+// register allocation of the main loop pushed one value to scratch.
+__device__ __forceinline__ int list_excl_count(int v, int* tmp, int* total) {
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6, l = threadIdx.x & 63;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (l >= o) inc += t;
+  }
+  if (l == 63) tmp[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int x = 0; x < nw; ++x) {
+      const int t = tmp[x];
+      tmp[x] = run;
+      run += t;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  const int r = tmp[w] + inc - v;
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
 }  // namespace
 
 template <int D, int BLK, int KCH, int LMAX>
@@ -176,7 +207,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     const int ok = (j >= 0 && j <= i) ? 1 : 0;
     FSA_DEBUG_RAISE(e < cnt && !ok, FSA_DBG_BLOCK_INDEX);
     int tot;
-    const int pos = block_excl_scan(ok, scan_tmp, &tot);
+    const int pos = list_excl_count(ok, scan_tmp, &tot);
     if (ok) Ls[nvalid + pos] = (uint16_t)j;
     nvalid += tot;
   }

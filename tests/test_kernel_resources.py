@@ -44,3 +44,16 @@ def test_topk_select_kernel_fits_two_workgroups_per_cu(tmp_path):
     assert d["sgpr"] <= 72, d
     assert d["scratch"] == 0, d
     assert 2 * d["lds"] <= 160 * 1024, d
+
+
+def test_prefill_attention_kernels_do_not_spill(tmp_path):
+    """The bf16 attention kernel runs two waves per SIMD at up to 256 VGPRs a
+    lane; its allocation is tight enough that unrelated code shapes have
+    pushed a value to scratch.  Every instantiation must stay spill-free and
+    within 256 VGPRs."""
+    kd = _descriptors(os.path.join(B.CSRC, "prefill_attn_bf16.hip"), tmp_path)
+    pf = {k: v for k, v in kd.items() if "prefill_attn_bf16_kernel" in k}
+    assert len(pf) >= 6, list(kd)
+    for name, d in pf.items():
+        assert d["scratch"] == 0, (name, d)
+        assert d["vgpr"] <= 256, (name, d)
