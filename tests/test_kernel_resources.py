@@ -57,3 +57,13 @@ def test_prefill_attention_kernels_do_not_spill(tmp_path):
     for name, d in pf.items():
         assert d["scratch"] == 0, (name, d)
         assert d["vgpr"] <= 256, (name, d)
+
+
+@pytest.mark.parametrize("src", ["topk.hip", "decode_attn.hip", "select_blocks.hip",
+                                 "block_stats.hip", "prefill_attn.hip"])
+def test_no_kernel_spills_to_scratch(src, tmp_path):
+    """Every kernel of the library keeps its registers out of scratch memory."""
+    kd = _descriptors(os.path.join(B.CSRC, src), tmp_path)
+    assert kd, src
+    spills = {k: v["scratch"] for k, v in kd.items() if v["scratch"]}
+    assert not spills, spills
