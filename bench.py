@@ -25,8 +25,9 @@ ideal block top-k) compared at matched density on the 32K prompt for 64- and
 Kernel times (medians, 50 timed steps after 5 warm-up steps by default) come
 from HIP events on the launch stream.  The headline value
 is the sparse prefill attention kernel's effective TFLOP/s on executed
-blocks (4*T*T*D FLOP per executed query-block/key-block pair); decode is
-reported as admitted KV bytes per second.
+blocks (4*T*T*D FLOP per executed query-block/key-block pair) over its mean
+launch time in the timed steps, and so is each roofline's `achieved`; decode
+is reported as admitted KV bytes per second.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--density 0.06]
 """
@@ -75,6 +76,10 @@ class Timer:
         """(median, min) in ms of the recorded launches after the first `skip`."""
         xs = [s.elapsed_time(e) for s, e in self.ev[name][skip:]]
         return float(np.median(xs)), float(np.min(xs))
+
+    def mean(self, name, skip=0):
+        """Mean in ms of the recorded launches after the first `skip`."""
+        return float(np.mean([s.elapsed_time(e) for s, e in self.ev[name][skip:]]))
 
     def clear(self):
         self.ev = {}
@@ -773,15 +778,15 @@ def main():
 
     k_ms = {n: tm.ms(n) for n in tm.ev}
     flops, executed = prefill_flops(pf)
-    attn_ms = k_ms["sparse_prefill_attn"][0]
+    attn_ms = tm.mean("sparse_prefill_attn")  # the rooflines take mean launch times
     tflops = flops / (attn_ms * 1e-3) / 1e12
     path_ms = sum(k_ms[n][0] for n in ("block_stats", "select_blocks", "sparse_prefill_attn"))
     idx_bytes = Dd["B"] * Dd["Hq"] * Dd["k"] * kv_row_bytes(Dd["D"])
-    reuse_ms = k_ms["decode_index"][0]
+    reuse_ms = tm.mean("decode_index")
     reuse_gbps = idx_bytes / (reuse_ms * 1e-3) / 1e9
     scan_bytes = Dd["B"] * Dd["N"] * Dd["Hkv"] * Dd["D"] * 2
     topk_ms = k_ms["topk_indices"][0]
-    group_ms = topk_ms + k_ms["decode_index_anchor"][0] + 3 * reuse_ms
+    group_ms = topk_ms + k_ms["decode_index_anchor"][0] + 3 * k_ms["decode_index"][0]  # medians
     group_bytes = scan_bytes + 4 * idx_bytes - Dd["B"] * Dd["Hq"] * Dd["k"] * Dd["D"] * 2
     seg = {}
     for name in ("global", "focus", "local", "streaming", "mixed"):
@@ -873,7 +878,9 @@ def main():
                             "kernel": "decode_split_kernel<128,1,INDEX> + combine",
                             "bytes_per_launch": idx_bytes, "avg_launch_ms": round(reuse_ms, 4)},
         "prefill": {"density": round(pf["density"], 4), "p_c": pf["p_c"], "p_r": pf["p_r"],
-                    "attn_ms": round(attn_ms, 4), "attn_min_ms": round(k_ms["sparse_prefill_attn"][1], 4),
+                    "attn_ms": round(attn_ms, 4),
+                    "attn_median_ms": round(k_ms["sparse_prefill_attn"][0], 4),
+                    "attn_min_ms": round(k_ms["sparse_prefill_attn"][1], 4),
                     "block_stats_ms": round(k_ms["block_stats"][0], 4),
                     "select_ms": round(k_ms["select_blocks"][0], 4),
                     "path_ms": round(path_ms, 4), "path_TFLOPs": round(flops / path_ms / 1e9, 2)},
