@@ -362,6 +362,51 @@ def test_empty_segment_gives_zero_output():
     assert (out.cpu() == 0).all() and torch.isinf(lse.cpu()).all()
 
 
+@pytest.mark.parametrize("n_split", [0, 1, 3])
+def test_empty_sequence_in_a_batch(n_split):
+    """A sequence with no cached tokens beside a ragged one: its top-k slots
+    are all -1 with kth -inf (scores -inf in the scored form), and index and
+    all-token decode give o = 0, lse = -inf; the other sequence still matches
+    the oracle."""
+    import free_sparse_attention_head_amd as fsa
+    B, N, Hq, Hkv, D, k = 2, 2048, 8, 2, 128, 64
+    print(f"[decode case empty-seq] n_split={n_split}", flush=True)
+    d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=2, seq_lens=[0, 1500], seed=91,
+                                device="cpu")
+    pt, sl = d["page_table"].cuda(), d["seq_lens"].cuda()
+    L0 = {x: t.cuda() for x, t in d["layers"][0].items()}
+    L1 = {x: t.cuda() for x, t in d["layers"][1].items()}
+    idx, kth = fsa.topk_indices(L0["q"], L0["k"], pt, sl, k, max_seq_len=N)
+    idxs, sco, kths = fsa.topk_indices_scored(L0["q"], L0["k"], pt, sl, k, max_seq_len=N)
+    assert (idx[0].cpu() == -1).all()
+    assert (idxs[0].cpu() == -1).all() and (sco[0].cpu() == -math.inf).all()
+    assert torch.equal(idx.cpu(), idxs.cpu())
+    scale = 1.0 / math.sqrt(D)
+    q0, q1 = workloads.to_f64(d["layers"][0]["q"]), workloads.to_f64(d["layers"][1]["q"])
+    assert np.isneginf(kth[0].cpu().numpy()).all()
+    for h in range(Hq):
+        K0, _ = seq_kv(d, 0, 1, oracle.kv_head(h, Hq, Hkv))
+        scores = oracle.anchor_scores(q0[1, h], K0)
+        ref, ref_kth = oracle.topk(scores, k)
+        n_diff, n_exc = topk_diff_excused(idx[1, h].cpu().numpy(), ref, scores, ref_kth)
+        assert n_diff == n_exc
+        assert abs(kth[1, h].item() - ref_kth) <= 1e-3
+    out, lse = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], pt, sl, mode=fsa.SEL_INDEX,
+                                      idx=idx, n_split=n_split, max_seq_len=N)
+    outa, lsea = fsa.sparse_decode_attn(L1["q"], L1["k"], L1["v"], pt, sl, mode=fsa.SEL_ALL,
+                                        n_split=n_split, max_seq_len=N)
+    for o, l in ((out, lse), (outa, lsea)):
+        assert (o[0].cpu() == 0).all() and (l[0].cpu() == -math.inf).all()
+    for h in range(Hq):
+        K1, V1 = seq_kv(d, 1, 1, oracle.kv_head(h, Hq, Hkv))
+        ro, rl = oracle.index_attention(q1[1, h], K1, V1, idx[1, h].cpu().numpy(), scale)
+        assert np.abs(out[1, h].float().cpu().numpy() - ro).max() <= TOL_BF16
+        assert abs(lse[1, h].item() - rl) <= 1e-2
+        ao, al = oracle.segment_attention(q1[1, h], K1, V1, [(0, 1500)], scale)
+        assert np.abs(outa[1, h].float().cpu().numpy() - ao).max() <= TOL_BF16
+        assert abs(lsea[1, h].item() - al) <= 1e-2
+
+
 @pytest.mark.parametrize("n_split", [64, 4096])
 def test_short_segments_with_many_splits(n_split):
     """A few hundred admitted tokens (three short segments, 600 in all) against
