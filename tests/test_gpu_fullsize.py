@@ -9,7 +9,9 @@ times, checked on sampled outputs that the fp64 oracle computes one by one.
   * 128K Kascade decode group: B=32, N=131072, 32 / 8 heads, k=2048, 4 layers
     (anchor top-k, indices reused by layers 1-3), shuffled 16-token pages; and
     its per-KV-head variant (pooled top-k, shared indices).
-  * 1M segment decode: B=4, N=2^20, global / focus / local / streaming masks.
+  * 1M segment decode: B=4, N=2^20, global / focus / local / streaming masks;
+    and the scored top-k with the anchor's attention over the same 1M pool
+    shape, ragged lengths.
 
 Sampled rows: block statistics and selector rows against the oracle
 (bit-exact up to near-threshold entries), attention outputs against the
@@ -198,6 +200,49 @@ def test_kascade_kv_shared_decode_128k_group():
                                                       Kl, Vl, row, 1 / math.sqrt(D))
                     assert np.abs(outs[li][b, h].double().cpu().numpy() - o_ref).max() <= TOL_BF16
     print(f"[fullsize kascade-kv] pooled top-k entries differing {n_diff}, excused {n_exc}", flush=True)
+    assert n_diff == n_exc
+
+
+def test_scored_topk_1m_context():
+    """Top-k at a 1M-token context (the segment workload's pool shape: B=4,
+    2^20 tokens, 32 / 8 heads, shuffled pages), ragged lengths (2^20, a
+    length not a multiple of the page, and exactly k), in the scored form the
+    anchor layer uses, and the anchor's V-only attention from those scores:
+    about 500 score tiles per row and the longest candidate streams the
+    select kernel reads."""
+    fsa = _fsa()
+    B, N, Hq, Hkv, D, k = 4, 1 << 20, 32, 8, 128, 2048
+    lens = [N, N - 12345, 700003, k]
+    print(f"[fullsize topk-1m] B={B} N={N} k={k} seq_lens={lens}", flush=True)
+    d = workloads.decode_inputs(B, N, Hq, Hkv, D, layers=1, seq_lens=lens, seed=1005, device="cuda")
+    pt, sl = d["page_table"], d["seq_lens"]
+    Lr = d["layers"][0]
+    idx, sco, kth = fsa.topk_indices_scored(Lr["q"], Lr["k"], pt, sl, k)
+    out, _ = fsa.sparse_decode_attn(Lr["q"], Lr["k"], Lr["v"], pt, sl, mode=fsa.SEL_INDEX_SCORED,
+                                    idx=idx, scores=sco)
+    torch.cuda.synchronize()
+    idx_h, sco_h, kth_h = idx.cpu().numpy(), sco.cpu().numpy(), kth.cpu().numpy()
+    assert (idx_h[3] == np.arange(k)).all()               # n == k: every key, in order
+    rng = np.random.default_rng(6)
+    n_diff = n_exc = 0
+    for b in (0, 1, 2):
+        for h in rng.choice(Hq, size=2, replace=False):
+            g = oracle.kv_head(h, Hq, Hkv)
+            n = lens[b]
+            K = _seq_kv(Lr["k"], pt[b], n, g)
+            qh = workloads.to_f64(Lr["q"][b, h])
+            s = oracle.anchor_scores(qh, K)
+            ref_idx, ref_kth = oracle.topk(s, k)
+            row = idx_h[b, h]
+            assert (np.diff(row) > 0).all() and row.min() >= 0 and row.max() < n
+            dd, ee = topk_diff_excused(row, ref_idx, s, ref_kth)
+            n_diff, n_exc = n_diff + dd, n_exc + ee
+            assert abs(kth_h[b, h] - ref_kth) <= BAND
+            assert np.abs(sco_h[b, h] - s[row]).max() <= 1e-3      # each kept key's own score
+            V = _seq_kv(Lr["v"], pt[b], n, g)
+            o_ref, _ = oracle.index_attention(qh, K, V, row, 1 / math.sqrt(D))
+            assert np.abs(out[b, h].double().cpu().numpy() - o_ref).max() <= TOL_BF16, (b, h)
+    print(f"[fullsize topk-1m] top-k entries differing {n_diff}, excused {n_exc}", flush=True)
     assert n_diff == n_exc
 
 
