@@ -16,8 +16,11 @@
 //     fragment reads below are bank-conflict free;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the wave's Q tile resident
 //     as the B operand (each lane then holds one query row's scores);
-//   * online softmax in fp32: raw-score row max, exp2 with the scale folded
-//     into an FMA, thresholded lazy rescale of O^T;
+//   * online softmax in fp32 without a per-chunk row max: the reference
+//     exponent is the first chunk's row max, exp2 takes the scale folded into
+//     an FMA, and a chunk whose row sum leaves the safe range (a row grew far
+//     past the reference, or overflowed) is redone after raising the
+//     reference to the true running max and rescaling O^T;
 //   * O^T += V^T P^T: P^T comes from registers, V^T fragments come from the
 //     row-major V tile through ds_read_b64_tr_b16, which hands lane i of each
 //     16-lane group column i of the 4 x 16 tile the group addresses.
@@ -32,7 +35,12 @@ namespace fsa {
 
 namespace {
 
-constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+// Largest row-sum share of one chunk in one lane (16 or 32 P values) that is
+// accepted against the current reference exponent: P values up to about 2^19
+// are exact in fp32 and bf16 alike, and the accumulated sums stay far inside
+// the fp32 range.  A larger (or infinite, or NaN) share sends the chunk through
+// the reference-raising path.
+constexpr float kChunkSumMax = 16777216.0f;  // 2^24
 constexpr int kMaxBlocks = 4096;  // key blocks per sequence (S / T) supported
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 #define FSA_LDS __attribute__((address_space(3)))
@@ -280,8 +288,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  float l_part[2] = {0.f, 0.f};  // row-sum partials of the chunks since the last rescale
+  // reference exponent of P in log2 units (scaled score of the reference max),
+  // and the row sum of the chunks so far relative to it
+  float mref = -INFINITY, l_run = 0.f;
+  float l_part = 0.f;  // the current chunk's row-sum share
 
   // per-lane LDS offsets of the fragment reads
   const int li = l & 15, q16 = (l >> 4) & 1;  // transposing-read lane coordinates
@@ -291,11 +301,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   constexpr int NKK = D / 16;                  // MFMA k-steps of S
   constexpr int NDT = D / 32, NM = (KC / 16) * NDT;  // MFMAs of PV
 
-  // Causal mask (diagonal block only), row max in raw units and the lazy
-  // rescale for chunk c; returns the exponent offset of P.  Register r of
-  // tile tl holds key koff + tl*32 + (r/4)*8 + lg*4 + r%4.  Chunks wholly
-  // after this wave's rows come out all masked (P = 0).
-  auto prelude = [&](int c, int j, floatx16 (&s)[NKT]) -> float {
+  // Causal mask (diagonal block only) for chunk c.  Register r of tile tl
+  // holds key koff + tl*32 + (r/4)*8 + lg*4 + r%4.  Chunks wholly after this
+  // wave's rows come out all masked (P = 0).
+  auto causal_mask = [&](int c, int j, floatx16 (&s)[NKT]) {
     const int koff = (c % NCH) * KC;
     if (j == i) {
       const int rel = koff + lg * 4 - qrow;
@@ -305,27 +314,35 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
         for (int r = 0; r < 16; ++r)
           if (rel + tl * 32 + (r >> 2) * 8 + (r & 3) > 0) s[tl][r] = -INFINITY;
     }
+  };
+  auto row_max = [&](const floatx16 (&s)[NKT]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int tl = 0; tl < NKT; ++tl)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tl][r]);
-    mx = max_xor32(mx);
-    // lazy rescale: the reference max moves only when a row grows by more
-    // than kRescale (log2 units), so p <= 256 and O^T is rescaled rarely
-    const bool grow = (mx - m_run) * scale_log2 > kRescale;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
-      m_run = m_new;
-      l_run = (l_run + l_part[0] + l_part[1]) * alpha;
-      l_part[0] = l_part[1] = 0.f;
+    return max_xor32(mx);
+  };
+  // The reference exponent is set from the first chunk's row max (before the
+  // chunk loop).  Later chunks compute no max (see raise_ref), except the last
+  // one (`full`), whose step has no S work to hide a retry behind: it raises
+  // the reference to the running max up front.
+  auto prelude = [&](int c, int j, floatx16 (&s)[NKT], bool full) -> float {
+    causal_mask(c, j, s);
+    if (full) {
+      const float mx = row_max(s);
+      const float m_new = (mx == -INFINITY) ? mref : fmaxf(mref, mx * scale_log2);
+      if (__builtin_amdgcn_ballot_w64(m_new > mref) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(mref - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        mref = m_new;
+      }
     }
-    return (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+    return mref;
   };
 
   // One sixteenth of the softmax of a chunk: P elements 2q and 2q+1 of the
@@ -341,7 +358,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     pb[0] = (__bf16)p0;
     pb[1] = (__bf16)p1;
     pp[q] = __builtin_bit_cast(uint32_t, pb);
-    l_part[q & 1] += p0 + p1;
+    if (q == 0) l_part = p0 + p1;  // the chunk's first slice starts the sum
+    else l_part += p0 + p1;
+  };
+
+  // A chunk whose row-sum share is out of range: raise the reference to the
+  // row's true running max (both wave halves agree on it), rescale O^T and
+  // the row sum, and redo the chunk's P.  Returns the chunk's new share.
+  auto raise_ref = [&](const floatx16 (&s)[NKT], uint32_t (&pp)[NP]) -> float {
+    const float mx = row_max(s);
+    const float m_new = (mx == -INFINITY) ? mref : fmaxf(mref, mx * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(mref - m_new);
+    mref = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) p_slice(s, mref, pp, q);
+    return l_part;
   };
 
   // S^T = K Q^T of the next chunk from K tile kS into sn (NKT 32x32 tiles:
@@ -435,7 +471,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // and its copies
   auto block_of = [&](int c) { return (int)Ls[min(c, n - 1) / NCH]; };
   int jq0 = 0, jq1 = 0, jq2 = 0;
-  auto step = [&](auto has_next, int c, const unsigned char* kS, const unsigned char* vP,
+  auto step = [&](auto has_next, auto full, int c, const unsigned char* kS, const unsigned char* vP,
                   unsigned char* kI, unsigned char* vI, floatx16 (&sc)[NKT], floatx16 (&sn)[NKT]) {
     tile_barrier();
     if (c + 2 < n) issue_k(c + 2, jq2, kI);
@@ -446,7 +482,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     jq2 = block_of(c + 3);
     bf16x8 ring[KRD][NKT];
     if constexpr (decltype(has_next)::value) k_first(kS, ring);
-    const float mc = prelude(c, jc, sc);
+    const float mc = prelude(c, jc, sc, decltype(full)::value);
     uint32_t pp[NP];
     // Two waves share each SIMD.  While one is in its S + softmax phase
     // (MFMAs interleaved with exp and convert work) it takes issue priority;
@@ -455,6 +491,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
     __builtin_amdgcn_s_setprio(1);
     s_and_p(has_next, std::true_type{}, kS, sn, sc, mc, pp, ring);
     __builtin_amdgcn_s_setprio(0);
+    float lc = l_part;
+    if constexpr (!decltype(full)::value)
+      if (__builtin_amdgcn_ballot_w64(!(lc <= kChunkSumMax)) != 0) lc = raise_ref(sc, pp);
+    l_run += lc;
     pv(pp, vP);
   };
 
@@ -473,16 +513,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
       k_first(kb0, ring);
       s_and_p(std::true_type{}, std::false_type{}, kb0, sA, sB, 0.f, pp0, ring);
     }
+    // reference exponent: the first chunk's row max.  Key 0 of that chunk is
+    // visible to every row (its block lies before the query block or is the
+    // diagonal one), so the max is finite.
+    causal_mask(0, jq0, sA);
+    {
+      const float mx = row_max(sA);
+      mref = (mx == -INFINITY) ? 0.f : mx * scale_log2;
+    }
     int c = 0;
     for (; c + 2 < n; c += 2) {
-      step(std::true_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
-      step(std::true_type{}, c + 1, kb0, vb1, kb1, vb0, sB, sA);
+      step(std::true_type{}, std::false_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
+      step(std::true_type{}, std::false_type{}, c + 1, kb0, vb1, kb1, vb0, sB, sA);
     }
+    // the last one or two steps raise the reference up front (`full`), as
+    // they have no (or only a last) S work to hide a retry behind
     if (c + 1 < n) {
-      step(std::true_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
-      step(std::false_type{}, c + 1, kb0, vb1, kb1, vb0, sB, sA);
+      step(std::true_type{}, std::true_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
+      step(std::false_type{}, std::true_type{}, c + 1, kb0, vb1, kb1, vb0, sB, sA);
     } else {
-      step(std::false_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
+      step(std::false_type{}, std::true_type{}, c, kb1, vb0, kb0, vb1, sA, sB);
     }
   }
 
@@ -490,7 +540,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   // wave has passed its barrier, so the staging regions are free again: the
   // wave writes its rows there (lane: 4 values of row lq at d0) and stores
   // them back as whole rows.
-  l_run += l_part[0] + l_part[1];
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int t = i * BLK + qrow;
@@ -518,7 +567,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void prefill_attn_bf16_kernel(
   }
   if (LSE != nullptr && lg == 0)
     LSE[((size_t)b * Hq + h) * S + t] =
-        l_tot > 0.f ? (m_run * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+        l_tot > 0.f ? (mref + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, int BLK, int KCH, int LMAX>

@@ -337,3 +337,55 @@ def test_longest_prompt_block_lists(T, D):
     got = o[0, rows, 0].double().numpy()
     assert np.abs(got - ref).max() <= TOL_BF16
     assert np.abs(lse[0, 0, rows].double().numpy() - ref_lse).max() <= 1e-2
+
+
+@pytest.mark.parametrize("D,T", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("spike", [False, True])
+def test_scores_growing_along_the_row(D, T, spike):
+    """Scores that climb far above the first chunk's along each row: keys carry
+    a growing component along the queries' shared direction (30-40 log2 units
+    of growth over the prompt), and optionally one key with a logit about 150
+    log2 units above its neighbours, past the fp32 range of exp2 against any
+    earlier reference.  The attention kernel raises its reference exponent in
+    both cases; the result is still the exact masked softmax (dense mode and a
+    random ascending list with the diagonal block)."""
+    import free_sparse_attention_head_amd as fsa
+    B, S, Hq, Hkv = 1, 1024, 2, 1
+    nB = S // T
+    print(f"[growth case] D={D} T={T} spike={spike}", flush=True)
+    rng = np.random.default_rng(77 + D + T + int(spike))
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = 0.5 * rng.standard_normal((B, S, Hq, D)) + 4.0 * u
+    ramp = 60.0 * np.arange(S) / S
+    k = 0.5 * rng.standard_normal((B, S, Hkv, D)) + ramp[None, :, None, None] * u
+    if spike:
+        k[0, 700, 0] = 0.5 * rng.standard_normal(D) + 300.0 * u
+    v = rng.standard_normal((B, S, Hkv, D))
+    qt, kt, vt = (torch.tensor(x, dtype=torch.bfloat16) for x in (q, k, v))
+    bidx = torch.zeros((B, Hq, nB, nB), dtype=torch.int32)
+    bcnt = torch.zeros((B, Hq, nB), dtype=torch.int32)
+    for h in range(Hq):
+        for i in range(nB):
+            keep = sorted(set(np.flatnonzero(rng.random(i) < 0.6).tolist()) | {i})
+            bidx[0, h, i, :len(keep)] = torch.tensor(keep, dtype=torch.int32)
+            bcnt[0, h, i] = len(keep)
+    o_sp, l_sp = fsa.sparse_prefill_attn(qt.cuda(), kt.cuda(), vt.cuda(), T, bidx.cuda(), bcnt.cuda())
+    o_dn, l_dn = fsa.sparse_prefill_attn(qt.cuda(), kt.cuda(), vt.cuda(), T)
+    o_sp, l_sp, o_dn, l_dn = (x.cpu() for x in (o_sp, l_sp, o_dn, l_dn))
+    qq, kk, vv = (workloads.to_f64(x) for x in (qt, kt, vt))
+    scale = 1 / math.sqrt(D)
+    worst = worst_lse = 0.0
+    for h in range(Hq):
+        m = lists_to_mask(bidx[0, h].numpy(), bcnt[0, h].numpy(), nB)
+        for got_o, got_l, ref in (
+                (o_sp, l_sp, oracle.masked_attention(qq[0, :, h], kk[0, :, 0], vv[0, :, 0], m, T, scale)),
+                (o_dn, l_dn, oracle.dense_attention(qq[0, :, h], kk[0, :, 0], vv[0, :, 0], scale))):
+            err = np.abs(got_o[0, :, h].double().numpy() - ref[0]).max()
+            lerr = np.abs(got_l[0, h].double().numpy() - ref[1]).max()
+            worst, worst_lse = max(worst, err), max(worst_lse, lerr)
+            assert err <= TOL_BF16, (h, err)
+            assert lerr <= LSE_TOL_BF16, (h, lerr)
+    # the growth is real: the last row's LSE sits far above the first block's
+    assert float(l_dn[0, 0, -1]) - float(l_dn[0, 0, T - 1]) > (60.0 if spike else 10.0)
+    print(f"[growth D={D} T={T} spike={spike}] max-abs error {worst:.3e}, worst lse error {worst_lse:.3e}")
