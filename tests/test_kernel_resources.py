@@ -91,3 +91,18 @@ def test_no_kernel_spills_to_scratch(src, tmp_path):
     assert kd, src
     spills = {k: v["scratch"] for k, v in kd.items() if v["scratch"]}
     assert not spills, spills
+
+
+def test_loop_scratch_check_sees_loop_blocks():
+    """The loop check flags a scratch access in a block the compiler marks as
+    part of a loop, and ignores one before the loop."""
+    text = ("k:                                      ; @k\n"
+            "\tscratch_store_dword off, v1, off\n"
+            ".LBB0_2:                                ; =>This Inner Loop Header: Depth=1\n"
+            "\tv_add_u32_e32 v2, v2, v3\n"
+            ".LBB0_3:                                ;   in Loop: Header=BB0_2 Depth=1\n"
+            "\tscratch_load_dword v4, off, off\n"
+            ".LBB0_4:\n"
+            "\tscratch_load_dword v1, off, off\n"
+            "\ts_endpgm\n")
+    assert _scratch_in_loops(text, "k") == [(".LBB0_3:", "scratch_load_dword v4, off, off")]
